@@ -1,0 +1,200 @@
+// api.hip -- the extern "C" entry points declared in include/nf4qlora.h:
+// argument validation, then the launches.  No allocation, no synchronization.
+#include <math.h>
+#include <string.h>
+
+#include "nf4_device.h"
+#include "nf4_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Validates an nf4_tensor for a linear call (cols % 64 == 0) or for
+// dequantization (rows*cols % 64 == 0).
+int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
+    if (!t) return NF4_EINVAL;
+    if (t->cfg.block_size != 64) return NF4_EUNSUPPORTED;
+    if (t->rows < 0 || t->cols < 0) return NF4_EINVAL;
+    if (t->cfg.double_quant != 0 && t->cfg.double_quant != 1) return NF4_EINVAL;
+    if (t->cfg.double_quant && t->cfg.dq_group < 1) return NF4_EUNSUPPORTED;
+    const int64_t n = t->rows * t->cols;
+    if (linear ? (t->cols % 64 != 0) : (n % 64 != 0)) return NF4_ESHAPE;
+    if (n > 0) {
+        if (!t->codes || !al16(t->codes)) return NF4_EINVAL;
+        if (t->cfg.double_quant) {
+            if (!t->scale_codes || !t->group_absmax) return NF4_EINVAL;
+        } else if (!t->absmax) {
+            return NF4_EINVAL;
+        }
+    }
+    v->codes = reinterpret_cast<const uint32_t*>(t->codes);
+    v->absmax = t->absmax;
+    v->qcodes = t->scale_codes;
+    v->gabs = t->group_absmax;
+    v->rows = t->rows;
+    v->cols = t->cols;
+    v->dq = t->cfg.double_quant;
+    v->group = t->cfg.double_quant ? t->cfg.dq_group : 1;
+    return NF4_OK;
+}
+
+inline bool bad_ptr(const void* p) { return !p || !al16(p); }
+
+}  // namespace
+
+namespace nf4 {
+int launch_status() {
+    const hipError_t e = hipGetLastError();
+    g_last_hip_error = int(e);
+    return e == hipSuccess ? NF4_OK : NF4_ELAUNCH;
+}
+}  // namespace nf4
+
+extern "C" {
+
+const float* nf4_table(void) {
+    static float t[16];
+    static bool init = false;
+    if (!init) {  // idempotent: every thread writes the same bits
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t b = nf4dev::level_bits(i);
+            memcpy(&t[i], &b, 4);
+        }
+        init = true;
+    }
+    return t;
+}
+
+const char* nf4_strerror(int code) {
+    switch (code) {
+        case NF4_OK: return "ok";
+        case NF4_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad rank or scale)";
+        case NF4_ESHAPE: return "shape not a multiple of the 64-element block (linear calls: cols % 64 != 0)";
+        case NF4_EUNSUPPORTED: return "unsupported configuration (block_size must be 64, dq_group >= 1)";
+        case NF4_EWORKSPACE: return "workspace missing or smaller than qlora_workspace_bytes()";
+        case NF4_ELAUNCH: return "HIP kernel launch failed (see nf4_last_hip_error)";
+        default: return "unknown error code";
+    }
+}
+
+int nf4_version(void) { return NF4QLORA_VERSION; }
+
+int nf4_last_hip_error(void) { return g_last_hip_error; }
+
+int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg, size_t* code_bytes,
+                      size_t* scale_bytes, size_t* group_bytes) {
+    if (!cfg || rows < 0 || cols < 0) return NF4_EINVAL;
+    if (cfg->block_size < 1) return NF4_EINVAL;
+    const int64_t n = rows * cols;
+    if (n % 2 != 0 || n % cfg->block_size != 0) return NF4_ESHAPE;
+    const int64_t nb = n / cfg->block_size;
+    if (cfg->double_quant && cfg->dq_group < 1) return NF4_EUNSUPPORTED;
+    if (code_bytes) *code_bytes = size_t(n / 2);
+    if (scale_bytes) *scale_bytes = size_t(cfg->double_quant ? nb : nb * 4);
+    if (group_bytes)
+        *group_bytes = cfg->double_quant ? size_t((nb + cfg->dq_group - 1) / cfg->dq_group) * 4 : 0;
+    return NF4_OK;
+}
+
+int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* cfg, uint8_t* codes,
+                 float* absmax, int8_t* scale_codes, float* group_absmax, void* stream) {
+    if (!cfg) return NF4_EINVAL;
+    if (cfg->block_size != 64) return NF4_EUNSUPPORTED;
+    if (cfg->double_quant != 0 && cfg->double_quant != 1) return NF4_EINVAL;
+    if (cfg->double_quant && cfg->dq_group < 1) return NF4_EUNSUPPORTED;
+    if (rows < 0 || cols < 0) return NF4_EINVAL;
+    const int64_t n = rows * cols;
+    if (n % 64 != 0) return NF4_ESHAPE;
+    if (n == 0) return NF4_OK;
+    if (bad_ptr(W) || bad_ptr(codes) || bad_ptr(absmax)) return NF4_EINVAL;
+    if (cfg->double_quant && (bad_ptr(scale_codes) || bad_ptr(group_absmax))) return NF4_EINVAL;
+    return nf4::launch_quantize(W, n, cfg->double_quant, cfg->dq_group, codes, absmax, scale_codes,
+                                group_absmax, static_cast<hipStream_t>(stream));
+}
+
+int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, false, &v);
+    if (rc) return rc;
+    if (v.rows * v.cols == 0) return NF4_OK;
+    if (bad_ptr(W_out)) return NF4_EINVAL;
+    return nf4::launch_dequant_f32(v, W_out, static_cast<hipStream_t>(stream));
+}
+
+int nf4_dequantize_bf16(const nf4_tensor* W, uint16_t* W_out, void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, false, &v);
+    if (rc) return rc;
+    if (v.rows * v.cols == 0) return NF4_OK;
+    if (bad_ptr(W_out)) return NF4_EINVAL;
+    return nf4::launch_dequant_bf16(v, W_out, static_cast<hipStream_t>(stream));
+}
+
+size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
+                             int32_t n_adapters) {
+    if (rows < 0 || cols < 0 || M < 0 || r < 0 || r > 256) return 0;
+    return nf4::workspace_bytes(op, rows, cols, M, r, n_adapters);
+}
+
+int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                         const uint16_t* B, int32_t r, float scale, uint16_t* h, float* u_out,
+                         void* ws, size_t ws_bytes, void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (M < 0 || r < 0 || r > 256 || !isfinite(scale)) return NF4_EINVAL;
+    if (!A || !B) r = 0;
+    if (M == 0 || v.rows == 0) return NF4_OK;
+    if (bad_ptr(x) || bad_ptr(h)) return NF4_EINVAL;
+    if (r > 0 && (bad_ptr(A) || bad_ptr(B))) return NF4_EINVAL;
+    if (u_out && !al16(u_out)) return NF4_EINVAL;
+    if (v.cols == 0) return NF4_EINVAL;
+    return nf4::forward_impl(v, x, M, A, B, r, scale, h, r > 0 ? u_out : nullptr, ws, ws_bytes,
+                             static_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_forward_multi(const nf4_tensor* W, const uint16_t* x, int64_t M,
+                               const uint16_t* A_bank, const uint16_t* B_bank, int32_t n_adapters,
+                               int32_t r, const float* scales, const int32_t* ids, uint16_t* h,
+                               void* ws, size_t ws_bytes, void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (M < 0 || r < 1 || r > 256 || n_adapters < 1) return NF4_EINVAL;
+    if (M == 0 || v.rows == 0) return NF4_OK;
+    if (v.cols == 0) return NF4_EINVAL;
+    if (bad_ptr(x) || bad_ptr(h) || bad_ptr(A_bank) || bad_ptr(B_bank) || bad_ptr(scales) ||
+        bad_ptr(ids))
+        return NF4_EINVAL;
+    return nf4::forward_multi_impl(v, x, M, A_bank, B_bank, n_adapters, r, scales, ids, h, ws,
+                                   ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t* dH, int64_t M,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                          const float* u, uint16_t* dX, float* dA, float* dB, void* ws,
+                          size_t ws_bytes, void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (M < 0 || r < 1 || r > 256 || !isfinite(scale)) return NF4_EINVAL;
+    if (bad_ptr(A) || bad_ptr(B) || bad_ptr(dA) || bad_ptr(dB)) return NF4_EINVAL;
+    if (v.rows == 0 || v.cols == 0) return NF4_EINVAL;
+    if (M > 0 && (bad_ptr(x) || bad_ptr(dH))) return NF4_EINVAL;
+    if (u && !al16(u)) return NF4_EINVAL;
+    if (dX && !al16(dX)) return NF4_EINVAL;
+    if (M == 0) {
+        // Empty batch: every gradient is an empty sum.
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        rc = nf4::zero_f32(dA, int64_t(r) * v.cols, st);
+        if (rc) return rc;
+        return nf4::zero_f32(dB, v.rows * int64_t(r), st);
+    }
+    return nf4::backward_impl(v, x, dH, M, A, B, r, scale, u, dX, dA, dB, ws, ws_bytes,
+                              static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// nf4_internal.h -- host-side declarations shared by the library's .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nf4qlora.h"
+
+namespace nf4 {
+
+// Records a failed launch for nf4_last_hip_error() and returns NF4_ELAUNCH.
+int launch_status();
+
+struct QView {  // a validated nf4_tensor
+    const uint32_t* codes;  // rows*cols/8 dwords
+    const float* absmax;
+    const int8_t* qcodes;
+    const float* gabs;
+    int64_t rows, cols;
+    int dq;        // 0/1
+    int group;     // dq_group
+};
+
+int launch_quantize(const float* W, int64_t n, int dq, int group, uint8_t* codes, float* absmax,
+                    int8_t* qcodes, float* gabs, hipStream_t s);
+int launch_dequant_f32(const QView& q, float* out, hipStream_t s);
+int launch_dequant_bf16(const QView& q, uint16_t* out, hipStream_t s);
+
+// Layer passes (defined in the GEMM / skinny / LoRA files).
+int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A,
+                 const uint16_t* B, int r, float scale, uint16_t* h, float* u_out, void* ws,
+                 size_t ws_bytes, hipStream_t s);
+int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* Ab,
+                       const uint16_t* Bb, int n, int r, const float* scales, const int32_t* ids,
+                       uint16_t* h, void* ws, size_t ws_bytes, hipStream_t s);
+int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M,
+                  const uint16_t* A, const uint16_t* B, int r, float scale, const float* u,
+                  uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t s);
+int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
+size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace nf4

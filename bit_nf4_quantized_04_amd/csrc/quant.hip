@@ -1,0 +1,168 @@
+// quant.hip -- NF4 blockwise quantizer, double quantization of the block
+// scales, and dequantization to fp32 / bf16.
+//
+// Quantizer: "QLoRA Finetuner", section "2. Block-by-Block NormalFloat4 (NF4)
+// Quantization" (absmax per 64-element block, division by it, nearest of the
+// 16 levels) and "From LoRA to QLoRA", "Pillar 1" (two codes per byte, first
+// element in the high nibble).  Double quantization: "QLoRA explained",
+// "Double quantization" (scale / absmax * 127, rounded, int8) with the group
+// size of "From LoRA to QLoRA", "Pillar 2" (256 blocks).
+#include "nf4_device.h"
+#include "nf4_internal.h"
+
+using namespace nf4dev;
+
+namespace {
+
+// Nearest level for a normalized value: code = #{k : w >= cut_k}, found with
+// a four-step binary search over the 15 sorted cuts (ties already resolved by
+// the choice of cuts, see cut_bits).
+__device__ __forceinline__ uint32_t nearest_code(float w) {
+#define CUT(k) bits_f(cut_bits(k))
+    uint32_t c = (w >= CUT(7)) ? 8u : 0u;
+    float t = (c & 8u) ? CUT(11) : CUT(3);
+    c |= (w >= t) ? 4u : 0u;
+    t = (c & 8u) ? ((c & 4u) ? CUT(13) : CUT(9)) : ((c & 4u) ? CUT(5) : CUT(1));
+    c |= (w >= t) ? 2u : 0u;
+    float lo = (c & 8u) ? ((c & 4u) ? ((c & 2u) ? CUT(14) : CUT(12)) : ((c & 2u) ? CUT(10) : CUT(8)))
+                        : ((c & 4u) ? ((c & 2u) ? CUT(6) : CUT(4)) : ((c & 2u) ? CUT(2) : CUT(0)));
+    c |= (w >= lo) ? 1u : 0u;
+#undef CUT
+    return c;
+}
+
+// One thread = 4 consecutive elements; 16 lanes = one 64-element block.  The
+// absmax is a 16-lane butterfly max; codes of 4 elements pack into 2 bytes.
+__global__ __launch_bounds__(256) void k_quant_blocks(const float4* __restrict__ W, int64_t n4,
+                                                      uint16_t* __restrict__ codes,
+                                                      float* __restrict__ absmax) {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) {
+        // n4 is a multiple of 16 and so is `stride`: the 16 lanes of a block
+        // enter and leave the loop together.
+        const float4 v = W[i];
+        float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+        uint32_t packed;
+        if (m == 0.0f) {
+            packed = 0x7777u;  // an all-zero block: every element is level 7 (0.0)
+        } else {
+            const uint32_t c0 = nearest_code(__fdiv_rn(v.x, m));
+            const uint32_t c1 = nearest_code(__fdiv_rn(v.y, m));
+            const uint32_t c2 = nearest_code(__fdiv_rn(v.z, m));
+            const uint32_t c3 = nearest_code(__fdiv_rn(v.w, m));
+            packed = ((c0 << 4) | c1) | (((c2 << 4) | c3) << 8);
+        }
+        codes[i] = uint16_t(packed);
+        if ((threadIdx.x & 15) == 0) absmax[i >> 4] = m;
+    }
+}
+
+// One wave per group of `G` consecutive block scales.
+__global__ __launch_bounds__(256) void k_dq_scales(const float* __restrict__ absmax, int64_t nb,
+                                                   int G, int8_t* __restrict__ q,
+                                                   float* __restrict__ gabs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t g = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t ng = (nb + G - 1) / G;
+    if (g >= ng) return;  // whole wave
+    const int64_t b0 = g * G;
+    const int64_t len = (nb - b0 < G) ? (nb - b0) : G;
+    float m = 0.0f;
+    for (int64_t j = lane; j < len; j += 64) m = fmaxf(m, absmax[b0 + j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) gabs[g] = m;
+    for (int64_t j = lane; j < len; j += 64) {
+        int code = 0;
+        if (m != 0.0f) code = (int)rintf(__fmul_rn(__fdiv_rn(absmax[b0 + j], m), 127.0f));
+        q[b0 + j] = int8_t(code);
+    }
+}
+
+// One thread = one dword of codes = 8 elements of one block.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
+                                                 const float* __restrict__ absmax,
+                                                 const int8_t* __restrict__ qcodes,
+                                                 const float* __restrict__ gabs, int G, int64_t n8,
+                                                 void* __restrict__ out) {
+    __shared__ float lv[16];
+    if (threadIdx.x < 16) lv[threadIdx.x] = bits_f(level_bits(threadIdx.x));
+    __syncthreads();
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride) {
+        const int64_t b = i >> 3;
+        float s;
+        if (qcodes) {
+            s = __fmul_rn(q_over_127(qcodes[b]), gabs[b / G]);
+        } else {
+            s = absmax[b];
+        }
+        const uint32_t c = codes[i];
+        float w[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[2 * j] = __fmul_rn(s, lv[(c >> (8 * j + 4)) & 15u]);
+            w[2 * j + 1] = __fmul_rn(s, lv[(c >> (8 * j)) & 15u]);
+        }
+        if constexpr (BF16) {
+            uint4 o;
+            o.x = pack_bf16x2(w[0], w[1]);
+            o.y = pack_bf16x2(w[2], w[3]);
+            o.z = pack_bf16x2(w[4], w[5]);
+            o.w = pack_bf16x2(w[6], w[7]);
+            reinterpret_cast<uint4*>(out)[i] = o;
+        } else {
+            float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+            o[0] = make_float4(w[0], w[1], w[2], w[3]);
+            o[1] = make_float4(w[4], w[5], w[6], w[7]);
+        }
+    }
+}
+
+inline unsigned grid_for(int64_t items, int64_t per_block) {
+    int64_t g = (items + per_block - 1) / per_block;
+    const int64_t cap = 256 * 64;  // enough to fill the chip; the kernels grid-stride
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return unsigned(g);
+}
+
+}  // namespace
+
+namespace nf4 {
+
+int launch_quantize(const float* W, int64_t n, int dq, int group, uint8_t* codes, float* absmax,
+                    int8_t* qcodes, float* gabs, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    hipLaunchKernelGGL(k_quant_blocks, dim3(grid_for(n4, 256)), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(W), n4, reinterpret_cast<uint16_t*>(codes),
+                       absmax);
+    if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    if (dq) {
+        const int64_t nb = n / 64;
+        const int64_t ng = (nb + group - 1) / group;
+        hipLaunchKernelGGL(k_dq_scales, dim3(unsigned((ng + 3) / 4)), dim3(256), 0, s, absmax, nb,
+                           group, qcodes, gabs);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    }
+    return NF4_OK;
+}
+
+int launch_dequant_f32(const QView& q, float* out, hipStream_t s) {
+    const int64_t n8 = q.rows * q.cols / 8;
+    hipLaunchKernelGGL(k_dequant<false>, dim3(grid_for(n8, 256)), dim3(256), 0, s, q.codes,
+                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, n8, (void*)out);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int launch_dequant_bf16(const QView& q, uint16_t* out, hipStream_t s) {
+    const int64_t n8 = q.rows * q.cols / 8;
+    hipLaunchKernelGGL(k_dequant<true>, dim3(grid_for(n8, 256)), dim3(256), 0, s, q.codes,
+                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, n8, (void*)out);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+}  // namespace nf4

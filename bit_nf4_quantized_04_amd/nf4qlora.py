@@ -1,0 +1,250 @@
+"""ctypes binding of libnf4qlora.so: argument marshalling only.
+
+The names follow the C ABI in include/nf4qlora.h.  Every computation runs in
+the library's HIP kernels; torch is used for device memory (output and
+workspace allocation) and for the current stream.  Importing this module
+loads the library and raises ImportError when it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4qlora.so")
+
+# torch first: its HIP runtime is the one the library must share.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libnf4qlora.so is not built; run `python -m bit_nf4_quantized_04_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+NF4_OK, NF4_EINVAL, NF4_ESHAPE, NF4_EUNSUPPORTED, NF4_EWORKSPACE, NF4_ELAUNCH = range(6)
+QLORA_OP_FORWARD, QLORA_OP_BACKWARD, QLORA_OP_FORWARD_MULTI = 1, 2, 3
+
+
+class nf4_config(C.Structure):
+    _fields_ = [("block_size", C.c_int32), ("double_quant", C.c_int32), ("dq_group", C.c_int32)]
+
+
+class nf4_tensor(C.Structure):
+    _fields_ = [
+        ("codes", C.c_void_p),
+        ("absmax", C.c_void_p),
+        ("scale_codes", C.c_void_p),
+        ("group_absmax", C.c_void_p),
+        ("rows", C.c_int64),
+        ("cols", C.c_int64),
+        ("cfg", nf4_config),
+    ]
+
+
+_P = C.c_void_p
+_I64 = C.c_int64
+_SIGS = {
+    "nf4_table": (C.POINTER(C.c_float), []),
+    "nf4_strerror": (C.c_char_p, [C.c_int]),
+    "nf4_version": (C.c_int, []),
+    "nf4_last_hip_error": (C.c_int, []),
+    "nf4_storage_sizes": (C.c_int, [_I64, _I64, C.POINTER(nf4_config), C.POINTER(C.c_size_t),
+                                    C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "nf4_quantize": (C.c_int, [_P, _I64, _I64, C.POINTER(nf4_config), _P, _P, _P, _P, _P]),
+    "nf4_dequantize": (C.c_int, [C.POINTER(nf4_tensor), _P, _P]),
+    "nf4_dequantize_bf16": (C.c_int, [C.POINTER(nf4_tensor), _P, _P]),
+    "qlora_workspace_bytes": (C.c_size_t, [C.c_int, _I64, _I64, _I64, C.c_int32, C.c_int32]),
+    "qlora_linear_forward": (C.c_int, [C.POINTER(nf4_tensor), _P, _I64, _P, _P, C.c_int32,
+                                       C.c_float, _P, _P, _P, C.c_size_t, _P]),
+    "qlora_linear_forward_multi": (C.c_int, [C.POINTER(nf4_tensor), _P, _I64, _P, _P, C.c_int32,
+                                             C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
+    "qlora_linear_backward": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, _I64, _P, _P, C.c_int32,
+                                        C.c_float, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.nf4_strerror(code).decode()
+        if code == NF4_ELAUNCH:
+            msg += " (hipError %d)" % _lib.nf4_last_hip_error()
+        super().__init__("%s: %s" % (where, msg))
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != NF4_OK:
+        raise NF4Error(rc, where)
+
+
+def _stream(stream=None):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------ host-only
+def nf4_table() -> np.ndarray:
+    p = _lib.nf4_table()
+    return np.ctypeslib.as_array(p, shape=(16,)).copy()
+
+
+def nf4_version() -> int:
+    return _lib.nf4_version()
+
+
+def nf4_strerror(code: int) -> str:
+    return _lib.nf4_strerror(code).decode()
+
+
+def nf4_storage_sizes(rows: int, cols: int, double_quant: bool, dq_group: int = 256,
+                      block_size: int = 64):
+    cfg = nf4_config(block_size, int(double_quant), dq_group)
+    a, b, c = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    _check(_lib.nf4_storage_sizes(rows, cols, C.byref(cfg), C.byref(a), C.byref(b), C.byref(c)),
+           "nf4_storage_sizes")
+    return a.value, b.value, c.value
+
+
+def qlora_workspace_bytes(op: int, rows: int, cols: int, M: int, r: int, n_adapters: int = 0) -> int:
+    return int(_lib.qlora_workspace_bytes(op, rows, cols, M, r, n_adapters))
+
+
+# ---------------------------------------------------------------- quantized W
+@dataclass
+class NF4Weight:
+    """Device buffers of a quantized [rows, cols] weight (torch tensors)."""
+
+    codes: object
+    absmax: object
+    scale_codes: object
+    group_absmax: object
+    rows: int
+    cols: int
+    double_quant: bool
+    dq_group: int = 256
+
+    def c_struct(self) -> nf4_tensor:
+        return nf4_tensor(
+            _ptr(self.codes) or None, _ptr(self.absmax) or None,
+            _ptr(self.scale_codes) if self.double_quant else None,
+            _ptr(self.group_absmax) if self.double_quant else None,
+            self.rows, self.cols, nf4_config(64, int(self.double_quant), self.dq_group))
+
+
+def nf4_quantize(W, double_quant: bool, dq_group: int = 256, stream=None) -> NF4Weight:
+    """Quantize a contiguous fp32 CUDA tensor [rows, cols]."""
+    import torch
+
+    rows, cols = W.shape
+    n = rows * cols
+    dev = W.device
+    nb = n // 64
+    codes = torch.empty(max(n // 2, 16), dtype=torch.uint8, device=dev)
+    absmax = torch.empty(max(nb, 4), dtype=torch.float32, device=dev)
+    sc = gab = None
+    if double_quant:
+        sc = torch.empty(max(nb, 16), dtype=torch.int8, device=dev)
+        gab = torch.empty(max((nb + dq_group - 1) // dq_group, 4), dtype=torch.float32, device=dev)
+    cfg = nf4_config(64, int(double_quant), dq_group)
+    _check(_lib.nf4_quantize(_ptr(W), rows, cols, C.byref(cfg), _ptr(codes), _ptr(absmax),
+                             _ptr(sc), _ptr(gab), _stream(stream)), "nf4_quantize")
+    return NF4Weight(codes[: n // 2], absmax[:nb], None if sc is None else sc[:nb],
+                     None if gab is None else gab[: (nb + dq_group - 1) // dq_group],
+                     rows, cols, double_quant, dq_group)
+
+
+def nf4_dequantize(w: NF4Weight, stream=None):
+    import torch
+
+    out = torch.empty((w.rows, w.cols), dtype=torch.float32, device=w.codes.device)
+    t = w.c_struct()
+    _check(_lib.nf4_dequantize(C.byref(t), _ptr(out), _stream(stream)), "nf4_dequantize")
+    return out
+
+
+def nf4_dequantize_bf16(w: NF4Weight, stream=None):
+    import torch
+
+    out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=w.codes.device)
+    t = w.c_struct()
+    _check(_lib.nf4_dequantize_bf16(C.byref(t), _ptr(out), _stream(stream)), "nf4_dequantize_bf16")
+    return out
+
+
+def _workspace(nbytes: int, device):
+    import torch
+
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def qlora_linear_forward(w: NF4Weight, x, A, B, scale: float, want_u: bool = False, ws=None,
+                         out=None, stream=None):
+    """h = x Wb^T + scale (x A^T) B^T; x, A, B bf16 CUDA tensors.  Returns h (and u)."""
+    import torch
+
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    u = torch.empty((M, r), dtype=torch.float32, device=x.device) if (want_u and r) else None
+    need = qlora_workspace_bytes(QLORA_OP_FORWARD, w.rows, w.cols, M, r)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    t = w.c_struct()
+    _check(_lib.qlora_linear_forward(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale),
+                                     _ptr(h), _ptr(u), _ptr(ws), ws.numel(), _stream(stream)),
+           "qlora_linear_forward")
+    return (h, u) if want_u else h
+
+
+def qlora_linear_forward_multi(w: NF4Weight, x, A_bank, B_bank, scales, ids, ws=None, out=None,
+                               stream=None):
+    """Per-token adapter forward; scales fp32 CUDA [n], ids int32 CUDA [M]."""
+    import torch
+
+    M = x.shape[0]
+    n, r = A_bank.shape[0], A_bank.shape[1]
+    h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    need = qlora_workspace_bytes(QLORA_OP_FORWARD_MULTI, w.rows, w.cols, M, r, n)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    t = w.c_struct()
+    _check(_lib.qlora_linear_forward_multi(C.byref(t), _ptr(x), M, _ptr(A_bank), _ptr(B_bank), n, r,
+                                           _ptr(scales), _ptr(ids), _ptr(h), _ptr(ws), ws.numel(),
+                                           _stream(stream)), "qlora_linear_forward_multi")
+    return h
+
+
+def qlora_linear_backward(w: NF4Weight, x, dH, A, B, scale: float, u=None, want_dx: bool = True,
+                          ws=None, stream=None):
+    """Returns (dX or None, dA fp32 [r, in], dB fp32 [out, r])."""
+    import torch
+
+    M = x.shape[0]
+    r = A.shape[0]
+    dev = x.device
+    dX = torch.empty((M, w.cols), dtype=torch.bfloat16, device=dev) if want_dx else None
+    dA = torch.empty((r, w.cols), dtype=torch.float32, device=dev)
+    dB = torch.empty((w.rows, r), dtype=torch.float32, device=dev)
+    need = qlora_workspace_bytes(QLORA_OP_BACKWARD, w.rows, w.cols, M, r)
+    if ws is None:
+        ws = _workspace(need, dev)
+    t = w.c_struct()
+    _check(_lib.qlora_linear_backward(C.byref(t), _ptr(x), _ptr(dH), M, _ptr(A), _ptr(B), r,
+                                      float(scale), _ptr(u), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                      ws.numel(), _stream(stream)), "qlora_linear_backward")
+    return dX, dA, dB

@@ -1,0 +1,175 @@
+/*
+ * nf4qlora.h -- C ABI of the MI355X (gfx950) NF4 QLoRA linear-layer library.
+ *
+ * The library computes the QLoRA linear layer
+ *
+ *     h = Wb x + (alpha/r) B (A x),        Wb = bf16( s~_b * NF4[code] )
+ *
+ * whose frozen base weight is stored as 4-bit NormalFloat codes in blocks of
+ * 64 elements, each block with an absmax scale that may itself be quantized
+ * to int8 ("double quantization").  Sources, by page title and section:
+ *
+ *  [P1] "QLoRA Finetuner", sections "1. Low-Rank Adaptation (LoRA)" (forward
+ *       h = W0 x + (alpha/r) B(A x)) and "2. Block-by-Block NormalFloat4 (NF4)
+ *       Quantization" (64-element blocks, absmax scale, division by the scale,
+ *       nearest of 16 levels, dequantization as scale times level).
+ *  [P2] "QLoRA Specification for EMEP Fine-Tuning", "Hyperparameters"
+ *       (quant type nf4, double quant on, compute dtype bfloat16).
+ *  [P3] "QLoRA explained: fine-tuning in 4-bit precision", "Double
+ *       quantization" (scales divided by their absmax, times 127, rounded to
+ *       int8), "The LoRA adapter path" (layout x W^T, (x A^T) B^T * scale; the
+ *       dequantized weight is cast to bfloat16 and receives no gradient),
+ *       "Common misconceptions" (the 16 NF4 levels).
+ *  [P5] "Parameter-Efficient Fine-Tuning: From LoRA to QLoRA", "Pillar 1"
+ *       (level table, worked example, two codes per byte, first element in
+ *       the high nibble), "Pillar 2" (8-bit scales in groups of 256), "The
+ *       Real-World Bottleneck" (one resident base, adapter chosen per request).
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major memory owned
+ *    by the caller, each aligned to 16 bytes (NF4_EINVAL otherwise).  The library never allocates, frees or synchronizes; it
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns.  Outputs must not alias inputs.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Layouts follow nn.Linear [P3 "The LoRA adapter path"]: W is [out, in]
+ *    (rows = out, cols = in), x is [M, in], A is [r, in], B is [out, r],
+ *    h is [M, out].
+ *  - Every call returns NF4_OK (0) or an error code; on error nothing has been
+ *    enqueued (except NF4_ELAUNCH, after which the HIP error is available from
+ *    nf4_last_hip_error(), per thread).  No exception crosses the ABI.
+ *  - Inputs must be finite.  The quantizer does not check this; a block that
+ *    holds Inf or NaN gets unspecified codes and scale.
+ */
+#ifndef NF4QLORA_H
+#define NF4QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4QLORA_VERSION 1
+
+enum {
+    NF4_OK = 0,
+    NF4_EINVAL = 1,        /* null pointer, negative size, r outside [0, 256], bad scale */
+    NF4_ESHAPE = 2,        /* rows*cols not a multiple of the block; linear calls: cols % 64 != 0 */
+    NF4_EUNSUPPORTED = 3,  /* block_size != 64, dq_group < 1 */
+    NF4_EWORKSPACE = 4,    /* workspace pointer NULL or smaller than qlora_workspace_bytes() */
+    NF4_ELAUNCH = 5        /* a HIP launch failed; see nf4_last_hip_error() */
+};
+
+/* Quantization settings [P2 "Hyperparameters"].  The quant type is NF4 and
+ * the compute dtype bf16; both are fixed. */
+typedef struct nf4_config {
+    int32_t block_size;    /* elements per block; must be 64 [P1 section 2] */
+    int32_t double_quant;  /* 0: fp32 block scales; 1: int8 scale codes + fp32 group constants */
+    int32_t dq_group;      /* blocks per second-level group, >= 1 (256 [P5 Pillar 2]);
+                              dq_group >= number of blocks gives one global constant [P3] */
+} nf4_config;
+
+/* A quantized weight [rows, cols] in caller-owned device buffers.
+ *  codes:        rows*cols/2 bytes; element e of the row-major flattening is
+ *                the high nibble of byte e/2 when e is even, the low nibble
+ *                when e is odd [P5 "Pillar 1", byte packing].
+ *  absmax:       rows*cols/64 fp32 block scales (read when double_quant == 0).
+ *  scale_codes:  rows*cols/64 int8 codes q_b in [0, 127] (double_quant == 1).
+ *  group_absmax: ceil(nblocks/dq_group) fp32 group constants c_g (double_quant == 1).
+ * The scale used for block b is s_b, or fl32(fl32(q_b/127) * c_g) with
+ * g = b / dq_group (the operation-by-operation inverse of the quantizer). */
+typedef struct nf4_tensor {
+    const uint8_t* codes;
+    const float* absmax;
+    const int8_t* scale_codes;
+    const float* group_absmax;
+    int64_t rows;
+    int64_t cols;
+    nf4_config cfg;
+} nf4_tensor;
+
+/* Host copy of the 16 NF4 levels (index = 4-bit code) [P3 "Common
+ * misconceptions"; P5 "Pillar 1" table].  Never NULL. */
+const float* nf4_table(void);
+const char* nf4_strerror(int code);
+int nf4_version(void);
+/* The last hipError_t recorded by a failed launch on the calling thread. */
+int nf4_last_hip_error(void);
+
+/* Storage of a [rows, cols] weight in bytes (host-only arithmetic): codes,
+ * first-level scale bytes stored (4 per block, or 1 per block with double
+ * quant), second-level bytes (4 per group, double quant only).  Any output
+ * pointer may be NULL.  [P5 worked example: 6 fp32 weights in one block take
+ * 3 + 4 = 7 bytes; P5 "Pillar 2": 0.5 bits/param of fp32 scales fall to about
+ * 0.127 with 8-bit scales in groups of 256.] */
+int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg,
+                      size_t* code_bytes, size_t* scale_bytes, size_t* group_bytes);
+
+/* Quantize W (fp32 [rows, cols], device) [P1 section 2; P5 "Pillar 1"]:
+ * per contiguous 64-element block of the row-major flattening,
+ *   s_b = max |w|, w' = fl32(w / s_b), code = nearest NF4 level to w'
+ *   (an exact tie goes to the lower level; an all-zero block gets code 7).
+ * Writes `codes` and `absmax` (always).  With double quant [P3 "Double
+ * quantization"; P5 "Pillar 2"] also writes, per group of dq_group blocks,
+ *   c_g = max s_b,  q_b = round_half_even(fl32(fl32(s_b / c_g) * 127))
+ * (q_b = 0 when c_g = 0) into scale_codes and group_absmax, which must then be
+ * non-NULL.  Errors: NF4_EINVAL (NULL pointer, negative size), NF4_ESHAPE
+ * (rows*cols % 64 != 0), NF4_EUNSUPPORTED (block_size != 64, dq_group < 1). */
+int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* cfg,
+                 uint8_t* codes, float* absmax, int8_t* scale_codes, float* group_absmax,
+                 void* stream);
+
+/* Dequantize to fp32 [rows, cols]: w~ = fl32(scale_b * NF4[code]) [P1
+ * section 2, last item].  Bit-exact contract. */
+int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream);
+/* Dequantize to bf16 bits [rows, cols]: round-to-nearest-even of w~ [P3 "The
+ * LoRA adapter path" casts the dequantized weight to bfloat16]. */
+int nf4_dequantize_bf16(const nf4_tensor* W, uint16_t* W_out, void* stream);
+
+/* Workspace sizes for the layer calls (bytes; 0 means none is needed). */
+enum { QLORA_OP_FORWARD = 1, QLORA_OP_BACKWARD = 2, QLORA_OP_FORWARD_MULTI = 3 };
+size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
+                             int32_t n_adapters);
+
+/* Forward of the QLoRA linear layer [P1 section 1; P3 "The LoRA adapter path"]:
+ *   u = x A^T (fp32 [M, r]),   h = x Wb^T + scale * u B^T   (h as bf16)
+ * W: rows = out, cols = in (cols % 64 == 0).  x bf16 [M, in]; A bf16 [r, in];
+ * B bf16 [out, r]; h bf16 [M, out], overwritten.  u_out (fp32 [M, r]) may be
+ * NULL; when given it receives u for the backward pass.  r == 0 or A/B NULL
+ * gives the base product only.  Dropout on the adapter branch is not applied
+ * (p = 0).  M == 0 is a successful no-op.  ws must hold
+ * qlora_workspace_bytes(QLORA_OP_FORWARD, ...).  Products use bf16 operands
+ * with fp32 accumulation; u stays fp32 (hi+lo bf16 pair inside the MFMA). */
+int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M,
+                         const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                         uint16_t* h, float* u_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Multi-adapter forward [P5 "The Real-World Bottleneck"]: token t uses
+ * adapter ids[t] (device int32 [M]):
+ *   h_t = x_t Wb^T + scales[id] * (x_t A_id^T) B_id^T
+ * A_bank bf16 [n, r, in]; B_bank bf16 [n, out, r]; scales: device fp32 [n]
+ * (alpha/r of each adapter).  A token whose id is outside [0, n) gets the base
+ * output only (the pages do not say; this is the library's choice). */
+int qlora_linear_forward_multi(const nf4_tensor* W, const uint16_t* x, int64_t M,
+                               const uint16_t* A_bank, const uint16_t* B_bank,
+                               int32_t n_adapters, int32_t r, const float* scales,
+                               const int32_t* ids, uint16_t* h, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Backward [P3 "The LoRA adapter path": gradients flow only into A and B; the
+ * dequantized weight is a constant, so there is no dW].  With u = x A^T:
+ *   dU = scale dH B,  dB = scale dH^T u,  dA = dU^T x,  dX = dH Wb + dU A.
+ * dH bf16 [M, out]; u fp32 [M, r] saved by the forward, or NULL to recompute;
+ * dX bf16 [M, in] (NULL: skipped); dA fp32 [r, in]; dB fp32 [out, r].  All
+ * outputs are overwritten.  r must be >= 1. */
+int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t* dH, int64_t M,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                          const float* u, uint16_t* dX, float* dA, float* dB,
+                          void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4QLORA_H */

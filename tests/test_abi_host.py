@@ -1,0 +1,141 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+function include/nf4qlora.h declares, and rejects bad arguments before any
+launch.  Calls that would launch a kernel are not made here."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4qlora.h")
+LIB = os.path.join(ROOT, "bit_nf4_quantized_04_amd", "libnf4qlora.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libnf4qlora.so not built")
+
+
+@pytest.fixture(scope="module")
+def F():
+    from bit_nf4_quantized_04_amd import nf4qlora
+
+    return nf4qlora
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_every_declared_function_is_exported(F):
+    names = declared_functions()
+    assert len(names) == 12, names
+    lib = C.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(F.EXPORTS)
+
+
+def test_version_table_and_strings(F):
+    from oracle import nf4_oracle as O
+
+    assert F.nf4_version() == 1
+    np.testing.assert_array_equal(F.nf4_table(), O.NF4_LEVELS)
+    for code in range(6):
+        assert F.nf4_strerror(code)
+    assert "unknown" in F.nf4_strerror(99)
+
+
+def test_storage_sizes_match_the_pages(F):
+    # Worked example ("From LoRA to QLoRA", Pillar 1): 6 weights, one block,
+    # 3 code bytes + 4 scale bytes = 7 bytes.
+    assert F.nf4_storage_sizes(2, 3, double_quant=False, block_size=6) == (3, 4, 0)
+    # Pillar 2: 0.5 bits/param of fp32 scales -> about 0.127 with int8 scales in groups of 256.
+    rows, cols = 4096, 4096
+    cb, sb, gb = F.nf4_storage_sizes(rows, cols, double_quant=False)
+    assert 8 * sb / (rows * cols) == 0.5
+    cb2, sb2, gb2 = F.nf4_storage_sizes(rows, cols, double_quant=True)
+    assert cb == cb2 == rows * cols // 2
+    assert round(8 * (sb2 + gb2) / (rows * cols), 3) == 0.127
+
+
+def _cfg(F, bs=64, dq=1, g=256):
+    return F.nf4_config(bs, dq, g)
+
+
+FAKE = C.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails validation first
+
+
+def test_quantize_argument_errors(F):
+    lib = F._lib
+    cfg = _cfg(F)
+    q = lambda W, r, c, cf, codes, ab, sc, ga: lib.nf4_quantize(W, r, c, cf, codes, ab, sc, ga, None)
+    assert q(None, 64, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
+    assert q(FAKE, 64, 64, None, FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
+    assert q(FAKE, -1, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
+    assert q(FAKE, 3, 5, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_ESHAPE
+    bad = _cfg(F, bs=128)
+    assert q(FAKE, 64, 64, C.byref(bad), FAKE, FAKE, FAKE, FAKE) == F.NF4_EUNSUPPORTED
+    bad = _cfg(F, g=0)
+    assert q(FAKE, 64, 64, C.byref(bad), FAKE, FAKE, FAKE, FAKE) == F.NF4_EUNSUPPORTED
+    assert q(FAKE, 64, 64, C.byref(cfg), FAKE, FAKE, None, FAKE) == F.NF4_EINVAL  # DQ needs its outputs
+    assert q(C.c_void_p(0x100004), 64, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
+    assert q(None, 0, 64, C.byref(cfg), None, None, None, None) == F.NF4_OK  # empty: no-op
+
+
+def _tensor(F, rows=128, cols=256, dq=1, bs=64, g=256, codes=FAKE):
+    return F.nf4_tensor(codes, FAKE, FAKE, FAKE, rows, cols, F.nf4_config(bs, dq, g))
+
+
+def test_layer_argument_errors(F):
+    lib = F._lib
+    t = _tensor(F)
+    fwd = lambda tt, x, M, A, B, r, s, h, ws, wsb: lib.qlora_linear_forward(
+        C.byref(tt), x, M, A, B, r, s, h, None, ws, wsb, None)
+    assert fwd(t, FAKE, -1, FAKE, FAKE, 4, 2.0, FAKE, FAKE, 1 << 30) == F.NF4_EINVAL
+    assert fwd(t, FAKE, 4, FAKE, FAKE, 300, 2.0, FAKE, FAKE, 1 << 30) == F.NF4_EINVAL
+    assert fwd(t, FAKE, 4, FAKE, FAKE, 4, float("nan"), FAKE, FAKE, 1 << 30) == F.NF4_EINVAL
+    assert fwd(t, None, 4, FAKE, FAKE, 4, 2.0, FAKE, FAKE, 1 << 30) == F.NF4_EINVAL
+    assert fwd(_tensor(F, cols=96), FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, FAKE, 1 << 30) == F.NF4_ESHAPE
+    assert fwd(_tensor(F, bs=32), FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, FAKE, 1 << 30) == F.NF4_EUNSUPPORTED
+    assert fwd(_tensor(F, codes=None), FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, FAKE, 1 << 30) == F.NF4_EINVAL
+    need = F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 128, 256, 4, 4)
+    assert need > 0
+    assert fwd(t, FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, FAKE, need - 1) == F.NF4_EWORKSPACE
+    assert fwd(t, FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, None, need) == F.NF4_EWORKSPACE
+    assert fwd(t, FAKE, 0, FAKE, FAKE, 4, 2.0, FAKE, None, 0) == F.NF4_OK  # M == 0: no-op
+    bwd = lambda tt, M, r, dA, wsb: lib.qlora_linear_backward(
+        C.byref(tt), FAKE, FAKE, M, FAKE, FAKE, r, 2.0, None, FAKE, dA, FAKE, FAKE, wsb, None)
+    assert bwd(t, 4, 0, FAKE, 1 << 30) == F.NF4_EINVAL  # backward needs r >= 1
+    assert bwd(t, 4, 4, None, 1 << 30) == F.NF4_EINVAL
+    nb = F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD, 128, 256, 4, 4)
+    assert bwd(t, 4, 4, FAKE, nb - 1) == F.NF4_EWORKSPACE
+    multi = lambda n, r, ids: lib.qlora_linear_forward_multi(
+        C.byref(t), FAKE, 4, FAKE, FAKE, n, r, FAKE, ids, FAKE, FAKE, 1 << 30, None)
+    assert multi(0, 4, FAKE) == F.NF4_EINVAL
+    assert multi(3, 4, None) == F.NF4_EINVAL
+    mb = F.qlora_workspace_bytes(F.QLORA_OP_FORWARD_MULTI, 128, 256, 4, 4, 3)
+    assert lib.qlora_linear_forward_multi(C.byref(t), FAKE, 4, FAKE, FAKE, 3, 4, FAKE, FAKE, FAKE,
+                                          FAKE, mb - 1, None) == F.NF4_EWORKSPACE
+
+
+def test_dequantize_argument_errors(F):
+    lib = F._lib
+    assert lib.nf4_dequantize(None, FAKE, None) == F.NF4_EINVAL
+    t = _tensor(F, rows=3, cols=5)
+    assert lib.nf4_dequantize(C.byref(t), FAKE, None) == F.NF4_ESHAPE
+    t = _tensor(F, rows=2, cols=96)  # 192 elements: a multiple of 64 is enough for dequantize
+    assert lib.nf4_dequantize(C.byref(t), None, None) == F.NF4_EINVAL
+    t = F.nf4_tensor(FAKE, None, None, None, 2, 64, F.nf4_config(64, 0, 256))
+    assert lib.nf4_dequantize_bf16(C.byref(t), FAKE, None) == F.NF4_EINVAL  # no-DQ needs absmax
+
+
+def test_workspace_sizes_are_monotone(F):
+    a = F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 16, 16)
+    b = F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 2048, 16)
+    assert 0 < a < b
+    assert F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 16, 0) == 0
+    assert F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD, 4096, 4096, 16, 16) > a
+    assert F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 16, 999) == 0

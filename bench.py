@@ -1,0 +1,266 @@
+"""Benchmark of the NF4 QLoRA linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 70b|7b|decode]
+
+Workload (default "70b"): the 70B MLP projection 8192 -> 28672 (W0 [28672, 8192],
+99.9% N(0, 0.015^2) entries and 0.1% 0.1 * Student-t(3) outliers), NF4 blocks of
+64 with int8 double quantization in groups of 256, r = 64, alpha = 128, synthetic
+seeded inputs.  One step is one pass of the layer's hot path:
+  * decode: the fused dequant-GEMV forward at M = 1 (u = x A^T, then
+    h = x Wb^T + s u B^T), rotating over 5 resident copies of the quantized
+    weight (630 MB > the 256 MB last-level cache) so every call streams W from HBM;
+  * training: forward (u and h) and backward (dX, dA, dB) at M = 4096.
+`value` is the decode throughput in algorithmic GB/s (the headline metric's
+first figure); the training pass is reported as bf16 TFLOP/s in the same line.
+Inputs are resident in HBM before the timed region starts.  Rank 0 prints one
+JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NF4 QLoRA linear: GB/s at M=1, bf16 TFLOP/s at M=4096, % of roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+WORKLOADS = {"decode": 2, "7b": 3, "70b": 4}
+
+
+def decode_bytes(out, inp, M, r, ngroups, with_A=True):
+    """Algorithmic HBM bytes of one decode forward (double quant)."""
+    b = out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * M * inp + 2 * M * out
+    b += 2 * r * out + (2 * r * inp if with_A else 0)
+    return b
+
+
+def gemv_kernel_bytes(out, inp, M, r, ngroups):
+    """Algorithmic bytes of the fused dequant product kernel alone: codes,
+    scale codes, group constants, x, B, u and h (A is read by the u kernel)."""
+    return (out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * M * inp + 2 * r * out
+            + 4 * M * r + 2 * M * out)
+
+
+def train_flops(out, inp, M, r):
+    fwd = 2 * M * out * inp + 2 * M * r * (inp + out)
+    bwd = 2 * M * out * inp + 4 * M * out * r + 4 * M * r * inp
+    return fwd, bwd
+
+
+def cpu_baseline(c, w, x_bits, a_bits, b_bits, scale, budget_s=10.0):
+    """The oracle (as it stands) doing the decode step on row samples of the
+    same weight, until about `budget_s` seconds of CPU work; GB/s of the same
+    algorithmic bytes."""
+    from oracle import nf4_oracle as O
+
+    out, inp = w.shape
+    rows_per = 16384 * 64 // inp  # 64 double-quant groups per sample
+    rng = np.random.default_rng(0)
+    # a handful of distinct row samples, quantized once (offline: not timed)
+    picks = [int(g) * rows_per for g in rng.choice(out // rows_per, size=min(8, out // rows_per),
+                                                   replace=False)]
+    prepared = [(g0, O.quantize(np.ascontiguousarray(w[g0:g0 + rows_per]), double_quant=True))
+                for g0 in picks]
+    ng = (rows_per * inp // 64 + 255) // 256
+    done_bytes, spent, samples = 0, 0.0, 0
+    while spent < budget_s:
+        g0, qt = prepared[samples % len(prepared)]
+        t0 = time.perf_counter()
+        wb = O.compute_weight(qt, (rows_per, inp))
+        _ = O.forward(wb, x_bits, a_bits, b_bits[g0:g0 + rows_per], scale)
+        spent += time.perf_counter() - t0
+        done_bytes += decode_bytes(rows_per, inp, 1, a_bits.shape[0], ng, with_A=True)
+        samples += 1
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    return {
+        "value": done_bytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas),
+        "kind": "oracle",
+        "sample": "%d samples of %d rows x %d (64 double-quant groups each) of the workload weight: "
+                  "oracle dequantize + bf16 cast (NumPy elementwise, 1 thread) and the float64 "
+                  "forward at M=1 (BLAS, %d threads); %.1f s of CPU work"
+                  % (samples, rows_per, inp, blas, spent),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="70b", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer's multi-GPU sharding is a design "
+              "(see DESIGN.md), not built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_nf4_quantized_04_amd import nf4qlora as F
+    from bit_nf4_quantized_04_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    c = WORKLOADS[args.workload]
+    sh = wl.SHAPES[c]
+    out, inp, r = sh["out"], sh["inp"], sh["r"]
+    scale = sh["alpha"] / r
+    Mtrain = max(sh["M"])
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- setup (untimed): inputs resident in HBM
+    w = wl.weight(c)
+    x1_bits = wl.activations(c, 1)
+    a_bits, b_bits = wl.adapters(c)
+    wt = torch.from_numpy(w).to(dev)
+    qs = [F.nf4_quantize(wt, double_quant=True)]
+    for _ in range(args.copies - 1):
+        q0 = qs[0]
+        qs.append(F.NF4Weight(q0.codes.clone(), q0.absmax.clone(), q0.scale_codes.clone(),
+                              q0.group_absmax.clone(), out, inp, True))
+    del wt
+    x1, A, B = bf(x1_bits), bf(a_bits), bf(b_bits)
+    xt = bf(wl.activations(c, Mtrain))
+    dH = bf(wl.upstream_grad(c, Mtrain))
+    ws_f1 = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, out, inp, 1, r), 256),
+                        dtype=torch.uint8, device=dev)
+    ws_ft = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, out, inp, Mtrain, r), 256),
+                        dtype=torch.uint8, device=dev)
+    ws_bt = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD, out, inp, Mtrain, r), 256),
+                        dtype=torch.uint8, device=dev)
+    h1 = torch.empty((1, out), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((Mtrain, out), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    ngroups = (out * inp // 64 + 255) // 256
+
+    def decode_step(i):
+        F.qlora_linear_forward(qs[i % len(qs)], x1, A, B, scale, ws=ws_f1, out=h1)
+
+    def train_step(i):
+        _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
+        F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
+
+    hev = F.HipEvents()
+
+    def timed(step, K, W, hook_events=None):
+        """Mean ms per step over K steps (HIP events on the current stream),
+        and with hook_events the dominant kernel's duration of every call."""
+        for i in range(W):
+            step(i)
+        torch.cuda.synchronize()
+        pairs = [(hev.create(), hev.create()) for _ in range(K)] if hook_events else []
+        t0, t1 = hev.create(), hev.create()
+        hev.record(t0)
+        for i in range(K):
+            if hook_events:
+                F.nf4_profile_events(*pairs[i])
+            step(i)
+        hev.record(t1)
+        torch.cuda.synchronize()
+        F.nf4_profile_events(None, None)
+        total = hev.elapsed_ms(t0, t1) / K
+        kern = [hev.elapsed_ms(a, b) for a, b in pairs]
+        for e in [t0, t1] + [e for p in pairs for e in p]:
+            hev.destroy(e)
+        return total, kern
+
+    # whole-step timing (no hook), then the dominant kernel with the hook
+    K, W = args.steps, args.warmup
+    t_dec, _ = timed(decode_step, K, W)
+    _, k_dec = timed(decode_step, K, 1, hook_events=True)
+    t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))
+    # dominant kernels of the training pass: forward product and dX product
+    fwd_k, bwd_k = [], []
+
+    def train_fwd(i):
+        F.qlora_linear_forward(qs[0], xt, A, B, scale, ws=ws_ft, out=ht)
+
+    _, fwd_k = timed(train_fwd, max(K // 2, 3), 1, hook_events=True)
+    _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
+
+    def train_bwd(i):
+        F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
+
+    _, bwd_k = timed(train_bwd, max(K // 2, 3), 1, hook_events=True)
+
+    dec_bytes = decode_bytes(out, inp, 1, r, ngroups)
+    value = dec_bytes / (t_dec * 1e-3) / 1e9
+    kb = gemv_kernel_bytes(out, inp, 1, r, ngroups)
+    k_ms = float(np.mean(k_dec))
+    achieved = kb / (k_ms * 1e-3) / 1e9
+    ffwd, fbwd = train_flops(out, inp, Mtrain, r)
+    tflops = (ffwd + fbwd) / (t_tr * 1e-3) / 1e12
+    gemm_flops = 2 * Mtrain * out * (inp + r)
+    kf_ms = float(np.mean(fwd_k))
+    dx_flops = 2 * Mtrain * out * inp + 2 * Mtrain * r * inp
+    kd_ms = float(np.mean(bwd_k))
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(t_dec, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random W0 of the workload's distribution, no trained weights)",
+        "config": {
+            "workload": "70B MLP 8192->28672 NF4 (block 64) + int8 double quant (group 256), "
+                        "r=64 alpha=128; decode M=1 fwd, training M=4096 fwd+bwd"
+                        if c == 4 else "workload %d (%d -> %d), r=%d" % (c, inp, out, r),
+            "out": out, "in": inp, "r": r, "alpha": sh["alpha"], "M_decode": 1, "M_train": Mtrain,
+            "weight_copies_rotated": len(qs),
+        },
+        "decode_ms": round(t_dec, 5),
+        "decode_GBps": round(value, 2),
+        "train_ms_fwd_bwd": round(t_tr, 4),
+        "train_TFLOPs": round(tflops, 2),
+        "train_frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "fused dequant product, M=1", "kernel_ms": round(k_ms, 5),
+            "algorithmic_bytes_per_launch": kb,
+        },
+        "roofline_train": {
+            "bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "forward_kernel_ms": round(kf_ms, 4),
+            "forward_achieved": round(gemm_flops / (kf_ms * 1e-3) / 1e12, 2),
+            "forward_frac": round(gemm_flops / (kf_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "dx_kernel_ms": round(kd_ms, 4),
+            "dx_achieved": round(dx_flops / (kd_ms * 1e-3) / 1e12, 2),
+            "dx_frac": round(dx_flops / (kd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, w, x1_bits, a_bits, b_bits, scale)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

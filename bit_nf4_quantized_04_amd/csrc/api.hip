@@ -9,6 +9,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -46,6 +47,12 @@ inline bool bad_ptr(const void* p) { return !p || !al16(p); }
 }  // namespace
 
 namespace nf4 {
+void prof_begin(hipStream_t s) {
+    if (g_prof_start && g_prof_stop) (void)hipEventRecord(g_prof_start, s);
+}
+void prof_end(hipStream_t s) {
+    if (g_prof_start && g_prof_stop) (void)hipEventRecord(g_prof_stop, s);
+}
 int launch_status() {
     const hipError_t e = hipGetLastError();
     g_last_hip_error = int(e);
@@ -83,6 +90,13 @@ const char* nf4_strerror(int code) {
 int nf4_version(void) { return NF4QLORA_VERSION; }
 
 int nf4_last_hip_error(void) { return g_last_hip_error; }
+
+int nf4_profile_events(void* start, void* stop) {
+    if ((start == nullptr) != (stop == nullptr)) return NF4_EINVAL;
+    g_prof_start = static_cast<hipEvent_t>(start);
+    g_prof_stop = static_cast<hipEvent_t>(stop);
+    return NF4_OK;
+}
 
 int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg, size_t* code_bytes,
                       size_t* scale_bytes, size_t* group_bytes) {

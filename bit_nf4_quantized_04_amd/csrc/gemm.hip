@@ -487,7 +487,10 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {
-        return gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1);
+        prof_begin(st);
+        const int rc0 = gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1);
+        prof_end(st);
+        return rc0;
     }
     float* u = u_out ? u_out : reinterpret_cast<float*>(w + fp.off_u);
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
@@ -495,7 +498,10 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     if (rc) return rc;
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};
-    return gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1);
+    prof_begin(st);
+    rc = gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1);
+    prof_end(st);
+    return rc;
 }
 
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M, const uint16_t* A,
@@ -552,8 +558,10 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
+        prof_begin(st);
         rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out,
                   LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1);
+        prof_end(st);
         if (rc) return rc;
     }
     return NF4_OK;
@@ -569,8 +577,11 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
                        scales, ids, su);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
-    return gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
-                OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1);
+    prof_begin(st);
+    const int rc = gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
+                        OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1);
+    prof_end(st);
+    return rc;
 }
 
 }  // namespace nf4

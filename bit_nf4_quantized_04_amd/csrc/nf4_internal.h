@@ -37,6 +37,9 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M,
                   const uint16_t* A, const uint16_t* B, int r, float scale, const float* u,
                   uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t s);
+// Profiling hook: records the caller's events around the dominant kernel.
+void prof_begin(hipStream_t s);
+void prof_end(hipStream_t s);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);
 

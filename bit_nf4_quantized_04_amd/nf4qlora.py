@@ -51,6 +51,7 @@ _SIGS = {
     "nf4_strerror": (C.c_char_p, [C.c_int]),
     "nf4_version": (C.c_int, []),
     "nf4_last_hip_error": (C.c_int, []),
+    "nf4_profile_events": (C.c_int, [_P, _P]),
     "nf4_storage_sizes": (C.c_int, [_I64, _I64, C.POINTER(nf4_config), C.POINTER(C.c_size_t),
                                     C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "nf4_quantize": (C.c_int, [_P, _I64, _I64, C.POINTER(nf4_config), _P, _P, _P, _P, _P]),
@@ -122,6 +123,50 @@ def nf4_storage_sizes(rows: int, cols: int, double_quant: bool, dq_group: int = 
 
 def qlora_workspace_bytes(op: int, rows: int, cols: int, M: int, r: int, n_adapters: int = 0) -> int:
     return int(_lib.qlora_workspace_bytes(op, rows, cols, M, r, n_adapters))
+
+
+def nf4_profile_events(start=None, stop=None) -> None:
+    """Record a pair of raw hipEvent_t handles (ints) around the dominant
+    kernel of later layer calls (None, None disables)."""
+    _check(_lib.nf4_profile_events(None if start is None else C.c_void_p(start),
+                                   None if stop is None else C.c_void_p(stop)),
+           "nf4_profile_events")
+
+
+class HipEvents:
+    """Minimal raw HIP event helper (the runtime torch loaded), for timing
+    kernels that the library launches on the current stream."""
+
+    def __init__(self):
+        import glob
+
+        import torch as _t
+
+        cands = glob.glob(os.path.join(os.path.dirname(_t.__file__), "lib", "libamdhip64.so*"))
+        self.rt = C.CDLL(cands[0])
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+
+    def create(self) -> int:
+        e = C.c_void_p()
+        if self.rt.hipEventCreate(C.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def record(self, ev: int, stream=None) -> None:
+        if self.rt.hipEventRecord(C.c_void_p(ev), _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        f = C.c_float()
+        if self.rt.hipEventElapsedTime(C.byref(f), C.c_void_p(a), C.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, ev: int) -> None:
+        self.rt.hipEventDestroy(C.c_void_p(ev))
 
 
 # ---------------------------------------------------------------- quantized W

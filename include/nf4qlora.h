@@ -168,6 +168,14 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
                           const float* u, uint16_t* dX, float* dA, float* dB,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Profiling hook (for benchmarks; not thread-safe).  When both are non-NULL,
+ * `start` and `stop` (hipEvent_t handles owned by the caller) are recorded on
+ * the call's stream immediately before and after the dominant kernel of every
+ * later qlora_linear_forward / _multi (the fused dequant product) and
+ * qlora_linear_backward (the fused dequant dX product), so
+ * hipEventElapsedTime gives that kernel's duration.  NULL, NULL disables. */
+int nf4_profile_events(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

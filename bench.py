@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--workload", default="70b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=5)
+    ap.add_argument("--only", choices=["decode", "train"], default=None,
+                    help="profile one pass only (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the layer's multi-GPU sharding is a design "
@@ -185,6 +187,11 @@ def main():
 
     # whole-step timing (no hook), then the dominant kernel with the hook
     K, W = args.steps, args.warmup
+    if args.only:
+        step = decode_step if args.only == "decode" else train_step
+        t, _ = timed(step, K, W)
+        print("%s pass: %.4f ms/step over %d steps" % (args.only, t, K), flush=True)
+        return
     t_dec, _ = timed(decode_step, K, W)
     _, k_dec = timed(decode_step, K, 1, hook_events=True)
     t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))

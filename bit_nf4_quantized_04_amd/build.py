@@ -32,6 +32,7 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-ffp-contract=fast",
+    "-fno-strict-aliasing",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]

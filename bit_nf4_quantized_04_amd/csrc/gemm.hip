@@ -394,7 +394,9 @@ struct FwdPlan {
     size_t off_u, off_ext, off_part, total;
 };
 
-FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
+// Workspace of the GEMM-path down-projection: u, its bf16 hi/lo extension,
+// split-K partials.
+FwdPlan plan_down(int64_t rows, int64_t cols, int64_t M, int r) {
     FwdPlan p{};
     size_t o = 0;
     if (r > 0) {
@@ -409,6 +411,15 @@ FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
     return p;
 }
 
+FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
+    if (M <= nf4::kSkinnyMaxM) {  // decode path: only u
+        FwdPlan p{};
+        p.total = nf4::skinny_ws_bytes(M, r);
+        return p;
+    }
+    return plan_down(rows, cols, M, r);
+}
+
 struct BwdPlan {
     FwdPlan f;       // recompute of u when it is not supplied
     int Zdu, Zdb, Zda;
@@ -417,7 +428,7 @@ struct BwdPlan {
 
 BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     BwdPlan p{};
-    p.f = plan_forward(rows, cols, M, r);
+    p.f = plan_down(rows, cols, M, r);
     size_t o = p.f.total;
     p.off_uh = o; o = nf4::align256(o + size_t(M) * r * 2);
     p.off_ul = o; o = nf4::align256(o + size_t(M) * r * 2);
@@ -484,6 +495,8 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     const FwdPlan fp = plan_forward(q.rows, q.cols, M, r);
     if (ws_bytes < fp.total || (fp.total && !ws)) return NF4_EWORKSPACE;
     char* w = static_cast<char*>(ws);
+    if (M <= kSkinnyMaxM)
+        return forward_skinny(q, x, M, A, B, r, scale, h, u_out ? u_out : reinterpret_cast<float*>(w), st);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {

@@ -40,6 +40,11 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
 // Profiling hook: records the caller's events around the dominant kernel.
 void prof_begin(hipStream_t s);
 void prof_end(hipStream_t s);
+// Decode path (M <= kSkinnyMaxM): u kernel + fused dequant-GEMV kernel.
+constexpr int64_t kSkinnyMaxM = 16;
+size_t skinny_ws_bytes(int64_t M, int r);
+int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+                   int r, float scale, uint16_t* h, float* u, hipStream_t st);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);
 

@@ -23,6 +23,7 @@ int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
     if (t->cfg.double_quant && t->cfg.dq_group < 1) return NF4_EUNSUPPORTED;
     const int64_t n = t->rows * t->cols;
     if (linear ? (t->cols % 64 != 0) : (n % 64 != 0)) return NF4_ESHAPE;
+    if (n / 64 >= (int64_t(1) << 31)) return NF4_EINVAL;  // block indices are 32-bit
     if (n > 0) {
         if (!t->codes || !al16(t->codes)) return NF4_EINVAL;
         if (t->cfg.double_quant) {
@@ -39,6 +40,9 @@ int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
     v->cols = t->cols;
     v->dq = t->cfg.double_quant;
     v->group = t->cfg.double_quant ? t->cfg.dq_group : 1;
+    v->gshift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == v->group) v->gshift = sh;
     return NF4_OK;
 }
 
@@ -47,11 +51,9 @@ inline bool bad_ptr(const void* p) { return !p || !al16(p); }
 }  // namespace
 
 namespace nf4 {
-void prof_begin(hipStream_t s) {
-    if (g_prof_start && g_prof_stop) (void)hipEventRecord(g_prof_start, s);
-}
-void prof_end(hipStream_t s) {
-    if (g_prof_start && g_prof_stop) (void)hipEventRecord(g_prof_stop, s);
+void prof_events(hipEvent_t* start, hipEvent_t* stop) {
+    *start = g_prof_start;
+    *stop = g_prof_stop;
 }
 int launch_status() {
     const hipError_t e = hipGetLastError();

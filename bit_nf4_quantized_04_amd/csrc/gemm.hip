@@ -297,11 +297,15 @@ __global__ __launch_bounds__(NT) void k_gemm(LA1 la1, LB1 lb1, int64_t K1, LA2 l
 
 template <class LA1, class LB1, class LA2, class LB2, class OUT>
 int gemm(hipStream_t st, int64_t Mr, int64_t Nc, LA1 la1, LB1 lb1, int64_t K1, LA2 la2, LB2 lb2,
-         int64_t K2, OUT out, int splits) {
+         int64_t K2, OUT out, int splits, bool dominant = false) {
     if (Mr <= 0 || Nc <= 0) return NF4_OK;
     dim3 grid(unsigned(nf4::cdiv(Nc, BN)), unsigned(nf4::cdiv(Mr, BM)), unsigned(splits));
-    hipLaunchKernelGGL((k_gemm<LA1, LB1, LA2, LB2, OUT>), grid, dim3(NT), 0, st, la1, lb1, K1, la2,
-                       lb2, K2, out, Mr, Nc, splits);
+    if (dominant)
+        nf4::launch_dominant(k_gemm<LA1, LB1, LA2, LB2, OUT>, grid, dim3(NT), 0, st, la1, lb1, K1,
+                             la2, lb2, K2, out, Mr, Nc, splits);
+    else
+        hipLaunchKernelGGL((k_gemm<LA1, LB1, LA2, LB2, OUT>), grid, dim3(NT), 0, st, la1, lb1, K1,
+                           la2, lb2, K2, out, Mr, Nc, splits);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : nf4::launch_status();
 }
 
@@ -412,7 +416,7 @@ FwdPlan plan_down(int64_t rows, int64_t cols, int64_t M, int r) {
 }
 
 FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
-    if (M <= nf4::kSkinnyMaxM) {  // decode path: only u
+    if (M <= nf4::kSkinnyMaxM && r <= nf4::kSkinnyMaxR) {  // decode path: u partials
         FwdPlan p{};
         p.total = nf4::skinny_ws_bytes(M, r);
         return p;
@@ -495,15 +499,12 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     const FwdPlan fp = plan_forward(q.rows, q.cols, M, r);
     if (ws_bytes < fp.total || (fp.total && !ws)) return NF4_EWORKSPACE;
     char* w = static_cast<char*>(ws);
-    if (M <= kSkinnyMaxM)
-        return forward_skinny(q, x, M, A, B, r, scale, h, u_out ? u_out : reinterpret_cast<float*>(w), st);
+    if (M <= kSkinnyMaxM && r <= kSkinnyMaxR)
+        return forward_skinny(q, x, M, A, B, r, scale, h, u_out, reinterpret_cast<float*>(w), st);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {
-        prof_begin(st);
-        const int rc0 = gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1);
-        prof_end(st);
-        return rc0;
+        return gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1, true);
     }
     float* u = u_out ? u_out : reinterpret_cast<float*>(w + fp.off_u);
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
@@ -511,10 +512,7 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     if (rc) return rc;
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};
-    prof_begin(st);
-    rc = gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1);
-    prof_end(st);
-    return rc;
+    return gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1, true);
 }
 
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M, const uint16_t* A,
@@ -571,10 +569,8 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
-        prof_begin(st);
         rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out,
-                  LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1);
-        prof_end(st);
+                  LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1, true);
         if (rc) return rc;
     }
     return NF4_OK;
@@ -590,11 +586,8 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
                        scales, ids, su);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
-    prof_begin(st);
-    const int rc = gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
-                        OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1);
-    prof_end(st);
-    return rc;
+    return gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
+                OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1, true);
 }
 
 }  // namespace nf4

@@ -1,6 +1,7 @@
 // nf4_internal.h -- host-side declarations shared by the library's .hip files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -20,6 +21,7 @@ struct QView {  // a validated nf4_tensor
     int64_t rows, cols;
     int dq;        // 0/1
     int group;     // dq_group
+    int gshift;    // log2(group) when group is a power of two, else -1
 };
 
 int launch_quantize(const float* W, int64_t n, int dq, int group, uint8_t* codes, float* absmax,
@@ -37,14 +39,27 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M,
                   const uint16_t* A, const uint16_t* B, int r, float scale, const float* u,
                   uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t s);
-// Profiling hook: records the caller's events around the dominant kernel.
-void prof_begin(hipStream_t s);
-void prof_end(hipStream_t s);
-// Decode path (M <= kSkinnyMaxM): u kernel + fused dequant-GEMV kernel.
+// Profiling hook: the caller's events (or null) that bracket the dominant
+// kernel of a call; launch_dominant attaches them to the dispatch itself.
+void prof_events(hipEvent_t* start, hipEvent_t* stop);
+
+template <typename Kernel, typename... Args>
+void launch_dominant(Kernel kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                     Args... args) {
+    hipEvent_t a, b;
+    prof_events(&a, &b);
+    if (a && b)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, b, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+}
+// Decode path (M <= kSkinnyMaxM, r <= kSkinnyMaxR): partial down-projection
+// kernel + fused dequant-GEMV kernel.
 constexpr int64_t kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxR = 64;
 size_t skinny_ws_bytes(int64_t M, int r);
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-                   int r, float scale, uint16_t* h, float* u, hipStream_t st);
+                   int r, float scale, uint16_t* h, float* u_out, float* part, hipStream_t st);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);
 

@@ -391,7 +391,9 @@ inline int choose_splits(int64_t tiles, int64_t ksteps) {
     return int(z);
 }
 
-inline int ext_cols(int r) { return int(nf4::cdiv(2 * r, BK) * BK); }
+// Columns of the LoRA K-extension [hi | lo | 0 pad]: a multiple of 64 so both
+// GEMM kernels step through it in whole K tiles.
+inline int ext_cols(int r) { return int(nf4::cdiv(2 * r, 64) * 64); }
 
 struct FwdPlan {
     int Zu;  // split-K of the down-projection
@@ -504,12 +506,14 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {
+        if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, nullptr, 0, nullptr, 0, h, st);
         return gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1, true);
     }
     float* u = u_out ? u_out : reinterpret_cast<float*>(w + fp.off_u);
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
     int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext);
     if (rc) return rc;
+    if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};
     return gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1, true);
@@ -569,8 +573,12 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
-        rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out,
-                  LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1, true);
+        if (use_big_gemm(M, in))
+            rc = dx_big(q, dH, M, duext, KL, A, r, dX, st);
+        else
+            rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out,
+                      LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1,
+                      true);
         if (rc) return rc;
     }
     return NF4_OK;

@@ -60,6 +60,12 @@ constexpr int kSkinnyMaxR = 64;
 size_t skinny_ws_bytes(int64_t M, int r);
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                    int r, float scale, uint16_t* h, float* u_out, float* part, hipStream_t st);
+// Large-M fused dequant-GEMMs (256 x 256 tiles).
+bool use_big_gemm(int64_t Mr, int64_t Nc);
+int forward_big(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
+                const uint16_t* B, int r, uint16_t* h, hipStream_t st);
+int dx_big(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL,
+           const uint16_t* A, int r, uint16_t* dX, hipStream_t st);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);
 

@@ -203,3 +203,38 @@ def test_multi_adapter_workload(F):
     wb = O.compute_weight(ref, w.shape)
     href = O.forward_multi(wb, x, ab, bb, scales.astype(np.float64), ids)
     U.assert_close("h", U.bf16_to_f64(h), href)
+
+
+# Shapes that take the large-tile (256 x 256) kernels: at least 512 output
+# tiles, ragged in every dimension, and cheap for the oracle.
+@pytest.mark.parametrize("M,out,inp,r", [(4000, 8200, 192, 16), (4096, 8192, 128, 0)])
+def test_forward_large_tiles(F, M, out, inp, r):
+    import torch
+
+    w, x, a, b, _ = _case(M + out, M, out, inp, max(r, 1))
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    if r:
+        h = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), 2.0)
+    else:
+        h = F.qlora_linear_forward(q, U.bf(x), None, None, 2.0)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    href = O._bf(x) @ wb.T
+    if r:
+        href, _ = O.forward(wb, x, a, b, 2.0)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+
+
+@pytest.mark.parametrize("M,out,inp,r", [(4000, 500, 8256, 16), (4096, 256, 8192, 64)])
+def test_backward_large_tiles(F, M, out, inp, r):
+    import torch
+
+    w, x, a, b, dh = _case(M + inp, M, out, inp, r)
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    dX, dA, dB = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), 0.5)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    g = O.backward(wb, x, dh, a, b, 0.5)
+    U.assert_close("dX", U.bf16_to_f64(dX), g["dX"])
+    U.assert_close("dA", dA.cpu().numpy(), g["dA"])
+    U.assert_close("dB", dB.cpu().numpy(), g["dB"])

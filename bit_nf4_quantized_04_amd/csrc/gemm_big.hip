@@ -1,6 +1,8 @@
 // gemm_big.hip -- the large-M fused dequant-GEMM (prefill / training):
 // 256 x 256 output tiles, K in steps of 64 (one NF4 block per weight row),
-// four waves of 128 x 128, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// eight waves of 128 (M) x 64 (N), v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation; two waves per SIMD so one wave's loads, dequantization and
+// LDS traffic overlap the other's MFMAs.
 //
 // Layer: h = x Wb^T + s (x A^T) B^T ("QLoRA Finetuner", "1. Low-Rank
 // Adaptation"; "QLoRA explained", "The LoRA adapter path"), and the dX
@@ -20,7 +22,7 @@ using namespace nf4dev;
 namespace {
 
 constexpr int TM = 256, TN = 256, TK = 64, TKP = TK + 8;
-constexpr int BT = 256;  // threads
+constexpr int BT = 512;  // threads: 8 waves, 2 per SIMD
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -32,8 +34,9 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f
 struct BigSmem {
     uint16_t A[2][TM][TKP];
     uint16_t B[2][TN][TKP];
-    float lv[16];
-    float q127[128];
+    // Per-lane 16-entry bf16 product tables of the B producers (waves 0-3):
+    // [wave][entry][lane] dword slots, entry in the low half (16-bit typed).
+    uint16_t tb[4][16][128];
 };
 
 typedef uint16_t (*Tile)[TKP];
@@ -45,17 +48,19 @@ typedef uint16_t (*Tile)[TKP];
 struct NoLoad {
     struct R {};
     __device__ void load(R&, int64_t, int64_t) const {}
-    __device__ void store(const R&, Tile, int64_t, int64_t, const BigSmem&) const {}
+    __device__ void store(const R&, Tile, int64_t, int64_t, BigSmem&) const {}
 };
 
-// element (row, k) = p[row*ld + k]
+// element (row, k) = p[row*ld + k].  Producer waves 4-7: thread 256 + t loads
+// row t/8 + 32i (i = 0..7), 16-byte chunk t%8.
 struct RowsBF16 {
     const uint16_t* p;
     int64_t rows, K, ld;
     bool vec;  // ld % 8 == 0 and p 16-byte aligned
     struct R { uint4 v[8]; };
     __device__ void load(R& r, int64_t row0, int64_t k0) const {
-        const int t = threadIdx.x, ch = t & 7;
+        if (threadIdx.x < 256) return;  // wave-uniform
+        const int t = threadIdx.x - 256, ch = t & 7;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t row = row0 + (t >> 3) + 32 * i, k = k0 + ch * 8;
@@ -75,24 +80,33 @@ struct RowsBF16 {
             r.v[i] = v;
         }
     }
-    __device__ void store(const R& r, Tile t, int64_t, int64_t, const BigSmem&) const {
-        const int tid = threadIdx.x, ch = tid & 7;
+    __device__ void store(const R& r, Tile t, int64_t, int64_t, BigSmem&) const {
+        if (threadIdx.x < 256) return;
+        const int tid = threadIdx.x - 256, ch = tid & 7;
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&t[(tid >> 3) + 32 * i][ch * 8]) = r.v[i];
     }
 };
 
-__device__ __forceinline__ float blk_scale(const nf4::QView& q, uint32_t qb, float cg,
-                                           const BigSmem& sm) {
-    return q.dq ? __fmul_rn(sm.q127[qb & 127u], cg) : __builtin_bit_cast(float, qb);
+// Scale of a block from its raw loads: fl32(fl32(q/127) * c_g) or the fp32 absmax.
+__device__ __forceinline__ float blk_scale(const nf4::QView& q, uint32_t qb, float cg) {
+    return q.dq ? __fmul_rn(q_over_127(int(qb & 127u)), cg) : __builtin_bit_cast(float, qb);
 }
 
-// NF4 weight rows (forward): element (n, k) = Wb[n][k]; thread t owns the
-// 64-element block of row row0 + t in this K step.
+// The 16 fp32 levels (constant-folded when e is a constant).
+__device__ __forceinline__ float level(int e) { return bits_f(level_bits(e)); }
+
+// NF4 weight rows (forward): element (n, k) = Wb[n][k].  Producer waves 0-3:
+// thread t < 256 owns the 64-element block of row row0 + t in this K step.
+// It writes that block's 16 products bf16(s~ T[c]) to its own table column
+// and looks every weight up there (two lookups = one packed bf16 pair), so
+// each weight costs about two VALU operations instead of a multiply and a
+// conversion.
 struct NF4Rows {
     nf4::QView q;
     struct R { uint4 c0, c1; uint32_t qb; float cg; bool ok; };
     __device__ void load(R& r, int64_t row0, int64_t k0) const {
+        if (threadIdx.x >= 256) return;  // wave-uniform
         const int64_t row = row0 + threadIdx.x;
         r.ok = row < q.rows;
         const int64_t crow = r.ok ? row : q.rows - 1;
@@ -109,39 +123,58 @@ struct NF4Rows {
             r.cg = 0.0f;
         }
     }
-    __device__ void store(const R& r, Tile t, int64_t, int64_t, const BigSmem& sm) const {
-        const float s = r.ok ? blk_scale(q, r.qb, r.cg, sm) : 0.0f;
+    __device__ void store(const R& r, Tile t, int64_t, int64_t, BigSmem& sm) const {
+        if (threadIdx.x >= 256) return;  // wave-uniform
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        const float s = r.ok ? blk_scale(q, r.qb, r.cg) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const uint32_t pk = pack_bf16x2(__fmul_rn(s, level(e)), __fmul_rn(s, level(e + 1)));
+            sm.tb[w][e][2 * l] = uint16_t(pk);
+            sm.tb[w][e + 1][2 * l] = uint16_t(pk >> 16);
+        }
+        // byte offset of tb[w][e][l] from tb[0]: e*256 + w*4096 + l*4
+        const char* tbase = reinterpret_cast<const char*>(&sm.tb[0][0][0]);
+        const uint32_t laneb = uint32_t(l) * 4u, P = uint32_t(w) * 0x10101010u;
         const uint32_t cw[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
         uint16_t* dst = &t[threadIdx.x][0];
 #pragma unroll
         for (int d = 0; d < 8; d += 2) {
-            uint32_t w[8];
+            uint32_t w8[8];
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
                 const uint32_t cd = cw[d + dd];
+                const uint32_t clo = (cd & 0x0F0F0F0Fu) | P;
+                const uint32_t chi = ((cd >> 4) & 0x0F0F0F0Fu) | P;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    w[dd * 4 + j] = pack_bf16x2(__fmul_rn(s, sm.lv[(cd >> (8 * j + 4)) & 15u]),
-                                                __fmul_rn(s, sm.lv[(cd >> (8 * j)) & 15u]));
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t sel = 0x0C0C0000u | ((4u + j) << 8);
+                    const uint32_t vh = *reinterpret_cast<const uint16_t*>(
+                        tbase + __builtin_amdgcn_perm(chi, laneb, sel));
+                    const uint32_t vl = *reinterpret_cast<const uint16_t*>(
+                        tbase + __builtin_amdgcn_perm(clo, laneb, sel));
+                    w8[dd * 4 + j] = vh | (vl << 16);
+                }
             }
-            *reinterpret_cast<uint4*>(dst + d * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-            *reinterpret_cast<uint4*>(dst + d * 8 + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+            *reinterpret_cast<uint4*>(dst + d * 8) = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+            *reinterpret_cast<uint4*>(dst + d * 8 + 8) = make_uint4(w8[4], w8[5], w8[6], w8[7]);
         }
     }
 };
 
 // NF4 weight transposed (dX): tile row n = weight column, k = weight row,
 // element (n, k) = Wb[k][n].  Thread t: weight rows k0 + 2(t%32) and +1, and
-// the 8-column chunks t/32 + 8i (i = 0..3); it writes (Wb[k][n], Wb[k+1][n])
-// pairs, consecutive lanes to consecutive LDS dwords.
+// two 8-column chunks; it writes (Wb[k][n], Wb[k+1][n])
+// pairs, consecutive lanes to consecutive LDS dwords.  (512 threads: chunks
+// t/32 + 16i, i = 0..1.)
 struct NF4Cols {
     nf4::QView q;
-    struct R { uint32_t c[4][2]; uint32_t qb[4][2]; float cg[4][2]; bool ok[4][2]; };
+    struct R { uint32_t c[2][2]; uint32_t qb[2][2]; float cg[2][2]; bool ok[2][2]; };
     __device__ void load(R& r, int64_t row0, int64_t k0) const {
         const int kp = threadIdx.x & 31, dc = threadIdx.x >> 5;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t col = row0 + (dc + 8 * i) * 8;
+        for (int i = 0; i < 2; ++i) {
+            const int64_t col = row0 + (dc + 16 * i) * 8;
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
                 const int64_t wr = k0 + 2 * kp + rr;
@@ -160,22 +193,22 @@ struct NF4Cols {
             }
         }
     }
-    __device__ void store(const R& r, Tile t, int64_t, int64_t, const BigSmem& sm) const {
+    __device__ void store(const R& r, Tile t, int64_t, int64_t, BigSmem&) const {
         const int kp = threadIdx.x & 31, dc = threadIdx.x >> 5;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             float w[2][8];
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const float s = r.ok[i][rr] ? blk_scale(q, r.qb[i][rr], r.cg[i][rr], sm) : 0.0f;
+                const float s = r.ok[i][rr] ? blk_scale(q, r.qb[i][rr], r.cg[i][rr]) : 0.0f;
                 const uint32_t cd = r.c[i][rr];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    w[rr][2 * j] = __fmul_rn(s, sm.lv[(cd >> (8 * j + 4)) & 15u]);
-                    w[rr][2 * j + 1] = __fmul_rn(s, sm.lv[(cd >> (8 * j)) & 15u]);
+                    w[rr][2 * j] = __fmul_rn(s, bits_f(level_bits((cd >> (8 * j + 4)) & 15u)));
+                    w[rr][2 * j + 1] = __fmul_rn(s, bits_f(level_bits((cd >> (8 * j)) & 15u)));
                 }
             }
-            const int n0 = (dc + 8 * i) * 8;
+            const int n0 = (dc + 16 * i) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 *reinterpret_cast<uint32_t*>(&t[n0 + e][2 * kp]) = pack_bf16x2(w[0][e], w[1][e]);
@@ -190,11 +223,11 @@ struct DupRows {
     int r;
     struct R {};
     __device__ void load(R&, int64_t, int64_t) const {}
-    __device__ void store(const R&, Tile t, int64_t row0, int64_t k0, const BigSmem&) const {
-        const int64_t n = row0 + threadIdx.x;
-        for (int kk = 0; kk < TK; ++kk) {
+    __device__ void store(const R&, Tile t, int64_t row0, int64_t k0, BigSmem&) const {
+        const int64_t n = row0 + (threadIdx.x >> 1);
+        for (int kk = (threadIdx.x & 1) * 32; kk < (threadIdx.x & 1) * 32 + 32; ++kk) {
             const int64_t c = k0 + kk;
-            t[threadIdx.x][kk] = (n < rows && c < 2 * r) ? B[n * r + (c % r)] : uint16_t(0);
+            t[threadIdx.x >> 1][kk] = (n < rows && c < 2 * r) ? B[n * r + (c % r)] : uint16_t(0);
         }
     }
 };
@@ -206,13 +239,29 @@ struct DupCols {
     int r;
     struct R {};
     __device__ void load(R&, int64_t, int64_t) const {}
-    __device__ void store(const R&, Tile t, int64_t row0, int64_t k0, const BigSmem&) const {
-        const int64_t n = row0 + threadIdx.x;
-        for (int kk = 0; kk < TK; ++kk) {
+    __device__ void store(const R&, Tile t, int64_t row0, int64_t k0, BigSmem&) const {
+        const int64_t n = row0 + (threadIdx.x >> 1);
+        for (int kk = (threadIdx.x & 1) * 32; kk < (threadIdx.x & 1) * 32 + 32; ++kk) {
             const int64_t c = k0 + kk;
-            t[threadIdx.x][kk] = (n < cols && c < 2 * r) ? A[(c % r) * cols + n] : uint16_t(0);
+            t[threadIdx.x >> 1][kk] = (n < cols && c < 2 * r) ? A[(c % r) * cols + n] : uint16_t(0);
         }
     }
+};
+
+// Register staging of the two K phases; one buffer when both phases use the
+// same loader type (their live ranges never overlap).
+template <class L1, class L2>
+struct Staging {
+    typename L1::R r1;
+    typename L2::R r2;
+    __device__ typename L1::R& first() { return r1; }
+    __device__ typename L2::R& second() { return r2; }
+};
+template <class L>
+struct Staging<L, L> {
+    typename L::R r;
+    __device__ typename L::R& first() { return r; }
+    __device__ typename L::R& second() { return r; }
 };
 
 // ------------------------------------------------------------------ kernel
@@ -222,9 +271,7 @@ __global__ __launch_bounds__(BT, 1) void k_gemm_big(LA1 la1, LB1 lb1, int64_t K1
                                                     int64_t ldo, int64_t Mr, int64_t Nc) {
     __shared__ __attribute__((aligned(16))) BigSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    if (tid < 16) sm.lv[tid] = bits_f(level_bits(tid));
-    if (tid < 128) sm.q127[tid] = q_over_127(tid);
+    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
 
     // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs;
     // give each XCD a contiguous run of tiles, walked in groups of 4 M-tiles
@@ -239,61 +286,65 @@ __global__ __launch_bounds__(BT, 1) void k_gemm_big(LA1 la1, LB1 lb1, int64_t K1
     const int64_t tm = first + (lin % gsz) % gm, tn = (lin % gsz) / gm;
     const int64_t m0 = tm * TM, n0 = tn * TN;
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int64_t S1 = (K1 + TK - 1) / TK, S2 = (K2 + TK - 1) / TK, S = S1 + S2;
-    typename LA1::R ra1;
-    typename LB1::R rb1;
-    typename LA2::R ra2;
-    typename LB2::R rb2;
+    Staging<LA1, LA2> ra;
+    Staging<LB1, LB2> rb;
     auto load = [&](int64_t s) {
         if (s < S1) {
-            la1.load(ra1, m0, s * TK);
-            lb1.load(rb1, n0, s * TK);
+            la1.load(ra.first(), m0, s * TK);
+            lb1.load(rb.first(), n0, s * TK);
         } else {
-            la2.load(ra2, m0, (s - S1) * TK);
-            lb2.load(rb2, n0, (s - S1) * TK);
+            la2.load(ra.second(), m0, (s - S1) * TK);
+            lb2.load(rb.second(), n0, (s - S1) * TK);
         }
     };
     auto store = [&](int64_t s, int buf) {
         if (s < S1) {
-            la1.store(ra1, sm.A[buf], m0, s * TK, sm);
-            lb1.store(rb1, sm.B[buf], n0, s * TK, sm);
+            la1.store(ra.first(), sm.A[buf], m0, s * TK, sm);
+            lb1.store(rb.first(), sm.B[buf], n0, s * TK, sm);
         } else {
-            la2.store(ra2, sm.A[buf], m0, (s - S1) * TK, sm);
-            lb2.store(rb2, sm.B[buf], n0, (s - S1) * TK, sm);
+            la2.store(ra.second(), sm.A[buf], m0, (s - S1) * TK, sm);
+            lb2.store(rb.second(), sm.B[buf], n0, (s - S1) * TK, sm);
         }
     };
-    __syncthreads();  // level / scale tables
     if (S > 0) {
         load(0);
         store(0, 0);
     }
     __syncthreads();
     const int rl = lane & 31, kh = 8 * (lane >> 5);
+    auto mfma_k = [&](int buf, int kk) {
+        u32x4_t a[4], bb[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = *reinterpret_cast<const u32x4_t*>(&sm.A[buf][wm * 128 + i * 32 + rl][kk + kh]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bb[j] = *reinterpret_cast<const u32x4_t*>(&sm.B[buf][wn * 64 + j * 32 + rl][kk + kh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
+    };
+    // The next step's dequantization and LDS stores are issued between this
+    // step's MFMA k-slices so the matrix unit stays busy while they run.
     for (int64_t s = 0; s < S; ++s) {
         const int buf = int(s & 1);
-        if (s + 1 < S) load(s + 1);
-#pragma unroll
-        for (int kk = 0; kk < TK; kk += 16) {
-            u32x4_t a[4], bb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = *reinterpret_cast<const u32x4_t*>(&sm.A[buf][wm * 128 + i * 32 + rl][kk + kh]);
-                bb[i] = *reinterpret_cast<const u32x4_t*>(&sm.B[buf][wn * 128 + i * 32 + rl][kk + kh]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
-        }
-        if (s + 1 < S) store(s + 1, buf ^ 1);
+        const bool more = s + 1 < S;
+        if (more) load(s + 1);
+        mfma_k(buf, 0);
+        mfma_k(buf, 16);
+        if (more) store(s + 1, buf ^ 1);
+        mfma_k(buf, 32);
+        mfma_k(buf, 48);
         __syncthreads();
     }
     // D layout of the 32x32 MFMA: lane holds column lane%32 and rows
@@ -301,11 +352,11 @@ __global__ __launch_bounds__(BT, 1) void k_gemm_big(LA1 la1, LB1 lb1, int64_t K1
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+                const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
                 if (m < Mr && n < Nc) out[m * ldo + n] = to_bf16(acc[i][j][v]);
             }
 }

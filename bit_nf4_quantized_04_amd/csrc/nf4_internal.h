@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/nf4qlora.h"
+#include "nf4qlora.h"  // from include/ (on the -I path)
 
 namespace nf4 {
 

@@ -502,7 +502,7 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     if (ws_bytes < fp.total || (fp.total && !ws)) return NF4_EWORKSPACE;
     char* w = static_cast<char*>(ws);
     if (M <= kSkinnyMaxM && r <= kSkinnyMaxR)
-        return forward_skinny(q, x, M, A, B, r, scale, h, u_out, reinterpret_cast<float*>(w), st);
+        return forward_skinny(q, x, M, A, B, r, scale, h, u_out, w, st);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {

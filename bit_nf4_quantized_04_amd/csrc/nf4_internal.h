@@ -59,7 +59,7 @@ constexpr int64_t kSkinnyMaxM = 16;
 constexpr int kSkinnyMaxR = 64;
 size_t skinny_ws_bytes(int64_t M, int r);
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-                   int r, float scale, uint16_t* h, float* u_out, float* part, hipStream_t st);
+                   int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st);
 // Large-M fused dequant-GEMMs (256 x 256 tiles).
 bool use_big_gemm(int64_t Mr, int64_t Nc);
 int forward_big(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,

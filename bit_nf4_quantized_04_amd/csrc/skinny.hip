@@ -15,6 +15,9 @@
 // distinct banks-by-lane, i.e. no bank conflicts.  Two lookups (high and low
 // nibble of a code byte) give one packed bf16 pair, i.e. one MFMA B register.
 // The block's weights are read from HBM exactly once, as 2 x 16 B per lane.
+#include <algorithm>
+#include <atomic>
+
 #include "nf4_device.h"
 #include "nf4_internal.h"
 
@@ -32,8 +35,11 @@ constexpr int DOWN_SPLIT = 16;
 
 __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__ x, int M,
                                                     int64_t K, const uint16_t* __restrict__ A,
-                                                    int r, float* __restrict__ part) {
+                                                    int r, float* __restrict__ part,
+                                                    unsigned* __restrict__ ctr) {
     __shared__ float red[4][16][17];
+    if (ctr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ctr = 0u;
+    if (r <= 0) return;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int i = l & 15, g = l >> 4;
     const int c = blockIdx.x * 16 + i;  // adapter row of this lane's B column
@@ -249,28 +255,52 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
 // product.  The off-diagonal entries are discarded (M = 1 wastes 15/16 of the
 // MFMA either way).  x at the lane's block is loaded once per wave and reused
 // for every row the wave visits.
-constexpr int G1_ITEMS = 8;  // rows per wave
+//
+// Table slots are 4 bytes: the low half is zero (written once), the high half
+// holds the bf16 product s~*T[e].  A 16-bit read of the high half gives the
+// pair {w, 0} and a 32-bit read of the slot gives {0, w}, so the even and the
+// odd weights of a code byte form two B operands with no packing instruction;
+// the two MFMAs against the same x fragment add both halves of the k range.
+//
+// The rank-r term s*u.B[o] rides on the same diagonal: lane l < r adds one
+// MFMA step whose A fragment is {hi, lo} of s*u[l] (a bf16 pair, so u keeps
+// fp32 precision) and whose B fragment is {B[o][l], B[o][l]}.
+//
+// Work is handed out in chunks of G1_NC rows per wave (a workgroup's four
+// waves are R regions x 4/R row subsets of one chunk).  The grid is the number
+// of resident workgroups; the first chunk of each is its block index, later
+// ones come from an atomic counter, so workgroups on faster memory paths take
+// more chunks and all finish together.  The counter is zeroed by the
+// down-projection kernel launched just before on the same stream.
+constexpr int G1_NC = 2;  // rows per wave per chunk (the ping-pong pair)
 
 template <bool DQ, bool GSH>
-__global__ __launch_bounds__(256) void k_gemv1(nf4::QView q, const uint16_t* __restrict__ x,
-                                               const float* __restrict__ upart, int r,
-                                               const uint16_t* __restrict__ B, float scale,
-                                               uint16_t* __restrict__ h, float* __restrict__ u_out,
-                                               int R) {
-    __shared__ __attribute__((aligned(16))) uint16_t tbl[4][16][128];  // [wave][entry][lane]
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv1(
+    nf4::QView q, const uint16_t* __restrict__ x, const float* __restrict__ upart, int r,
+    const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
+    float* __restrict__ u_out, int R, int nchunks, unsigned* __restrict__ ctr) {
+    __shared__ __attribute__((aligned(16))) uint32_t tbl[4][16][64];  // [wave][entry][lane]
     __shared__ float q127[128];
-    __shared__ float part[4][G1_ITEMS];  // per-wave row partials
-    __shared__ float dlds[4][G1_ITEMS][16];  // diagonal D[i][i] per (wave, row, i)
+    __shared__ float dlds[2][4][G1_NC][16];  // diagonal D[i][i] per (parity, wave, row, i)
     __shared__ float us[64];
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int64_t N = q.rows, K = q.cols;
     const int nkb = int(K / 64);
-    // workgroup: (4 / R) * G1_ITEMS rows; wave w -> region w % R, row subset w / R
-    const int rows_wg = (4 / R) * G1_ITEMS;
-    const int64_t o0 = int64_t(blockIdx.x) * rows_wg;
+    const int S = 4 / R, rows_chunk = S * G1_NC;
     const int rho = w % R, sub = w / R;
     if (DQ && tid < 128) q127[tid] = q_over_127(tid);
+    char* tb = reinterpret_cast<char*>(&tbl[0][0][0]);
+    char* mine = tb + (w * 16 * 64 + l) * 4;  // slot (w, 0, l); entry stride 256 B
+#pragma unroll
+    for (int e = 0; e < 16; ++e) *reinterpret_cast<uint32_t*>(mine + e * 256) = 0u;
+    // u = sum of the down-projection partials, in a fixed order
+    for (int idx = tid; idx < r; idx += 256) {
+        float a = 0.0f;
+        for (int zz = 0; zz < DOWN_SPLIT; ++zz) a += upart[int64_t(zz) * r + idx];
+        us[idx] = a;
+        if (blockIdx.x == 0 && u_out) u_out[idx] = a;
+    }
 
     const int blk = rho * 64 + l;  // this lane's block within a row
     const bool blk_ok = blk < nkb;
@@ -284,28 +314,34 @@ __global__ __launch_bounds__(256) void k_gemv1(nf4::QView q, const uint16_t* __r
     }
     const uint32_t laneb = uint32_t(l) * 4u;
     const uint32_t P = uint32_t(w) * 0x10101010u;
-    const char* tb = reinterpret_cast<const char*>(&tbl[0][0][0]);
+    // nibble mask kept in a VGPR so that (c & mask) | P is one v_and_or_b32
+    uint32_t nmask = 0x0F0F0F0Fu;
+    asm volatile("" : "+v"(nmask));
+    const bool lora = r > 0 && rho == 0;  // wave-uniform: region-0 waves add s*u.B
+    const bool lane_r = l < r;
+    const uint32_t lane_rc = uint32_t(lane_r ? l : 0);  // clamped B column
 
     struct Fetch {  // raw loads only
         uint4 c0, c1;
         uint32_t qb;
         float cg;
+        uint32_t bv;
         bool ok;
     };
-    // rows of this wave: r0 + it, it < G1_ITEMS (wave-uniform); row pointers
-    // advance by one row per item
-    const int64_t r0 = o0 + int64_t(sub) * G1_ITEMS;
-    const uint4* cp0 = reinterpret_cast<const uint4*>(q.codes) + 2 * int64_t(cb);
-    const int64_t row_u4 = K / 32;
-    auto fetch = [&](int it, Fetch& f) {
-        const int64_t row = r0 + it;
+    // byte offsets from wave-uniform bases (32 bits: the launcher keeps the
+    // code array under 4 GB), so every load is base + one VGPR offset
+    const uint32_t row_bytes = uint32_t(K / 2);
+    const uint32_t lane_bytes = uint32_t(cb) * 32u;
+    const char* codes = reinterpret_cast<const char*>(q.codes);
+    const char* bbase = reinterpret_cast<const char*>(B);
+    auto fetch = [&](int64_t row, Fetch& f) {
         const bool rok = row < N;  // uniform
-        const int64_t crow = rok ? row : N - 1;
+        const uint32_t crow = uint32_t(rok ? row : N - 1);
         f.ok = blk_ok && rok;
-        const uint4* cp = cp0 + crow * row_u4;
-        f.c0 = cp[0];
-        f.c1 = cp[1];
-        const uint32_t b = uint32_t(crow) * uint32_t(nkb) + uint32_t(cb);
+        const uint32_t off = crow * row_bytes + lane_bytes;
+        f.c0 = *reinterpret_cast<const uint4*>(codes + off);
+        f.c1 = *reinterpret_cast<const uint4*>(codes + off + 16u);
+        const uint32_t b = crow * uint32_t(nkb) + uint32_t(cb);
         if (DQ) {
             const uint32_t gi = GSH ? (b >> q.gshift) : (b / uint32_t(q.group));
             f.qb = uint32_t(uint8_t(q.qcodes[b]));
@@ -314,94 +350,132 @@ __global__ __launch_bounds__(256) void k_gemv1(nf4::QView q, const uint16_t* __r
             f.qb = __builtin_bit_cast(uint32_t, q.absmax[b]);
             f.cg = 0.0f;
         }
+        // (without an adapter the load reads the codes instead: the same load
+        // count on every path, the value unused)
+        f.bv = *reinterpret_cast<const uint16_t*>(lora ? bbase + (crow * uint32_t(r) + lane_rc) * 2u : codes);
     };
     // the diagonal element held by this lane: D[4(l/16)+e][l%16] with e = l%16 - 4(l/16)
     const int de = (l & 15) - 4 * (l >> 4);
-    __syncthreads();  // q127 ready
+    __syncthreads();  // q127, us ready
+    // A fragment of the rank-r step: {hi, lo} of s*u[l] in the first dword
+    uint32_t ua0 = 0u;
+    if (lora && lane_r) {
+        uint16_t hi, lo;
+        split_bf16(__fmul_rn(scale, us[l]), hi, lo);
+        ua0 = uint32_t(hi) | (uint32_t(lo) << 16);
+    }
 
-    auto process = [&](const Fetch& f, int it) {
+    auto put = [&](int e, uint16_t v) { *reinterpret_cast<uint16_t*>(mine + e * 256 + 2) = v; };
+    auto process = [&](const Fetch& f, int par, int i) {
         const float sc = DQ ? __fmul_rn(q127[f.qb & 127u], f.cg) : bits_f(f.qb);
-        const float sblk = f.ok ? sc : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-            const uint32_t pk = pack_bf16x2(__fmul_rn(sblk, bits_f(level_bits(e))),
-                                            __fmul_rn(sblk, bits_f(level_bits(e + 1))));
-            tbl[w][e][2 * l] = uint16_t(pk);
-            tbl[w][e + 1][2 * l] = uint16_t(pk >> 16);
-        }
+        const float s = f.ok ? sc : 0.0f;
+        // entries 0 and 15 are -s and +s exactly; entry 7 (level 0) stays 0
+        const uint32_t pe = pack_bf16x2(-s, s);
+        put(0, uint16_t(pe));
+        put(15, uint16_t(pe >> 16));
+        auto pair = [&](int e0, int e1) {
+            const uint32_t pk = pack_bf16x2(__fmul_rn(s, bits_f(level_bits(e0))),
+                                            __fmul_rn(s, bits_f(level_bits(e1))));
+            put(e0, uint16_t(pk));
+            put(e1, uint16_t(pk >> 16));
+        };
+        pair(1, 2);
+        pair(3, 4);
+        pair(5, 6);
+        pair(8, 9);
+        pair(10, 11);
+        pair(12, 13);
+        put(14, to_bf16(__fmul_rn(s, bits_f(level_bits(14)))));
         const uint32_t cw[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (lora) {
+            // zeros made in place (a hoisted constant vector would be spilled)
+            uint32_t z, bv = f.bv;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+            asm volatile("" : "+v"(bv));  // keep the B load's use here, not in the fetch
+            bv = lane_r ? bv : 0u;
+            const u32x4_t ua = {ua0, z, z, z};
+            const u32x4_t bb = {bv | (bv << 16), z, z, z};
+            acc = mfma16(ua, bb, acc);
+        }
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             const uint32_t cd = cw[st];
-            const uint32_t clo = (cd & 0x0F0F0F0Fu) | P;
-            const uint32_t chi = ((cd >> 4) & 0x0F0F0F0Fu) | P;
-            u32x4_t bw;
+            const uint32_t clo = (cd & nmask) | P;         // odd elements (low nibbles)
+            const uint32_t chi = ((cd >> 4) & nmask) | P;  // even elements (high nibbles)
+            u32x4_t we, wo;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const uint32_t sel = 0x0C0C0000u | ((4u + t) << 8);
                 const uint32_t ah = __builtin_amdgcn_perm(chi, laneb, sel);
                 const uint32_t al = __builtin_amdgcn_perm(clo, laneb, sel);
-                const uint32_t vh = *reinterpret_cast<const uint16_t*>(tb + ah);
-                const uint32_t vl = *reinterpret_cast<const uint16_t*>(tb + al);
-                bw[t] = vh | (vl << 16);
+                we[t] = *reinterpret_cast<const uint16_t*>(tb + ah + 2);
+                wo[t] = *reinterpret_cast<const uint32_t*>(tb + al);
             }
-            acc = mfma16(xa[st], bw, acc);
+            acc = mfma16(xa[st], we, acc);
+            acc = mfma16(xa[st], wo, acc);
         }
         float d = 0.0f;
         d = (de == 0) ? acc[0] : d;
         d = (de == 1) ? acc[1] : d;
         d = (de == 2) ? acc[2] : d;
         d = (de == 3) ? acc[3] : d;
-        if (de >= 0 && de < 4) dlds[w][it][l & 15] = d;  // the 16 diagonal holders
+        if (de >= 0 && de < 4) dlds[par][w][i][l & 15] = d;  // the 16 diagonal holders
     };
 
-    // Ping-pong prefetch; the scheduling barriers keep each row's loads issued
-    // a whole row ahead of their use (the scheduler would otherwise sink them).
+    // chunk c: rows c*rows_chunk + sub*G1_NC + {0, 1}; row 0 of the next chunk
+    // is fetched while row 1 of this one is processed (unconditionally: past
+    // the end the fetch reads the clamped last row, which keeps the load
+    // counts of every path equal).  The scheduling barriers keep each row's
+    // loads issued a whole row ahead of their use.
+    const int G = int(gridDim.x);
+    int c = blockIdx.x;
     Fetch fa, fb;
-    fetch(0, fa);
-#pragma unroll
-    for (int it = 0; it < G1_ITEMS; it += 2) {
-        fetch(it + 1, fb);
+    fetch(int64_t(c) * rows_chunk + sub * G1_NC, fa);
+    for (int k = 0; c < nchunks; ++k, c += G) {
+        const int64_t rbase = int64_t(c) * rows_chunk + sub * G1_NC;
+        fetch(rbase + 1, fb);
         __builtin_amdgcn_sched_barrier(0);
-        process(fa, it);
-        if (it + 2 < G1_ITEMS) fetch(it + 2, fa);
+        process(fa, k & 1, 0);
+        fetch(rbase + int64_t(G) * rows_chunk, fa);
         __builtin_amdgcn_sched_barrier(0);
-        process(fb, it + 1);
-    }
-    // row sums of the diagonal values: lanes 0..G1_ITEMS-1 of each wave sum
-    // one row's 64 entries in order
-    if (l < G1_ITEMS) {
-        float v = 0.0f;
-        for (int k = 0; k < 16; ++k) v += dlds[w][l][k];
-        part[w][l] = v;
-    }
-    // u = sum of the down-projection partials, in a fixed order
-    for (int idx = tid; idx < r; idx += 256) {
-        float a = 0.0f;
-        for (int zz = 0; zz < DOWN_SPLIT; ++zz) a += upart[int64_t(zz) * r + idx];
-        us[idx] = a;
-        if (blockIdx.x == 0 && u_out) u_out[idx] = a;
-    }
-    __syncthreads();
-    // epilogue: row (sub, it) = regions summed + s * u . B[o]; 16 lanes per row
-    for (int ri = tid >> 4; ri < rows_wg; ri += 16) {
-        const int sb2 = ri / G1_ITEMS, it = ri % G1_ITEMS, ln = tid & 15;
-        const int64_t o = o0 + ri;
-        float ls = 0.0f;
-        if (o < N) {
-            const uint16_t* br = B + o * r;
-            for (int c = ln; c < r; c += 16) ls = fmaf(us[c], bf16_f(br[c]), ls);
-        }
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 16);
-        if (ln == 0 && o < N) {
+        process(fb, k & 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        // finish the chunk's rows: regions summed, in order
+        if (tid < rows_chunk) {
+            const int sb = tid / G1_NC, i = tid % G1_NC;
+            const int64_t o = int64_t(c) * rows_chunk + tid;
             float v = 0.0f;
-            for (int rr = 0; rr < R; ++rr) v += part[sb2 * R + rr][it];
-            if (r > 0) v += scale * ls;
-            h[o] = to_bf16(v);
+            for (int rr = 0; rr < R; ++rr) {
+                const float* dd = dlds[k & 1][sb * R + rr][i];
+                float t = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) t += dd[e];
+                v += t;
+            }
+            if (o < N) h[o] = to_bf16(v);
         }
     }
+}
+
+// Resident workgroups of a kernel on the current device (computed once).
+template <typename Kern>
+int resident_wgs(Kern kernel, int threads, int cache_slot) {
+    static std::atomic<int> cache[8];
+    int v = cache[cache_slot].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess ||
+        cus <= 0 || per <= 0) {
+        (void)hipGetLastError();
+        return 256 * 4;  // a safe guess: it only sizes the work per wave
+    }
+    v = cus * per;
+    cache[cache_slot].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 }  // namespace
@@ -409,29 +483,32 @@ __global__ __launch_bounds__(256) void k_gemv1(nf4::QView q, const uint16_t* __r
 namespace nf4 {
 
 size_t skinny_ws_bytes(int64_t M, int r) {
-    return align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4);
+    // down-projection partials, then the work counter of the M = 1 kernel
+    return align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4) + (M == 1 ? 256 : 0);
 }
 
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-                   int r, float scale, uint16_t* h, float* u_out, float* part, hipStream_t st) {
-    if (r > 0) {
-        hipLaunchKernelGGL(k_down_small, dim3(unsigned(cdiv(r, 16)), DOWN_SPLIT), dim3(256), 0, st, x,
-                           int(M), q.cols, A, r, part);
-        if (hipPeekAtLastError() != hipSuccess) return launch_status();
-    }
+                   int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st) {
+    float* part = reinterpret_cast<float*>(ws);
+    unsigned* ctr = reinterpret_cast<unsigned*>(
+        ws + align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4));
     const int64_t nkb = q.cols / 64;
     const int R = nkb <= 64 ? 1 : nkb <= 128 ? 2 : nkb <= 256 ? 4 : 0;
-    if (M == 1 && R > 0 && r <= 64) {
-        const int rows_wg = (4 / R) * G1_ITEMS;
-        const dim3 grid1(unsigned(cdiv(q.rows, rows_wg)));
-        if (q.dq) {
-            if (q.gshift >= 0)
-                launch_dominant(k_gemv1<true, true>, grid1, dim3(256), 0, st, q, x, part, r, B, scale, h, u_out, R);
-            else
-                launch_dominant(k_gemv1<true, false>, grid1, dim3(256), 0, st, q, x, part, r, B, scale, h, u_out, R);
-        } else {
-            launch_dominant(k_gemv1<false, true>, grid1, dim3(256), 0, st, q, x, part, r, B, scale, h, u_out, R);
-        }
+    // (32-bit byte offsets inside the M = 1 kernel: codes under 4 GB)
+    const bool gemv1 = M == 1 && R > 0 && r <= 64 && q.rows * q.cols / 2 < (int64_t(1) << 32);
+    // the down-projection kernel also zeroes the M = 1 work counter
+    hipLaunchKernelGGL(k_down_small, dim3(unsigned(std::max<int64_t>(1, cdiv(r, 16))), DOWN_SPLIT),
+                       dim3(256), 0, st, x, int(M), q.cols, A, r, part, gemv1 ? ctr : nullptr);
+    if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    if (gemv1) {
+        auto kern = q.dq ? (q.gshift >= 0 ? k_gemv1<true, true> : k_gemv1<true, false>)
+                         : k_gemv1<false, true>;
+        const int slot = q.dq ? (q.gshift >= 0 ? 0 : 1) : 2;
+        const int64_t rows_chunk = (4 / R) * G1_NC;
+        const int64_t nchunks = cdiv(q.rows, rows_chunk);
+        const int64_t grid = std::min<int64_t>(nchunks, resident_wgs(kern, 256, slot));
+        launch_dominant(kern, dim3(unsigned(grid)), dim3(256), 0, st, q, x, part, r, B, scale, h,
+                        u_out, R, int(nchunks), ctr);
         return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
     }
     const dim3 grid(unsigned(cdiv(q.rows, 16)));

@@ -83,3 +83,25 @@ def oracle_weight_rows(w: np.ndarray, rows, dq: bool, group: int = 256):
             q = O.quantize(w[o:o + 1], double_quant=False)
             res[o] = O.compute_weight(q, (cols,))
     return res
+
+
+def oracle_weight_cols(w: np.ndarray, cols_idx, dq: bool = True, group: int = 256,
+                       chunk_groups: int = 64) -> np.ndarray:
+    """Oracle Wb (float64) at every row of the selected columns of W [out, in]:
+    the whole tensor is quantized by the oracle in group-aligned chunks (the
+    same result as one call) and only the selected columns are kept."""
+    out, cols = w.shape
+    flat = w.reshape(-1)
+    cols_idx = np.asarray(cols_idx)
+    res = np.empty((out, cols_idx.size), dtype=np.float64)
+    step = 64 * group * chunk_groups
+    for lo in range(0, flat.size, step):
+        hi = min(lo + step, flat.size)
+        q = O.quantize(flat[lo:hi], double_quant=dq, dq_group=group)
+        wb = O.compute_weight(q, (hi - lo,))
+        r0, r1 = lo // cols, (hi + cols - 1) // cols
+        for o in range(r0, r1):
+            idx = o * cols + cols_idx
+            sel = (idx >= lo) & (idx < hi)
+            res[o, sel] = wb[idx[sel] - lo]
+    return res

@@ -238,3 +238,48 @@ def test_backward_large_tiles(F, M, out, inp, r):
     U.assert_close("dX", U.bf16_to_f64(dX), g["dX"])
     U.assert_close("dA", dA.cpu().numpy(), g["dA"])
     U.assert_close("dB", dB.cpu().numpy(), g["dB"])
+
+
+def test_70b_workload_full_size_sampled(F):
+    """The 70B MLP projection 8192 -> 28672 at full size, in the launch
+    configurations the benchmark times: decode (M = 1) forward and backward,
+    training (M = 4096) forward and backward.  h is compared on 24 sampled
+    weight rows, dX on 8 sampled input columns (the oracle quantizes the whole
+    tensor for those), dA and dB in full."""
+    import torch
+    from bit_nf4_quantized_04_amd import workloads as wl
+
+    c = 4
+    w, xt, a, b, s = _workload(c, 4096)
+    x1 = wl.activations(c, 1)
+    dh = wl.upstream_grad(c, 4096)
+    dh1 = dh[:1]
+    out, inp = w.shape
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    h1, u1 = F.qlora_linear_forward(q, U.bf(x1), U.bf(a), U.bf(b), s, want_u=True)
+    ht, ut = F.qlora_linear_forward(q, U.bf(xt), U.bf(a), U.bf(b), s, want_u=True)
+    g1 = F.qlora_linear_backward(q, U.bf(x1), U.bf(dh1), U.bf(a), U.bf(b), s, u=u1)
+    gt = F.qlora_linear_backward(q, U.bf(xt), U.bf(dh), U.bf(a), U.bf(b), s, u=ut)
+    torch.cuda.synchronize()
+    h1, ht = U.bf16_to_f64(h1), U.bf16_to_f64(ht)
+    g1 = [U.bf16_to_f64(g1[0]), g1[1].cpu().numpy(), g1[2].cpu().numpy()]
+    gt = [U.bf16_to_f64(gt[0]), gt[1].cpu().numpy(), gt[2].cpu().numpy()]
+    del q
+
+    rng = np.random.default_rng(40)
+    rows = np.unique(np.concatenate([[0, out - 1], rng.integers(0, out, 22)]))
+    kcols = np.unique(np.concatenate([[0, inp - 1], rng.integers(0, inp, 6)]))
+    wr = U.oracle_weight_rows(w, rows, True)
+    wrows = np.stack([wr[o] for o in rows])  # [n_rows, in]
+    xa, aa, ba, dha = O._bf(xt), O._bf(a), O._bf(b), O._bf(dh)
+    for xx, hh in ((O._bf(x1), h1), (xa, ht)):
+        u = xx @ aa.T
+        href = xx @ wrows.T + s * (u @ ba[rows].T)
+        U.assert_close("h rows M=%d" % xx.shape[0], hh[:, rows], href)
+    wc = U.oracle_weight_cols(w, kcols, True)  # [out, n_cols]
+    for xx, dd, gg in ((O._bf(x1), dha[:1], g1), (xa, dha, gt)):
+        u = xx @ aa.T
+        du = s * (dd @ ba)
+        U.assert_close("dX cols M=%d" % xx.shape[0], gg[0][:, kcols], dd @ wc + du @ aa[:, kcols])
+        U.assert_close("dA M=%d" % xx.shape[0], gg[1], du.T @ xx)
+        U.assert_close("dB M=%d" % xx.shape[0], gg[2], s * (dd.T @ u))

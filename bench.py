@@ -50,6 +50,30 @@ def gemv_kernel_bytes(out, inp, M, r, ngroups):
             + 4 * M * r + 2 * M * out)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch (read + write) of `kernel` from the committed
+    counter summary, or None when the library's sources have changed since the
+    counters were taken (the summary records a hash of them)."""
+    import hashlib
+
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "bit_nf4_quantized_04_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    k = rec.get("kernels", {}).get(kernel)
+    if rec.get("source_sha256_16") != h.hexdigest()[:16] or not k:
+        return None
+    return int(round(k["read_bytes"] + k["write_bytes"]))
+
+
 def train_flops(out, inp, M, r):
     fwd = 2 * M * out * inp + 2 * M * r * (inp + out)
     bwd = 2 * M * out * inp + 4 * M * out * r + 4 * M * r * inp
@@ -98,6 +122,24 @@ def cpu_baseline(c, w, x_bits, a_bits, b_bits, scale, budget_s=10.0):
     }
 
 
+def copy_calibration(torch, dev, K, W, nbytes=512 << 20):
+    """A plain copy of known size (nbytes read + nbytes written per launch):
+    what the HBM byte counters read for it scales the counters of the layer's
+    kernels."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(W):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / K
+    print("copy pass: %d bytes read + %d written per launch, %.4f ms/launch (%.1f GB/s)"
+          % (nbytes, nbytes, dt * 1e3, 2 * nbytes / dt / 1e9), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,12 +148,13 @@ def main():
     ap.add_argument("--workload", default="70b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "train"], default=None,
-                    help="profile one pass only (no JSON line)")
+    ap.add_argument("--only", choices=["decode", "train", "copy"], default=None,
+                    help="profile one pass only (no JSON line); 'copy' runs a plain 512 MiB "
+                         "device-to-device copy, the calibration for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the layer's multi-GPU sharding is a design "
-              "(see DESIGN.md), not built; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: sharding the layer over several GPUs is "
+              "not built; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -120,6 +163,9 @@ def main():
     from bit_nf4_quantized_04_amd import workloads as wl
 
     dev = torch.device("cuda:0")
+    if args.only == "copy":
+        copy_calibration(torch, dev, args.steps, args.warmup)
+        return
     c = WORKLOADS[args.workload]
     sh = wl.SHAPES[c]
     out, inp, r = sh["out"], sh["inp"], sh["r"]
@@ -248,7 +294,7 @@ def main():
         "train_frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_gemv1"),
             "kernel": "fused dequant product, M=1", "kernel_ms": round(k_ms, 5),
             "algorithmic_bytes_per_launch": kb,
         },
@@ -260,7 +306,8 @@ def main():
             "dx_kernel_ms": round(kd_ms, 4),
             "dx_achieved": round(dx_flops / (kd_ms * 1e-3) / 1e12, 2),
             "dx_frac": round(dx_flops / (kd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic_forward": measured_traffic("k_gemm_big (forward)"),
+            "traffic_dx": measured_traffic("k_gemm_big (dX)"),
         },
         "cpu_baseline": None,
     }

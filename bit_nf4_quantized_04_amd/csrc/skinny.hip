@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
 constexpr int G1_NC = 2;  // rows per wave per chunk (the ping-pong pair)
 
 template <bool DQ, bool GSH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv1(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_gemv1(
     nf4::QView q, const uint16_t* __restrict__ x, const float* __restrict__ upart, int r,
     const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
     float* __restrict__ u_out, int R, int nchunks, unsigned* __restrict__ ctr) {

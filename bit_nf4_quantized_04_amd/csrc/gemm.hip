@@ -397,7 +397,7 @@ inline int ext_cols(int r) { return int(nf4::cdiv(2 * r, 64) * 64); }
 
 struct FwdPlan {
     int Zu;  // split-K of the down-projection
-    size_t off_u, off_ext, off_part, total;
+    size_t off_u, off_ext, off_part, off_sc, total;
 };
 
 // Workspace of the GEMM-path down-projection: u, its bf16 hi/lo extension,
@@ -423,7 +423,12 @@ FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
         p.total = nf4::skinny_ws_bytes(M, r);
         return p;
     }
-    return plan_down(rows, cols, M, r);
+    FwdPlan p = plan_down(rows, cols, M, r);
+    if (nf4::use_big_gemm(M, rows)) {  // fp32 block scales of the register-dequant GEMM
+        p.off_sc = p.total;
+        p.total += nf4::rd_scales_bytes(rows, cols);
+    }
+    return p;
 }
 
 struct BwdPlan {
@@ -506,14 +511,22 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {
-        if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, nullptr, 0, nullptr, 0, h, st);
+        if (use_big_gemm(M, q.rows)) {
+            if (use_rd(q, M, 0, 0))
+                return forward_rd(q, x, M, nullptr, 0, nullptr, 0, h, reinterpret_cast<float*>(w + fp.off_sc), st);
+            return forward_big(q, x, M, nullptr, 0, nullptr, 0, h, st);
+        }
         return gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1, true);
     }
     float* u = u_out ? u_out : reinterpret_cast<float*>(w + fp.off_u);
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
     int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext);
     if (rc) return rc;
-    if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
+    if (use_big_gemm(M, q.rows)) {
+        if (use_rd(q, M, r, ext_cols(r)))
+            return forward_rd(q, x, M, ext, ext_cols(r), B, r, h, reinterpret_cast<float*>(w + fp.off_sc), st);
+        return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
+    }
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};
     return gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1, true);

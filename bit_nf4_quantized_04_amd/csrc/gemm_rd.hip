@@ -1,0 +1,444 @@
+// gemm_rd.hip -- large-M forward fused dequant-GEMM with the NF4 weight
+// dequantized straight into MFMA operand registers.
+//
+// Layer: h = x Wb^T + s (x A^T) B^T ("QLoRA Finetuner", "1. Low-Rank
+// Adaptation"; "QLoRA explained", "The LoRA adapter path"), with
+// Wb = bf16(s~ T[code]) ("QLoRA Finetuner", section 2, last item, and the
+// bf16 cast of "The LoRA adapter path").
+//
+// Tiles of 256 tokens x 256 weight rows, K in steps of 64 (one NF4 block per
+// weight row).  Four waves, one per SIMD; wave w owns the 256 x 64 slab of
+// weight rows [64w, 64w + 64) and keeps its 256 x 64 fp32 accumulator in
+// AGPRs.  v_mfma_f32_32x32x16_bf16: the tokens are the A rows (x tile staged
+// in LDS, shared by the four waves) and the weight rows the B columns.
+//
+// The B operand never touches LDS.  In the 32x32x16 layout lane (n, hh)
+// (n = lane % 32, hh = lane / 32) supplies 8 k values of column n; here the
+// k order inside a 64-block is permuted so that lane hh of slice s holds
+// elements 32hh + 8s .. 32hh + 8s + 7 of the block, i.e. one code dword of a
+// 16-byte half block (the x tile is read with the same permutation).  The
+// lane builds the block's 16 products bf16(fl32(s~ T[e])) once, as eight
+// byte planes (low bytes and high bytes of entries 0-3, 4-7, 8-11, 12-15),
+// and turns 8 nibbles into 8 bf16 values with byte permutes: two half-table
+// selects and a merge on bit 3 per byte plane, then one interleave of low and
+// high bytes per bf16 pair.  So each weight costs about three VALU operations
+// and no LDS traffic, leaving the LDS to the shared x tile.
+//
+// The rank-r branch continues the K loop over the [hi | lo] bf16 split of
+// s*u (2r columns, zero padded to a multiple of 64) against [B | B], so h is
+// written once and u keeps fp32 precision.
+//
+// Every global read of the K loop is an LDS DMA (global_load_lds), so that
+// all outstanding loads are of one kind and a wait count can name exactly the
+// ones a step needs: the x tile of step t+3 goes into a ring of four shared
+// tiles, and each lane's own code half-blocks and fp32 block scales of step
+// t+2 into a ring of two per-wave slots.  The block scales are made by a
+// small pass before the GEMM (fl32(fl32(q/127) * c_g) per block, the same
+// expression as every other dequantization here).
+#include <algorithm>
+
+#include "nf4_device.h"
+#include "nf4_internal.h"
+
+using namespace nf4dev;
+
+namespace {
+
+constexpr int RM = 256, RN = 256, RKS = 64;
+constexpr int RT = 256;  // 4 waves
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// x tile [256 rows][64 k] bf16 in LDS: row-major 128 B rows of eight 16-byte
+// chunks, chunk c of row m stored at position c ^ ((m >> 1) & 7).  Sixteen
+// consecutive rows then cover all 64 banks once for a given chunk, so both
+// the fragment reads and the tile writes are conflict-free.
+__device__ __forceinline__ int xpos(int m, int c) { return m * 8 + (c ^ ((m >> 1) & 7)); }
+
+// Byte planes of a block's 16 bf16 products: pl[0..3] low bytes of entries
+// 0-3, 4-7, 8-11, 12-15, pl[4..7] the high bytes.
+struct Planes { uint32_t v[8]; };
+
+__device__ __forceinline__ Planes make_planes(float s) {
+    float p[16];
+    p[0] = -s;
+    p[7] = 0.0f;
+    p[15] = s;
+#pragma unroll
+    for (int e = 1; e < 15; ++e)
+        if (e != 7) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+    uint32_t w[8];  // w[i] = bf16 pair (entry 2i, entry 2i+1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+    Planes t;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        t.v[g] = perm(w[2 * g + 1], w[2 * g], 0x06040200u);      // low bytes of entries 4g..4g+3
+        t.v[4 + g] = perm(w[2 * g + 1], w[2 * g], 0x07050301u);  // high bytes
+    }
+    return t;
+}
+
+// Constants of the nibble decode, held in VGPRs so that the selector
+// arithmetic fuses into single VOP3 operations.
+struct DecK {
+    uint32_t m7, m4, id, sa, sb;
+    __device__ __forceinline__ void init() {
+        m7 = 0x07070707u;
+        m4 = 0x04040404u;
+        id = 0x03020100u;
+        sa = 0x05010400u;
+        sb = 0x07030602u;
+        asm volatile("" : "+v"(m7), "+v"(m4), "+v"(id), "+v"(sa), "+v"(sb));
+    }
+};
+
+// Eight nibbles (one code dword: element 2i in the high nibble of byte i,
+// element 2i+1 in the low nibble) -> four bf16 pairs in element order.
+__device__ __forceinline__ void lookup8(const DecK& k, const Planes& t, uint32_t cd, u32x4_t& out) {
+    const uint32_t c4 = cd >> 4;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        // bytes: element 4h, 4h+1, 4h+2, 4h+3 codes in the low nibbles
+        const uint32_t raw = perm(cd, c4, half ? k.sb : k.sa);
+        const uint32_t s3 = raw & k.m7;
+        const uint32_t s2 = ((raw >> 1) & k.m4) | k.id;  // byte i, or 4+i if bit 3
+        const uint32_t lo = perm(perm(t.v[3], t.v[2], s3), perm(t.v[1], t.v[0], s3), s2);
+        const uint32_t hi = perm(perm(t.v[7], t.v[6], s3), perm(t.v[5], t.v[4], s3), s2);
+        out[2 * half] = perm(hi, lo, k.sa);      // elements 4h, 4h+1
+        out[2 * half + 1] = perm(hi, lo, k.sb);  // elements 4h+2, 4h+3
+    }
+}
+
+struct FwdArgs {
+    const uint8_t* codes;  // [N][K/2]
+    const float* scales;   // [N * K / 64] fp32 block scales
+    const uint16_t* x;     // [M][K]
+    const uint16_t* ext;   // [M][KL] (hi | lo of s*u, zero padded), or null
+    const uint16_t* B;     // [N][r]
+    uint16_t* h;           // [M][N]
+    int64_t M, N, K;
+    int KL, r;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int XBUF = RM * 8;  // one x tile: 256 rows x 8 chunks of 16 bytes
+// Per-wave weight slot: codes [row j][64 lanes][16 B], then scales [j][64][4 B].
+constexpr int WSLOT = 2 * 64 * 16 + 2 * 64 * 4;  // bytes per wave
+// DMA instructions per lane: 8 per x tile, 4 per weight slot.  At the wait
+// that closes step t the x tile of step t+3 (8) is the only DMA allowed to
+// be still in flight.
+constexpr int VM_XTILE = 8;
+
+struct Frag { u32x4_t v[8]; };
+
+struct FwdCtx {
+    const FwdArgs& a;
+    int S1, S;
+    int nl, hh, w, lane;
+    bool wok[2];
+    uint32_t xoff[8], eoff[8];  // byte offsets of this lane's x / extension DMA sources
+    uint32_t coff[2];           // byte offset of this lane's code half-block, step 0
+    uint32_t soff[2];           // byte offset of row j's block scale, step 0
+    DecK dk;
+
+    // x tile of step s into LDS tile `dst`: DMA instruction i of wave w fills
+    // chunk positions 64(8w + i) .. +63 (one 16-byte chunk per lane).
+    __device__ __forceinline__ void xdma(int s, uint4* dst) const {
+        const bool main = s < S1;
+        const char* base = main ? reinterpret_cast<const char*>(a.x) + int64_t(s) * (RKS * 2)
+                                : reinterpret_cast<const char*>(a.ext) + int64_t(s - S1) * (RKS * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + (main ? xoff[i] : eoff[i])),
+                                             (lds_void_t*)(dst + 64 * (8 * w + i)), 16, 0, 0);
+    }
+    // this lane's codes and block scales of step s into its wave's slot
+    __device__ __forceinline__ void wdma(int s, char* slot) const {
+        char* mine = slot + w * WSLOT;
+        const char* cb = reinterpret_cast<const char*>(a.codes) + int64_t(s) * 32;
+        const char* sb = reinterpret_cast<const char*>(a.scales) + int64_t(s) * 4;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(cb + coff[j]), (lds_void_t*)(mine + j * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(sb + soff[j]), (lds_void_t*)(mine + 2048 + j * 256), 4, 0, 0);
+    }
+    __device__ __forceinline__ void wread(const char* slot, uint4 (&cw)[2], float (&sc)[2]) const {
+        const char* mine = slot + w * WSLOT;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            cw[j] = *reinterpret_cast<const uint4*>(mine + j * 1024 + lane * 16);
+            const float v = *reinterpret_cast<const float*>(mine + 2048 + j * 256 + lane * 4);
+            sc[j] = wok[j] ? v : 0.0f;
+        }
+    }
+    // A fragments of slice sl: rows 32i + nl, logical chunk 4hh + sl
+    __device__ __forceinline__ void aread(const uint4* xb, int sl, Frag& f) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f.v[i] = __builtin_bit_cast(u32x4_t, xb[xpos(32 * i + nl, 4 * hh + sl)]);
+    }
+    // rank-r operand: element c of the extension (c < 2r) is B[n][c mod r]
+    __device__ __forceinline__ void bload(int s, int64_t row, bool ok, int sl, u32x4_t& out) const {
+        const int r = a.r;
+        const int c0 = (s - S1) * RKS + 32 * hh + 8 * sl;
+        uint16_t e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int c = c0 + t;
+            e[t] = (c < 2 * r && ok) ? a.B[row * r + (c % r)] : uint16_t(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) out[t] = uint32_t(e[2 * t]) | (uint32_t(e[2 * t + 1]) << 16);
+    }
+    __device__ __forceinline__ void lookups(const Planes (&p)[2], const uint4 (&cw)[2], int sl, u32x4_t (&bf)[2]) const {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            lookup8(dk, p[j], sl == 0 ? cw[j].x : sl == 1 ? cw[j].y : sl == 2 ? cw[j].z : cw[j].w, bf[j]);
+    }
+};
+
+__device__ __forceinline__ void mma(f32x16_t (&acc)[8][2], const Frag& af, const u32x4_t (&bf)[2]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af.v[i], bf[j], acc[i][j]);
+}
+
+// Interleave the 16 MFMAs of a slice with the slice's other work: after each
+// MFMA one LDS read, up to four VALU operations and one DMA.
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+}
+
+constexpr uint32_t vmcnt_imm(int n) {  // s_waitcnt vmcnt(n), other counters unconstrained
+    return uint32_t((n & 15) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// One NF4 step t.  x tiles: `cur` = step t, `nxt` = step t+1, `xd` receives
+// step t+3.  Weight slots: `wn` holds step t+1 (read at the end of the step),
+// `wd` (step t's, already in registers) receives step t+2.  On entry fa/ba
+// are slice 0's operands and cw/pl the codes and planes of step t; on exit
+// they are those of step t+1.
+__device__ __forceinline__ void nf4_step(const FwdCtx& c, int t, const uint4* cur, const uint4* nxt,
+                                         uint4* xd, const char* wn, char* wd, f32x16_t (&acc)[8][2],
+                                         Frag& fa, u32x4_t (&ba)[2], uint4 (&cw)[2], Planes (&pl)[2]) {
+    Frag fb;
+    u32x4_t bb[2];
+    // slice 0: prepare slice 1; DMA the x tile of step t+3
+    c.aread(cur, 1, fb);
+    c.lookups(pl, cw, 1, bb);
+    c.xdma(t + 3 < c.S ? t + 3 : c.S - 1, xd);
+    mma(acc, fa, ba);
+    interleave();
+    // slice 1: prepare slice 2
+    c.aread(cur, 2, fa);
+    c.lookups(pl, cw, 2, ba);
+    mma(acc, fb, bb);
+    interleave();
+    // slice 2: prepare slice 3
+    c.aread(cur, 3, fb);
+    c.lookups(pl, cw, 3, bb);
+    mma(acc, fa, ba);
+    interleave();
+    // slice 3: x tile t+1 (every wave's share) and this lane's weights of
+    // step t+1 are complete; then step t+2's weights go into the slot this
+    // step's occupied, and step t+1's first slice is prepared
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_XTILE));
+    __builtin_amdgcn_s_barrier();
+    c.wdma(t + 2 < c.S1 ? t + 2 : c.S1 - 1, wd);
+    float sc[2];
+    c.wread(wn, cw, sc);
+    pl[0] = make_planes(sc[0]);
+    pl[1] = make_planes(sc[1]);
+    c.aread(nxt, 0, fa);
+    c.lookups(pl, cw, 0, ba);
+    mma(acc, fb, bb);
+    interleave();
+}
+
+__global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
+    // the ring of x tiles and the two weight slots: separate arrays, so that
+    // the compiler can see that a DMA into one never overlaps reads of another
+    __shared__ __attribute__((aligned(16))) uint4 xs0[XBUF], xs1[XBUF], xs2[XBUF], xs3[XBUF];
+    __shared__ __attribute__((aligned(16))) char wb0[4 * WSLOT], wb1[4 * WSLOT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t N = a.N, K = a.K, M = a.M;
+
+    // XCD-aware tile order (workgroups are dealt round-robin to the 8 XCDs):
+    // each XCD walks a contiguous run of tiles, 4 token tiles at a time, so
+    // neighbouring tiles on one XCD share x rows or weight rows in its L2.
+    const int64_t nMt = (M + RM - 1) / RM, nNt = (N + RN - 1) / RN, T = nMt * nNt;
+    const int64_t bid = blockIdx.x;
+    const int64_t lin = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int64_t G = 4, gsz = G * nNt;
+    const int64_t grp = lin / gsz, first = grp * G;
+    const int64_t gm = (nMt - first < G) ? (nMt - first) : G;
+    const int64_t tm = first + (lin % gsz) % gm, tn = (lin % gsz) / gm;
+    const int64_t m0 = tm * RM, n0 = tn * RN;
+
+    FwdCtx c{a};
+    c.S1 = int(K / RKS);
+    c.S = c.S1 + (a.ext ? a.KL / RKS : 0);
+    c.nl = lane & 31;
+    c.hh = lane >> 5;
+    c.w = w;
+    c.lane = lane;
+    c.dk.init();
+    int64_t wrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t rr = n0 + 64 * w + 32 * j + c.nl;
+        c.wok[j] = rr < N;
+        wrow[j] = c.wok[j] ? rr : N - 1;
+        c.coff[j] = uint32_t(wrow[j] * (K / 2) + 16 * c.hh);
+        c.soff[j] = uint32_t(wrow[j] * (K / 64) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int p = 64 * (8 * w + i) + lane;  // chunk position this lane's DMA writes
+        const int m = p >> 3;
+        const int ch = (p & 7) ^ ((m >> 1) & 7);  // logical chunk stored there
+        int64_t row = m0 + m;
+        row = row < M ? row : M - 1;  // rows past M are computed and dropped
+        c.xoff[i] = uint32_t((row * K + 8 * ch) * 2);
+        c.eoff[i] = uint32_t((row * a.KL + 8 * ch) * 2);
+    }
+
+    f32x16_t acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int S1 = c.S1, S = c.S;
+    // ---- prologue, in the order the steady state assumes: x tiles 0..2,
+    // weights of steps 0 and 1 (step 1's after tile 2)
+    c.xdma(0, xs0);
+    c.wdma(0, wb0);
+    c.xdma(1 < S ? 1 : S - 1, xs1);
+    c.xdma(2 < S ? 2 : S - 1, xs2);
+    c.wdma(1 < S1 ? 1 : S1 - 1, wb1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * VM_XTILE + 4));
+    __syncthreads();  // x tile 0 and the step-0 weights ready
+    uint4 cw[2];
+    Planes pl[2];
+    {
+        float sc[2];
+        c.wread(wb0, cw, sc);
+        pl[0] = make_planes(sc[0]);
+        pl[1] = make_planes(sc[1]);
+    }
+    Frag fa;
+    u32x4_t ba[2];
+    c.aread(xs0, 0, fa);
+    c.lookups(pl, cw, 0, ba);
+
+    // four steps per iteration so every ring index is static (the launcher
+    // guarantees S1 % 4 == 0)
+    for (int t = 0; t < S1; t += 4) {
+        nf4_step(c, t, xs0, xs1, xs3, wb1, wb0, acc, fa, ba, cw, pl);
+        nf4_step(c, t + 1, xs1, xs2, xs0, wb0, wb1, acc, fa, ba, cw, pl);
+        nf4_step(c, t + 2, xs2, xs3, xs1, wb1, wb0, acc, fa, ba, cw, pl);
+        nf4_step(c, t + 3, xs3, xs0, xs2, wb0, wb1, acc, fa, ba, cw, pl);
+    }
+
+    // ---- rank-r steps (at most three, all already DMA'd): x tile from the
+    // ring, the B operand gathered from global memory
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int s = S1; s < S; ++s) {
+        const int k = s & 3;
+        const uint4* tl = k == 0 ? xs0 : k == 1 ? xs1 : k == 2 ? xs2 : xs3;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            Frag f;
+            u32x4_t bf[2];
+            c.aread(tl, sl, f);
+            c.bload(s, wrow[0], c.wok[0], sl, bf[0]);
+            c.bload(s, wrow[1], c.wok[1], sl, bf[1]);
+            mma(acc, f, bf);
+        }
+    }
+
+    // D layout of the 32x32 MFMA: lane holds column lane%32 and rows
+    // 8*(v/4) + 4*(lane/32) + v%4, v = 0..15.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + 64 * w + 32 * j + c.nl;
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * c.hh + (v & 3);
+                if (m < M) a.h[m * N + n] = to_bf16(acc[i][j][v]);
+            }
+    }
+}
+
+// fp32 block scales of a double-quantized weight: fl32(fl32(q_b/127) * c_g).
+template <bool GSH>
+__global__ __launch_bounds__(256) void k_block_scales(nf4::QView q, int64_t nb, float* __restrict__ out) {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x; b < nb; b += stride) {
+        const int64_t g = GSH ? (b >> q.gshift) : (b / q.group);
+        out[b] = __fmul_rn(q_over_127(q.qcodes[b]), q.gabs[g]);
+    }
+}
+
+}  // namespace
+
+namespace nf4 {
+
+size_t rd_scales_bytes(int64_t rows, int64_t cols) { return align256(size_t(rows * cols / 64) * 4); }
+
+bool use_rd(const QView& q, int64_t M, int r, int KL) {
+    // at most three rank-r steps, NF4 steps in fours, 32-bit offsets
+    return !((r > 0 && KL > 3 * RKS) || q.cols % (4 * RKS) != 0 ||
+             q.rows * q.cols / 2 >= (int64_t(1) << 32) || M * q.cols * 2 >= (int64_t(1) << 32) ||
+             (r > 0 && M * KL * 2 >= (int64_t(1) << 32)));
+}
+
+int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
+               const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st) {
+    const float* scales = q.absmax;
+    const int64_t nb = q.rows * q.cols / 64;
+    if (q.dq) {
+        const unsigned g = unsigned(std::min<int64_t>(cdiv(nb, 256), 4096));
+        if (q.gshift >= 0)
+            hipLaunchKernelGGL(k_block_scales<true>, dim3(g), dim3(256), 0, st, q, nb, scale_ws);
+        else
+            hipLaunchKernelGGL(k_block_scales<false>, dim3(g), dim3(256), 0, st, q, nb, scale_ws);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+        scales = scale_ws;
+    }
+    FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, r > 0 ? ext : nullptr, B, h,
+              M, q.rows, q.cols, KL, r};
+    const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
+    launch_dominant(k_fwd_rd, dim3(unsigned(T)), dim3(RT), 0, st, a);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+}  // namespace nf4

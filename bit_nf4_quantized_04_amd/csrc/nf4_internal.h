@@ -64,6 +64,13 @@ int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t*
 bool use_big_gemm(int64_t Mr, int64_t Nc);
 int forward_big(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
                 const uint16_t* B, int r, uint16_t* h, hipStream_t st);
+// Forward with the weight dequantized into MFMA operand registers (256 x 256
+// tiles); double quant needs rd_scales_bytes() of workspace for the fp32
+// block scales.
+size_t rd_scales_bytes(int64_t rows, int64_t cols);
+bool use_rd(const QView& q, int64_t M, int r, int KL);
+int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
+               const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
 int dx_big(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL,
            const uint16_t* A, int r, uint16_t* dX, hipStream_t st);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)

@@ -136,10 +136,12 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 constexpr int XBUF = RM * 8;  // one x tile: 256 rows x 8 chunks of 16 bytes
 // Per-wave weight slot: codes [row j][64 lanes][16 B], then scales [j][64][4 B].
 constexpr int WSLOT = 2 * 64 * 16 + 2 * 64 * 4;  // bytes per wave
-// DMA instructions per lane: 8 per x tile, 4 per weight slot.  At the wait
-// that closes step t the x tile of step t+3 (8) is the only DMA allowed to
-// be still in flight.
-constexpr int VM_XTILE = 8;
+// DMA instructions per lane: 8 per x tile, 4 per weight slot.  Issue order:
+// step t DMAs x tile t+3 in its first slice and weights t+3 in its second.
+// At the wait in step t's second slice (x tile t+1 and weights t+1 needed)
+// x tile t+2, weights t+2 and x tile t+3 may still be in flight.
+constexpr int VM_XTILE = 8, VM_WSLOT = 4;
+constexpr int VM_STEP_WAIT = 2 * VM_XTILE + VM_WSLOT;
 
 struct Frag { u32x4_t v[8]; };
 
@@ -234,43 +236,44 @@ constexpr uint32_t vmcnt_imm(int n) {  // s_waitcnt vmcnt(n), other counters unc
 }
 
 // One NF4 step t.  x tiles: `cur` = step t, `nxt` = step t+1, `xd` receives
-// step t+3.  Weight slots: `wn` holds step t+1 (read at the end of the step),
-// `wd` (step t's, already in registers) receives step t+2.  On entry fa/ba
-// are slice 0's operands and cw/pl the codes and planes of step t; on exit
-// they are those of step t+1.
+// step t+3.  Weight slot `wn` holds step t+1: it is read in the second slice
+// and then receives step t+3 (the other slot holds step t+2).  On entry
+// fa/ba are slice 0's operands and cw/pl the codes and planes of step t; the
+// step builds cwn/pln for step t+1 and leaves fa/ba as its slice 0 operands.
 __device__ __forceinline__ void nf4_step(const FwdCtx& c, int t, const uint4* cur, const uint4* nxt,
-                                         uint4* xd, const char* wn, char* wd, f32x16_t (&acc)[8][2],
-                                         Frag& fa, u32x4_t (&ba)[2], uint4 (&cw)[2], Planes (&pl)[2]) {
+                                         uint4* xd, char* wn, f32x16_t (&acc)[8][2], Frag& fa,
+                                         u32x4_t (&ba)[2], const uint4 (&cw)[2], const Planes (&pl)[2],
+                                         uint4 (&cwn)[2], Planes (&pln)[2]) {
     Frag fb;
     u32x4_t bb[2];
+    float sc[2];
     // slice 0: prepare slice 1; DMA the x tile of step t+3
     c.aread(cur, 1, fb);
     c.lookups(pl, cw, 1, bb);
     c.xdma(t + 3 < c.S ? t + 3 : c.S - 1, xd);
     mma(acc, fa, ba);
     interleave();
-    // slice 1: prepare slice 2
+    // slice 1: this lane's weights of step t+1 (and x tile t+1) complete; they
+    // go to registers, the slot receives step t+3's; prepare slice 2
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_STEP_WAIT));
+    c.wread(wn, cwn, sc);
+    c.wdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, wn);
     c.aread(cur, 2, fa);
     c.lookups(pl, cw, 2, ba);
+    pln[0] = make_planes(sc[0]);
     mma(acc, fb, bb);
     interleave();
     // slice 2: prepare slice 3
     c.aread(cur, 3, fb);
     c.lookups(pl, cw, 3, bb);
+    pln[1] = make_planes(sc[1]);
     mma(acc, fa, ba);
     interleave();
-    // slice 3: x tile t+1 (every wave's share) and this lane's weights of
-    // step t+1 are complete; then step t+2's weights go into the slot this
-    // step's occupied, and step t+1's first slice is prepared
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_XTILE));
+    // slice 3: every wave's share of x tile t+1 is in; prepare step t+1's
+    // first slice
     __builtin_amdgcn_s_barrier();
-    c.wdma(t + 2 < c.S1 ? t + 2 : c.S1 - 1, wd);
-    float sc[2];
-    c.wread(wn, cw, sc);
-    pl[0] = make_planes(sc[0]);
-    pl[1] = make_planes(sc[1]);
     c.aread(nxt, 0, fa);
-    c.lookups(pl, cw, 0, ba);
+    c.lookups(pln, cwn, 0, ba);
     mma(acc, fb, bb);
     interleave();
 }
@@ -333,20 +336,22 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int S1 = c.S1, S = c.S;
-    // ---- prologue, in the order the steady state assumes: x tiles 0..2,
-    // weights of steps 0 and 1 (step 1's after tile 2)
+    // ---- prologue, in the issue order of the steady state: x tile s, then
+    // weights s, for s = 0, 1, 2 (weights 2 go into slot 0 once weights 0
+    // are in registers)
     c.xdma(0, xs0);
     c.wdma(0, wb0);
     c.xdma(1 < S ? 1 : S - 1, xs1);
-    c.xdma(2 < S ? 2 : S - 1, xs2);
     c.wdma(1 < S1 ? 1 : S1 - 1, wb1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * VM_XTILE + 4));
+    c.xdma(2 < S ? 2 : S - 1, xs2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * VM_XTILE + VM_WSLOT));
     __syncthreads();  // x tile 0 and the step-0 weights ready
-    uint4 cw[2];
-    Planes pl[2];
+    uint4 cw[2], cw2[2];
+    Planes pl[2], pl2[2];
     {
         float sc[2];
         c.wread(wb0, cw, sc);
+        c.wdma(2 < S1 ? 2 : S1 - 1, wb0);
         pl[0] = make_planes(sc[0]);
         pl[1] = make_planes(sc[1]);
     }
@@ -358,10 +363,10 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     // four steps per iteration so every ring index is static (the launcher
     // guarantees S1 % 4 == 0)
     for (int t = 0; t < S1; t += 4) {
-        nf4_step(c, t, xs0, xs1, xs3, wb1, wb0, acc, fa, ba, cw, pl);
-        nf4_step(c, t + 1, xs1, xs2, xs0, wb0, wb1, acc, fa, ba, cw, pl);
-        nf4_step(c, t + 2, xs2, xs3, xs1, wb1, wb0, acc, fa, ba, cw, pl);
-        nf4_step(c, t + 3, xs3, xs0, xs2, wb0, wb1, acc, fa, ba, cw, pl);
+        nf4_step(c, t, xs0, xs1, xs3, wb1, acc, fa, ba, cw, pl, cw2, pl2);
+        nf4_step(c, t + 1, xs1, xs2, xs0, wb0, acc, fa, ba, cw2, pl2, cw, pl);
+        nf4_step(c, t + 2, xs2, xs3, xs1, wb1, acc, fa, ba, cw, pl, cw2, pl2);
+        nf4_step(c, t + 3, xs3, xs0, xs2, wb0, acc, fa, ba, cw2, pl2, cw, pl);
     }
 
     // ---- rank-r steps (at most three, all already DMA'd): x tile from the

@@ -407,7 +407,7 @@ FwdPlan plan_down(int64_t rows, int64_t cols, int64_t M, int r) {
     size_t o = 0;
     if (r > 0) {
         const int64_t tiles = nf4::cdiv(M, BM) * nf4::cdiv(r, BN);
-        p.Zu = choose_splits(tiles, nf4::cdiv(cols, BK));
+        p.Zu = r <= 64 ? nf4::nt_splits(M, cols) : choose_splits(tiles, nf4::cdiv(cols, BK));
         p.off_u = o; o = nf4::align256(o + size_t(M) * r * 4);
         p.off_ext = o; o = nf4::align256(o + size_t(M) * ext_cols(r) * 2);
         p.off_part = o; o = nf4::align256(o + size_t(p.Zu) * M * r * 4);
@@ -434,12 +434,14 @@ FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
 struct BwdPlan {
     FwdPlan f;       // recompute of u when it is not supplied
     int Zdu, Zdb, Zda;
-    size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_part, total;
+    bool skinny;     // r <= 64: the lora_bwd.hip products
+    size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, total;
 };
 
 BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     BwdPlan p{};
     p.f = plan_down(rows, cols, M, r);
+    p.skinny = r <= 64 && rows % 16 == 0;  // dU streams dH rows 16 elements at a time
     size_t o = p.f.total;
     p.off_uh = o; o = nf4::align256(o + size_t(M) * r * 2);
     p.off_ul = o; o = nf4::align256(o + size_t(M) * r * 2);
@@ -447,9 +449,18 @@ BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     p.off_duext = o; o = nf4::align256(o + size_t(M) * ext_cols(r) * 2);
     p.off_duh = o; o = nf4::align256(o + size_t(M) * r * 2);
     p.off_dul = o; o = nf4::align256(o + size_t(M) * r * 2);
-    p.Zdu = choose_splits(nf4::cdiv(M, BM) * nf4::cdiv(r, BN), nf4::cdiv(rows, BK));
-    p.Zdb = choose_splits(nf4::cdiv(rows, BM) * nf4::cdiv(r, BN), 2 * nf4::cdiv(M, BK));
-    p.Zda = choose_splits(nf4::cdiv(r, BM) * nf4::cdiv(cols, BN), 2 * nf4::cdiv(M, BK));
+    if (p.skinny) {
+        p.off_bt = o; o = nf4::align256(o + size_t(rows) * r * 2);
+        p.off_uq = o; o = nf4::align256(o + size_t(M) * 128 * 2);
+        p.off_duq = o; o = nf4::align256(o + size_t(M) * 128 * 2);
+        p.Zdu = nf4::nt_splits(M, rows);
+        p.Zdb = nf4::tn_splits(rows, M);
+        p.Zda = nf4::tn_splits(cols, M);
+    } else {
+        p.Zdu = choose_splits(nf4::cdiv(M, BM) * nf4::cdiv(r, BN), nf4::cdiv(rows, BK));
+        p.Zdb = choose_splits(nf4::cdiv(rows, BM) * nf4::cdiv(r, BN), 2 * nf4::cdiv(M, BK));
+        p.Zda = choose_splits(nf4::cdiv(r, BM) * nf4::cdiv(cols, BN), 2 * nf4::cdiv(M, BK));
+    }
     size_t part = size_t(p.Zdu) * M * r;
     if (size_t(p.Zdb) * rows * r > part) part = size_t(p.Zdb) * rows * r;
     if (size_t(p.Zda) * r * cols > part) part = size_t(p.Zda) * r * cols;
@@ -472,9 +483,14 @@ int down_projection(hipStream_t st, const nf4::QView& q, const uint16_t* x, int6
                     const uint16_t* A, int r, float scale, const FwdPlan& fp, char* ws, float* u,
                     uint16_t* ext) {
     float* part = reinterpret_cast<float*>(ws + fp.off_part);
-    LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
-    LdRowMajor la{A, r, q.cols, q.cols, al16(A)};
-    int rc = gemm(st, M, r, lx, la, q.cols, LdNone{}, LdNone{}, 0, OutPartial{part, M, r}, fp.Zu);
+    int rc;
+    if (r <= 64) {
+        rc = nf4::nt_product(st, x, M, q.cols, A, r, fp.Zu, part);
+    } else {
+        LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
+        LdRowMajor la{A, r, q.cols, q.cols, al16(A)};
+        rc = gemm(st, M, r, lx, la, q.cols, LdNone{}, LdNone{}, 0, OutPartial{part, M, r}, fp.Zu);
+    }
     if (rc) return rc;
     hipLaunchKernelGGL(k_reduce, dim3(ew_grid(M * r)), dim3(256), 0, st, part, fp.Zu, M * r, 1.0f, u);
     hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * ext_cols(r))), dim3(256), 0, st, u, M, r,
@@ -557,10 +573,30 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     uint16_t* duh = reinterpret_cast<uint16_t*>(w + bp.off_duh);
     uint16_t* dul = reinterpret_cast<uint16_t*>(w + bp.off_dul);
     float* part = reinterpret_cast<float*>(w + bp.off_part);
+    const bool dh_vec = al16(dH) && (out % 8 == 0);
+    if (bp.skinny) {
+        uint16_t* bt = reinterpret_cast<uint16_t*>(w + bp.off_bt);
+        uint16_t* uq = reinterpret_cast<uint16_t*>(w + bp.off_uq);
+        uint16_t* duq = reinterpret_cast<uint16_t*>(w + bp.off_duq);
+        // dU = s dH B (B^T made contiguous along out first)
+        if ((rc = transpose16(st, B, out, r, bt))) return rc;
+        if ((rc = nt_product(st, dH, M, out, bt, r, bp.Zdu, part))) return rc;
+        hipLaunchKernelGGL(k_reduce, dim3(ew_grid(M * r)), dim3(256), 0, st, part, bp.Zdu, M * r, scale, du);
+        hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * KL)), dim3(256), 0, st, du, M, r, KL, 1.0f, duext,
+                           (uint16_t*)nullptr, (uint16_t*)nullptr);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+        // dB = s dH^T u, dA = dU^T x: reductions over the tokens
+        if ((rc = split128(st, u, M, r, uq))) return rc;
+        if ((rc = split128(st, du, M, r, duq))) return rc;
+        if ((rc = tn_product(st, dH, M, out, uq, r, bp.Zdb, part))) return rc;
+        hipLaunchKernelGGL(k_reduce, dim3(ew_grid(out * r)), dim3(256), 0, st, part, bp.Zdb, out * r, scale, dB);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+        if ((rc = tn_product(st, x, M, in, duq, r, bp.Zda, part))) return rc;
+        if ((rc = reduce_t(st, part, bp.Zda, in, r, 1.0f, dA))) return rc;
+    } else {
     hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * r)), dim3(256), 0, st, u, M, r, r, 1.0f,
                        (uint16_t*)nullptr, uh, ul);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
-    const bool dh_vec = al16(dH) && (out % 8 == 0);
     // dU = s dH B : [M][r], K = out.  B as [K=out][N=r].
     rc = gemm(st, M, r, LdRowMajor{dH, M, out, out, dh_vec}, LdColMajor{B, r, out, r, al16(B) && r % 8 == 0},
               out, LdNone{}, LdNone{}, 0, OutPartial{part, M, r}, bp.Zdu);
@@ -584,6 +620,7 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     if (rc) return rc;
     hipLaunchKernelGGL(k_reduce, dim3(ew_grid(r * in)), dim3(256), 0, st, part, bp.Zda, r * in, 1.0f, dA);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    }
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
         if (use_big_gemm(M, in))

@@ -1,0 +1,313 @@
+// lora_bwd.hip -- the skinny products of the rank-r branch at large M:
+//
+//   u  = x A^T                (forward down-projection, [M][r], K = in)
+//   dU = s dH B               ([M][r], K = out)
+//   dB = s dH^T u             ([out][r], reduction over the M tokens)
+//   dA = dU^T x               ([r][in], reduction over the M tokens)
+//
+// ("QLoRA Finetuner", "1. Low-Rank Adaptation": h = W0 x + (alpha/r) B(A x);
+// the gradients are the plain derivative of that forward, and only A and B
+// receive them: "QLoRA explained", "The LoRA adapter path".)
+//
+// All four stream one large bf16 operand (x or dH) against a small one
+// (r <= 64 columns), so they are HBM-bound and split their reduction
+// across the grid (fp32 partials, summed in a fixed order afterwards).
+//
+//  * k_nt: both operands contiguous along the reduction (u with A, dU with
+//    B^T): MFMA operands are loaded straight from global memory.
+//  * k_tn: both operands contiguous across it (dB: dH and u; dA: x and dU):
+//    64-token tiles are staged row-major in LDS and read transposed with
+//    ds_read_b64_tr_b16 (in each 16-lane group, lane 4e + g addresses row
+//    k0 + e, column c0 + 4g; lane 4g + m then receives the four rows' values
+//    of column c0 + 4g + m, i.e. four consecutive k of its own column).
+//    The fp32 u / dU enter as a bf16 hi + lo pair ([M][128]: hi at column j,
+//    lo at 64 + j), so they keep fp32 precision.
+#include <algorithm>
+
+#include "nf4_device.h"
+#include "nf4_internal.h"
+
+using namespace nf4dev;
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ k_nt
+// part[z][m][j] = sum over k in chunk z of P[m][k] * Q[j][k]; P [M][K],
+// Q [J][K] bf16, J <= 32 * NF.  Wave w of block bx owns rows
+// 128 bx + 32 w .. +31; lane (row, hh) loads 8 consecutive k of its row.
+template <int NF>
+__global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int64_t M, int64_t K,
+                                            const uint16_t* __restrict__ Q, int J, int64_t kchunk,
+                                            float* __restrict__ part) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rl = lane & 31, hh = lane >> 5;
+    const int64_t m = int64_t(blockIdx.x) * 128 + 32 * w + rl;
+    const int64_t mc = m < M ? m : M - 1;
+    const int z = blockIdx.y;
+    const int64_t k0 = int64_t(z) * kchunk, k1 = std::min<int64_t>(K, k0 + kchunk);
+    const uint16_t* pr = P + mc * K + 8 * hh;
+    const uint16_t* qr[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int j = 32 * f + rl;
+        qr[f] = Q + int64_t(j < J ? j : J - 1) * K + 8 * hh;
+    }
+    f32x16_t acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[f][v] = 0.0f;
+    int64_t k = k0;
+    for (; k + 128 <= k1; k += 128) {  // eight slices of 16, all loads first
+        u32x4_t a[8], b[8][NF];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            a[s] = *reinterpret_cast<const u32x4_t*>(pr + k + 16 * s);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) b[s][f] = *reinterpret_cast<const u32x4_t*>(qr[f] + k + 16 * s);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) acc[f] = mfma32(a[s], b[s][f], acc[f]);
+    }
+    for (; k < k1; k += 16) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(pr + k);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[f] = mfma32(a, *reinterpret_cast<const u32x4_t*>(qr[f] + k), acc[f]);
+    }
+    // D layout: lane holds column rl and rows 8(v/4) + 4hh + v%4 of the frag
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int j = 32 * f + rl;
+        if (j >= J) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t mm = int64_t(blockIdx.x) * 128 + 32 * w + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (mm < M) part[(int64_t(z) * M + mm) * J + j] = acc[f][v];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ k_tn
+// part[z][R][j] = sum over tokens m in chunk z of P[m][R] * (Qh[m][j] + Ql[m][j])
+// with Q2 = [M][128] (hi at j, lo at 64 + j), j < J <= 64.  Block bx owns
+// columns R0 = 256 bx .. +255 of P; wave w the 64 of them at 64 w.
+constexpr int TN_PS = 256 + 32;  // LDS row stride of the P tile (elements): 576 bytes
+constexpr int TN_QS = 128 + 32;  // of the Q tile: 320 bytes
+
+// Four consecutive k (rows kb + 8(q>>1) + 4h .. +3) of column cb + (lane % 32),
+// for h = 0 and 1: the eight k of an MFMA operand fragment.
+__device__ __forceinline__ u32x4_t tr_frag(const uint16_t* tile, int stride, int kb, int cb, int lane) {
+    const int q = lane >> 4, i = lane & 15;
+    const int col = cb + 16 * (q & 1) + 4 * (i & 3);
+    const int row = kb + 8 * (q >> 1) + (i >> 2);
+    const uint16_t* p0 = tile + row * stride + col;
+    const uint16_t* p1 = p0 + 4 * stride;
+    const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0));
+    const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p1));
+    const uint2 d0 = __builtin_bit_cast(uint2, v0), d1 = __builtin_bit_cast(uint2, v1);
+    return u32x4_t{d0.x, d0.y, d1.x, d1.y};
+}
+
+__global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int64_t M, int64_t RR,
+                                            const uint16_t* __restrict__ Q2, int J, int64_t mchunk,
+                                            float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) uint16_t pt[64 * TN_PS];
+    __shared__ __attribute__((aligned(16))) uint16_t qt[64 * TN_QS];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t R0 = int64_t(blockIdx.x) * 256;
+    const int z = blockIdx.y;
+    const int64_t m0 = int64_t(z) * mchunk, m1 = std::min<int64_t>(M, m0 + mchunk);
+    const bool pvec = RR % 8 == 0;
+
+    // tile loads into registers: P chunk c = tid + 256 i (row c/32, 16-byte
+    // chunk c%32), Q chunk c = tid + 256 i (row c/16, chunk c%16); rows past
+    // the chunk are zero (they would otherwise count twice)
+    uint4 pv[8], qv[4];
+    auto load = [&](int64_t mb) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * i;
+            const int64_t mm = mb + (c >> 5), rr = R0 + 8 * (c & 31);
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (mm < m1) {
+                const uint16_t* src = P + mm * RR + rr;
+                if (pvec && rr + 8 <= RR) {
+                    v = *reinterpret_cast<const uint4*>(src);
+                } else {
+                    uint16_t e[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) e[t] = rr + t < RR ? src[t] : uint16_t(0);
+                    v = make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                                   e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+                }
+            }
+            pv[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            const int64_t mm = mb + (c >> 4);
+            qv[i] = mm < m1 ? *reinterpret_cast<const uint4*>(Q2 + mm * 128 + 8 * (c & 15)) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<uint4*>(&pt[(c >> 5) * TN_PS + 8 * (c & 31)]) = pv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<uint4*>(&qt[(c >> 4) * TN_QS + 8 * (c & 15)]) = qv[i];
+        }
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
+
+    if (m0 < m1) load(m0);
+    for (int64_t mb = m0; mb < m1; mb += 64) {
+        __syncthreads();  // the previous step's reads are done
+        store();
+        __syncthreads();
+        if (mb + 64 < m1) load(mb + 64);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            u32x4_t a[2], b[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = tr_frag(pt, TN_PS, 16 * sl, 64 * w + 32 * i, lane);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) b[f] = tr_frag(qt, TN_QS, 16 * sl, 32 * f, lane);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) acc[i][f] = mfma32(a[i], b[f], acc[i][f]);
+        }
+    }
+    // C[R][j] = hi part (frags 0, 1) + lo part (frags 2, 3)
+    const int rl = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int j = 32 * f + rl;
+        if (j >= J) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t R = R0 + 64 * w + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+                if (R < RR) part[(int64_t(z) * RR + R) * J + j] = acc[i][f][v] + acc[i][f + 2][v];
+            }
+    }
+}
+
+// q2 [M][128]: bf16 hi of v[m][j] at column j, lo at 64 + j (j < r <= 64), zero elsewhere.
+__global__ __launch_bounds__(256) void k_split128(const float* __restrict__ v, int64_t M, int r,
+                                                  uint16_t* __restrict__ q2) {
+    const int64_t n = M * 128;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+        const int64_t m = i >> 7;
+        const int c = int(i & 127), j = c & 63;
+        uint16_t val = 0;
+        if (j < r) {
+            uint16_t h, l;
+            split_bf16(v[m * r + j], h, l);
+            val = c < 64 ? h : l;
+        }
+        q2[i] = val;
+    }
+}
+
+// bt [r][n] = b [n][r] (bf16)
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ b, int64_t n, int r,
+                                                     uint16_t* __restrict__ bt) {
+    const int64_t tot = n * r;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < tot; i += int64_t(gridDim.x) * 256) {
+        const int64_t j = i / n, o = i % n;
+        bt[i] = b[o * r + j];
+    }
+}
+
+// out[j][i] = scale * sum_z part[z][i][j]  (i < n, j < r): the transposed reduce of dA
+__global__ __launch_bounds__(256) void k_reduce_t(const float* __restrict__ part, int Z, int64_t n, int r,
+                                                  float scale, float* __restrict__ out) {
+    const int64_t tot = n * r;
+    for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < tot; t += int64_t(gridDim.x) * 256) {
+        const int64_t j = t / n, i = t % n;
+        float a = 0.0f;
+        for (int z = 0; z < Z; ++z) a += part[(int64_t(z) * n + i) * r + j];
+        out[t] = a * scale;
+    }
+}
+
+unsigned ew(int64_t n) { return unsigned(std::max<int64_t>(1, std::min<int64_t>(8192, (n + 255) / 256))); }
+
+}  // namespace
+
+namespace nf4 {
+
+// Splits of the reduction so that the grid holds about 1024 workgroups.
+int nt_splits(int64_t M, int64_t K) {
+    const int64_t tiles = cdiv(M, 128);
+    int64_t z = cdiv(1024, tiles);
+    z = std::min<int64_t>(z, std::max<int64_t>(1, K / 128));
+    return int(std::max<int64_t>(1, std::min<int64_t>(z, 64)));
+}
+int tn_splits(int64_t RR, int64_t M) {
+    const int64_t tiles = cdiv(RR, 256);
+    int64_t z = cdiv(768, tiles);
+    z = std::min<int64_t>(z, std::max<int64_t>(1, M / 64));
+    return int(std::max<int64_t>(1, std::min<int64_t>(z, 64)));
+}
+
+int nt_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t K, const uint16_t* Q, int J, int Z,
+               float* part) {
+    const int64_t kchunk = cdiv(cdiv(K, Z), 16) * 16;
+    const dim3 grid(unsigned(cdiv(M, 128)), unsigned(Z));
+    if (J <= 32)
+        hipLaunchKernelGGL(k_nt<1>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, part);
+    else
+        hipLaunchKernelGGL(k_nt<2>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, part);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const uint16_t* Q2, int J, int Z,
+               float* part) {
+    const int64_t mchunk = cdiv(cdiv(M, Z), 64) * 64;
+    hipLaunchKernelGGL(k_tn, dim3(unsigned(cdiv(RR, 256)), unsigned(Z)), dim3(256), 0, st, P, M, RR, Q2, J,
+                       mchunk, part);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int split128(hipStream_t st, const float* v, int64_t M, int r, uint16_t* q2) {
+    hipLaunchKernelGGL(k_split128, dim3(ew(M * 128)), dim3(256), 0, st, v, M, r, q2);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt) {
+    hipLaunchKernelGGL(k_transpose16, dim3(ew(n * r)), dim3(256), 0, st, b, n, r, bt);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int reduce_t(hipStream_t st, const float* part, int Z, int64_t n, int r, float scale, float* out) {
+    hipLaunchKernelGGL(k_reduce_t, dim3(ew(n * r)), dim3(256), 0, st, part, Z, n, r, scale, out);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+}  // namespace nf4

@@ -73,6 +73,17 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
                const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
 int dx_big(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL,
            const uint16_t* A, int r, uint16_t* dX, hipStream_t st);
+// Skinny rank-r products (lora_bwd.hip), r <= 64: fp32 partials over Z
+// splits of the reduction.
+int nt_splits(int64_t M, int64_t K);
+int tn_splits(int64_t RR, int64_t M);
+int nt_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t K, const uint16_t* Q, int J, int Z,
+               float* part);
+int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const uint16_t* Q2, int J, int Z,
+               float* part);
+int split128(hipStream_t st, const float* v, int64_t M, int r, uint16_t* q2);
+int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt);
+int reduce_t(hipStream_t st, const float* part, int Z, int64_t n, int r, float scale, float* out);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);
 

@@ -46,6 +46,7 @@ SMALL = [  # (M, out, in, r): ragged M and out, several tiles, r from 1 to 64
     (130, 257, 192, 16),
     (3, 64, 64, 64),
     (260, 300, 448, 24),
+    (300, 160, 192, 40),  # out % 16 == 0: the streamed rank-r backward products
 ]
 
 

@@ -435,7 +435,8 @@ struct BwdPlan {
     FwdPlan f;       // recompute of u when it is not supplied
     int Zdu, Zdb, Zda;
     bool skinny;     // r <= 64: the lora_bwd.hip products
-    size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, total;
+    size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, off_sc,
+        total;
 };
 
 BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
@@ -465,6 +466,10 @@ BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     if (size_t(p.Zdb) * rows * r > part) part = size_t(p.Zdb) * rows * r;
     if (size_t(p.Zda) * r * cols > part) part = size_t(p.Zda) * r * cols;
     p.off_part = o; o = nf4::align256(o + part * 4);
+    if (nf4::use_big_gemm(M, cols)) {  // fp32 block scales of the register-dequant dX
+        p.off_sc = o;
+        o += nf4::rd_scales_bytes(rows, cols);
+    }
     p.total = o;
     return p;
 }
@@ -623,7 +628,9 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     }
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
-        if (use_big_gemm(M, in))
+        if (use_big_gemm(M, in) && use_dx_rd(q, M, r, KL))
+            rc = dx_rd(q, dH, M, duext, KL, A, r, dX, reinterpret_cast<float*>(w + bp.off_sc), st);
+        else if (use_big_gemm(M, in))
             rc = dx_big(q, dH, M, duext, KL, A, r, dX, st);
         else
             rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out,

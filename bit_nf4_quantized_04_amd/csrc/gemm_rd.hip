@@ -403,6 +403,281 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ dX
+// dX = dH Wb + [dU_hi | dU_lo] [A; A]  (the backward of the same layer; the
+// dequantized weight is a constant there, "QLoRA explained", "The LoRA
+// adapter path").  Tiles of 256 tokens x 256 input features, K = out in
+// steps of 32 weight rows.  Four waves, wave w owns the 256 x 64 slab of
+// columns [64w, 64w + 64) with its accumulator in AGPRs.
+//
+// Here the reduction runs across weight rows, so the weight is dequantized
+// in its natural layout: thread t makes 32 consecutive columns (half an NF4
+// block) of one weight row with the byte-plane lookup and writes them to a
+// row-major LDS tile; the MFMA B operand is read from that tile transposed
+// with ds_read_b64_tr_b16 (in each 16-lane group lane 4e + g addresses row
+// k0 + e, column c0 + 4g, and lane 4g + m receives column c0 + 4g + m of
+// those four rows: four consecutive k of one column).  The dH tile (A
+// operand) and each thread's own codes and block scale come by DMA into a
+// ring of four LDS buffers (one per step: the dH tile, then the staging), so
+// the K loop issues no other global load and its wait counts name exactly
+// the DMAs a step needs.  The transposed reads of a step are one asm block
+// that waits for its own results.
+constexpr int DK = 32;                   // weight rows per K step
+constexpr int DHBUF = RM * 4;            // dH tile: 256 rows x 4 chunks of 16 bytes
+constexpr int WTS = 256 + 32;            // W tile row stride (elements), 576 bytes
+constexpr int WTBUF = DK * WTS;          // W tile (elements)
+constexpr int DSLOT = 64 * 16 + 64 * 4;  // staging per wave: codes, then the scale
+constexpr int DXBUF = DHBUF + 4 * DSLOT / 16;  // one ring buffer (uint4): dH tile, staging
+constexpr int DX_VM_STEP = 6;            // DMAs per thread per step: 4 dH, 2 staging
+
+struct DxArgs {
+    const uint8_t* codes;  // [out][in/2]
+    const float* scales;   // [out * in / 64]
+    const uint16_t* dh;    // [M][out]
+    const uint16_t* ext;   // [M][KL] (dU hi | lo), or null
+    const uint16_t* A;     // [r][in]
+    uint16_t* dx;          // [M][in]
+    int64_t M, out, in;
+    int KL, r;
+};
+
+// dH tile layout: row m of 4 chunks, chunk c stored at c ^ ((m >> 2) & 3)
+// (sixteen consecutive rows then hit sixteen distinct bank groups)
+__device__ __forceinline__ int dpos(int m, int c) { return m * 4 + (c ^ ((m >> 2) & 3)); }
+
+struct DxCtx {
+    const DxArgs& a;
+    int S1, S;
+    int w, lane, tid;
+    uint32_t hoff[4], eoff[4];  // byte offsets of this lane's dH / extension DMA sources
+    uint32_t coff;              // byte offset of this thread's code half-block, step 0
+    uint32_t soff;              // byte offset of its block scale, step 0
+    uint32_t tro;               // byte offset of this lane's first transposed read in a W tile
+    DecK dk;
+
+    __device__ __forceinline__ void hdma(int s, uint4* dst) const {
+        const bool main = s < S1;
+        const char* base = main ? reinterpret_cast<const char*>(a.dh) + int64_t(s) * (DK * 2)
+                                : reinterpret_cast<const char*>(a.ext) + int64_t(s - S1) * (DK * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + (main ? hoff[i] : eoff[i])),
+                                             (lds_void_t*)(dst + 64 * (4 * w + i)), 16, 0, 0);
+    }
+    __device__ __forceinline__ void sdma(int s, uint4* buf) const {
+        char* mine = reinterpret_cast<char*>(buf + DHBUF) + w * DSLOT;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const char*>(a.codes) + coff +
+                                                       int64_t(s) * DK * (a.in / 2)),
+                                         (lds_void_t*)(mine), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const char*>(a.scales) + soff +
+                                                       int64_t(s) * DK * (a.in / 64) * 4),
+                                         (lds_void_t*)(mine + 1024), 4, 0, 0);
+    }
+    // this thread's 32 weights (staged in `slot`) into W tile `wt`
+    __device__ __forceinline__ void dequant(const uint4* buf, uint16_t* wt) const {
+        const char* mine = reinterpret_cast<const char*>(buf + DHBUF) + w * DSLOT;
+        const uint4 cw = *reinterpret_cast<const uint4*>(mine + lane * 16);
+        const float sc = *reinterpret_cast<const float*>(mine + 1024 + lane * 4);
+        const Planes p = make_planes(sc);
+        u32x4_t o[4];
+        lookup8(dk, p, cw.x, o[0]);
+        lookup8(dk, p, cw.y, o[1]);
+        lookup8(dk, p, cw.z, o[2]);
+        lookup8(dk, p, cw.w, o[3]);
+        const int unit = tid >> 1, half = tid & 1;
+        uint16_t* dst = wt + (unit >> 2) * WTS + 64 * (unit & 3) + 32 * half;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4_t*>(dst + 8 * d) = o[d];
+    }
+    // rank-r rows of the B operand: row c of the extension (c < 2r) is A[c mod r]
+    __device__ __forceinline__ void afill(int s, int64_t i0, uint16_t* wt) const {
+        const int r = a.r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = tid + 256 * k;  // 1024 chunks: 32 rows x 32 chunks of 8
+            const int row = e >> 5, ch = e & 31;
+            const int c = (s - S1) * DK + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (c < 2 * r) v = *reinterpret_cast<const uint4*>(a.A + int64_t(c % r) * a.in + i0 + 8 * ch);
+            *reinterpret_cast<uint4*>(wt + row * WTS + 8 * ch) = v;
+        }
+    }
+    __device__ __forceinline__ void aread(const uint4* ht, int sl, Frag& f) const {
+        const int nl = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f.v[i] = __builtin_bit_cast(u32x4_t, ht[dpos(32 * i + nl, 2 * sl + hh)]);
+    }
+    // the step's B operand (2 slices x 2 column frags) from W tile `wt`: eight
+    // transposed 8-byte reads off one address, and a wait for all of them
+    __device__ __forceinline__ void bread(const uint16_t* wt, u32x4_t (&b0)[2], u32x4_t (&b1)[2]) const {
+        const uint32_t ad = uint32_t(reinterpret_cast<uintptr_t>(wt)) + tro;
+        uint2 v[8];
+        // offsets: +4 rows = 2304 B, +32 columns = 64 B, +16 rows (slice 1) = 9216 B
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %8 offset:2304\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+            "ds_read_b64_tr_b16 %3, %8 offset:2368\n\t"
+            "ds_read_b64_tr_b16 %4, %8 offset:9216\n\t"
+            "ds_read_b64_tr_b16 %5, %8 offset:11520\n\t"
+            "ds_read_b64_tr_b16 %6, %8 offset:9280\n\t"
+            "ds_read_b64_tr_b16 %7, %8 offset:11584\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+              "=&v"(v[7])
+            : "v"(ad)
+            : "memory");
+        b0[0] = u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
+        b0[1] = u32x4_t{v[2].x, v[2].y, v[3].x, v[3].y};
+        b1[0] = u32x4_t{v[4].x, v[4].y, v[5].x, v[5].y};
+        b1[1] = u32x4_t{v[6].x, v[6].y, v[7].x, v[7].y};
+    }
+};
+
+// One K step t: MFMAs on ring buffer `bc` (dH tile of step t) and W tile
+// `wc`; meanwhile DMAs of step t+3 into buffer `bd`, and the dequantization
+// of step t+1 (staged in buffer `bn`) into W tile `wn`.
+__device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, const uint4* bn, uint4* bd,
+                                        const uint16_t* wc, uint16_t* wn, f32x16_t (&acc)[8][2]) {
+    Frag fa, fb;
+    u32x4_t ba[2], bb[2];
+    c.bread(wc, ba, bb);
+    c.aread(bc, 0, fa);
+    c.hdma(t + 3 < c.S ? t + 3 : c.S - 1, bd);
+    c.sdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, bd);
+    c.aread(bc, 1, fb);
+    mma(acc, fa, ba);
+    // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
+    // (the scheduling barrier keeps the staging reads below the wait)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
+    __builtin_amdgcn_sched_barrier(0);
+    c.dequant(bn, wn);
+    interleave();
+    mma(acc, fb, bb);
+    interleave();
+    // W tile t+1 (LDS writes) complete before the barrier; no fence: nothing
+    // else must be waited for
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP) & ~0xf00u);
+    __builtin_amdgcn_s_barrier();
+}
+
+// The K loop over the ring of four buffers, four steps per iteration so the
+// ring indices are static (the launcher guarantees a multiple of four
+// steps).  The buffers are separate arrays so that the compiler can see that
+// a DMA into one never overlaps reads of another.
+__device__ __forceinline__ void dx_loop(const DxCtx& c, uint4* __restrict__ B0, uint4* __restrict__ B1,
+                                        uint4* __restrict__ B2, uint4* __restrict__ B3,
+                                        uint16_t* __restrict__ W0, uint16_t* __restrict__ W1,
+                                        f32x16_t (&acc)[8][2]) {
+    for (int t = 0; t < c.S1; t += 4) {
+        dx_step(c, t, B0, B1, B3, W0, W1, acc);
+        dx_step(c, t + 1, B1, B2, B0, W1, W0, acc);
+        dx_step(c, t + 2, B2, B3, B1, W0, W1, acc);
+        dx_step(c, t + 3, B3, B0, B2, W1, W0, acc);
+    }
+}
+
+__global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
+    __shared__ __attribute__((aligned(16))) uint4 h0[DXBUF], h1[DXBUF], h2[DXBUF], h3[DXBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t wt0[WTBUF], wt1[WTBUF];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t M = a.M, N = a.in;
+
+    // XCD-aware tile order, as in the forward
+    const int64_t nMt = (M + RM - 1) / RM, nNt = (N + RN - 1) / RN, T = nMt * nNt;
+    const int64_t bid = blockIdx.x;
+    const int64_t lin = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int64_t G = 4, gsz = G * nNt;
+    const int64_t grp = lin / gsz, first = grp * G;
+    const int64_t gm = (nMt - first < G) ? (nMt - first) : G;
+    const int64_t tm = first + (lin % gsz) % gm, tn = (lin % gsz) / gm;
+    const int64_t m0 = tm * RM, i0 = tn * RN;
+
+    DxCtx c{a};
+    c.S1 = int(a.out / DK);
+    c.S = c.S1 + (a.ext ? a.KL / DK : 0);
+    c.w = w;
+    c.lane = lane;
+    c.tid = tid;
+    c.dk.init();
+    {
+        const int unit = tid >> 1, half = tid & 1;
+        const int64_t row = unit >> 2, q = unit & 3;
+        c.coff = uint32_t(row * (N / 2) + (i0 + 64 * q) / 2 + 16 * half);
+        c.soff = uint32_t((row * (N / 64) + i0 / 64 + q) * 4);
+        const int qq = lane >> 4, i = lane & 15;
+        const int col = 64 * w + 16 * (qq & 1) + 4 * (i & 3);
+        const int rw = 8 * (qq >> 1) + (i >> 2);
+        c.tro = uint32_t((rw * WTS + col) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = 64 * (4 * w + i) + lane;  // chunk position this lane's DMA writes
+        const int m = p >> 2;
+        const int ch = (p & 3) ^ ((m >> 2) & 3);  // logical chunk stored there
+        int64_t row = m0 + m;
+        row = row < M ? row : M - 1;  // rows past M are computed and dropped
+        c.hoff[i] = uint32_t((row * a.out + 8 * ch) * 2);
+        c.eoff[i] = uint32_t((row * a.KL + 8 * ch) * 2);
+    }
+
+    f32x16_t acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int S1 = c.S1, S = c.S;
+    // ---- prologue: steps 0, 1, 2 (dH tile, then staging) in flight
+    c.hdma(0, h0);
+    c.sdma(0, h0);
+    c.hdma(1 < S ? 1 : S - 1, h1);
+    c.sdma(1 < S1 ? 1 : S1 - 1, h1);
+    c.hdma(2 < S ? 2 : S - 1, h2);
+    c.sdma(2 < S1 ? 2 : S1 - 1, h2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));  // step 0
+    c.dequant(h0, wt0);
+    __syncthreads();
+
+    dx_loop(c, h0, h1, h2, h3, wt0, wt1, acc);
+
+    // ---- rank-r steps: dH-side tiles from the ring (the first three were
+    // DMA'd by the loop), the B rows copied from A
+    for (int s = S1; s < S; ++s) {
+        const int k = s & 3;
+        uint4* ht = k == 0 ? h0 : k == 1 ? h1 : k == 2 ? h2 : h3;
+        if (s + 3 < S) c.hdma(s + 3, k == 0 ? h3 : k == 1 ? h0 : k == 2 ? h1 : h2);
+        c.afill(s, i0, wt0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        Frag f0, f1;
+        u32x4_t b0[2], b1[2];
+        c.bread(wt0, b0, b1);
+        c.aread(ht, 0, f0);
+        c.aread(ht, 1, f1);
+        mma(acc, f0, b0);
+        mma(acc, f1, b1);
+        __syncthreads();
+    }
+
+    // D layout: lane holds column lane%32 and rows 8(v/4) + 4(lane/32) + v%4
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t n = i0 + 64 * w + 32 * j + (lane & 31);
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M) a.dx[m * N + n] = to_bf16(acc[i][j][v]);
+            }
+    }
+}
+
 // fp32 block scales of a double-quantized weight: fl32(fl32(q_b/127) * c_g).
 template <bool GSH>
 __global__ __launch_bounds__(256) void k_block_scales(nf4::QView q, int64_t nb, float* __restrict__ out) {
@@ -424,6 +699,40 @@ bool use_rd(const QView& q, int64_t M, int r, int KL) {
     return !((r > 0 && KL > 3 * RKS) || q.cols % (4 * RKS) != 0 ||
              q.rows * q.cols / 2 >= (int64_t(1) << 32) || M * q.cols * 2 >= (int64_t(1) << 32) ||
              (r > 0 && M * KL * 2 >= (int64_t(1) << 32)));
+}
+
+// fp32 block scales: the absmax array, or the double-quant decode into scale_ws
+int block_scales(const QView& q, float* scale_ws, const float** scales, hipStream_t st) {
+    *scales = q.absmax;
+    if (!q.dq) return NF4_OK;
+    const int64_t nb = q.rows * q.cols / 64;
+    const unsigned g = unsigned(std::min<int64_t>(cdiv(nb, 256), 4096));
+    if (q.gshift >= 0)
+        hipLaunchKernelGGL(k_block_scales<true>, dim3(g), dim3(256), 0, st, q, nb, scale_ws);
+    else
+        hipLaunchKernelGGL(k_block_scales<false>, dim3(g), dim3(256), 0, st, q, nb, scale_ws);
+    if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    *scales = scale_ws;
+    return NF4_OK;
+}
+
+bool use_dx_rd(const QView& q, int64_t M, int r, int KL) {
+    // whole steps of 32 weight rows in fours, whole 256-column tiles, 32-bit offsets
+    return q.rows % (4 * DK) == 0 && q.cols % RN == 0 && (r == 0 || KL % DK == 0) &&
+           q.rows * q.cols / 2 < (int64_t(1) << 32) && M * q.rows * 2 < (int64_t(1) << 32) &&
+           (r == 0 || M * KL * 2 < (int64_t(1) << 32));
+}
+
+int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
+          int r, uint16_t* dX, float* scale_ws, hipStream_t st) {
+    const float* scales;
+    int rc = block_scales(q, scale_ws, &scales, st);
+    if (rc) return rc;
+    DxArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, dH, r > 0 ? duext : nullptr, A, dX,
+             M, q.rows, q.cols, KL, r};
+    const int64_t T = cdiv(M, RM) * cdiv(q.cols, RN);
+    launch_dominant(k_dx_rd, dim3(unsigned(T)), dim3(RT), 0, st, a);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,

@@ -71,6 +71,11 @@ size_t rd_scales_bytes(int64_t rows, int64_t cols);
 bool use_rd(const QView& q, int64_t M, int r, int KL);
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
                const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
+// dX with the weight dequantized into a row-major LDS tile read transposed
+// (256 x 256 tiles); double quant needs rd_scales_bytes() of workspace.
+bool use_dx_rd(const QView& q, int64_t M, int r, int KL);
+int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
+          int r, uint16_t* dX, float* scale_ws, hipStream_t st);
 int dx_big(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL,
            const uint16_t* A, int r, uint16_t* dX, hipStream_t st);
 // Skinny rank-r products (lora_bwd.hip), r <= 64: fp32 partials over Z

@@ -306,8 +306,8 @@ def main():
             "dx_kernel_ms": round(kd_ms, 4),
             "dx_achieved": round(dx_flops / (kd_ms * 1e-3) / 1e12, 2),
             "dx_frac": round(dx_flops / (kd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic_forward": measured_traffic("k_gemm_big (forward)"),
-            "traffic_dx": measured_traffic("k_gemm_big (dX)"),
+            "traffic_forward": measured_traffic("k_fwd_rd"),
+            "traffic_dx": measured_traffic("k_dx_rd"),
         },
         "cpu_baseline": None,
     }

@@ -35,10 +35,8 @@ constexpr int DOWN_SPLIT = 16;
 
 __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__ x, int M,
                                                     int64_t K, const uint16_t* __restrict__ A,
-                                                    int r, float* __restrict__ part,
-                                                    unsigned* __restrict__ ctr) {
+                                                    int r, float* __restrict__ part) {
     __shared__ float red[4][16][17];
-    if (ctr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ctr = 0u;
     if (r <= 0) return;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int i = l & 15, g = l >> 4;
@@ -268,17 +266,16 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
 //
 // Work is handed out in chunks of G1_NC rows per wave (a workgroup's four
 // waves are R regions x 4/R row subsets of one chunk).  The grid is the number
-// of resident workgroups; the first chunk of each is its block index, later
-// ones come from an atomic counter, so workgroups on faster memory paths take
-// more chunks and all finish together.  The counter is zeroed by the
-// down-projection kernel launched just before on the same stream.
+// of resident workgroups (at most), and workgroup b takes chunks b, b + G,
+// b + 2G, ... of the G-strided sequence: neighbouring workgroups stream
+// neighbouring rows, and no counter or atomic is involved.
 constexpr int G1_NC = 2;  // rows per wave per chunk (the ping-pong pair)
 
 template <bool DQ, bool GSH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_gemv1(
     nf4::QView q, const uint16_t* __restrict__ x, const float* __restrict__ upart, int r,
     const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
-    float* __restrict__ u_out, int R, int nchunks, unsigned* __restrict__ ctr) {
+    float* __restrict__ u_out, int R, int nchunks) {
     __shared__ __attribute__((aligned(16))) uint32_t tbl[4][16][64];  // [wave][entry][lane]
     __shared__ float q127[128];
     __shared__ float dlds[2][4][G1_NC][16];  // diagonal D[i][i] per (parity, wave, row, i)
@@ -483,22 +480,19 @@ int resident_wgs(Kern kernel, int threads, int cache_slot) {
 namespace nf4 {
 
 size_t skinny_ws_bytes(int64_t M, int r) {
-    // down-projection partials, then the work counter of the M = 1 kernel
-    return align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4) + (M == 1 ? 256 : 0);
+    // down-projection partials
+    return align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4);
 }
 
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                    int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st) {
     float* part = reinterpret_cast<float*>(ws);
-    unsigned* ctr = reinterpret_cast<unsigned*>(
-        ws + align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4));
     const int64_t nkb = q.cols / 64;
     const int R = nkb <= 64 ? 1 : nkb <= 128 ? 2 : nkb <= 256 ? 4 : 0;
     // (32-bit byte offsets inside the M = 1 kernel: codes under 4 GB)
     const bool gemv1 = M == 1 && R > 0 && r <= 64 && q.rows * q.cols / 2 < (int64_t(1) << 32);
-    // the down-projection kernel also zeroes the M = 1 work counter
     hipLaunchKernelGGL(k_down_small, dim3(unsigned(std::max<int64_t>(1, cdiv(r, 16))), DOWN_SPLIT),
-                       dim3(256), 0, st, x, int(M), q.cols, A, r, part, gemv1 ? ctr : nullptr);
+                       dim3(256), 0, st, x, int(M), q.cols, A, r, part);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (gemv1) {
         auto kern = q.dq ? (q.gshift >= 0 ? k_gemv1<true, true> : k_gemv1<true, false>)
@@ -508,7 +502,7 @@ int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t*
         const int64_t nchunks = cdiv(q.rows, rows_chunk);
         const int64_t grid = std::min<int64_t>(nchunks, resident_wgs(kern, 256, slot));
         launch_dominant(kern, dim3(unsigned(grid)), dim3(256), 0, st, q, x, part, r, B, scale, h,
-                        u_out, R, int(nchunks), ctr);
+                        u_out, R, int(nchunks));
         return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
     }
     const dim3 grid(unsigned(cdiv(q.rows, 16)));

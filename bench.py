@@ -50,6 +50,12 @@ def gemv_kernel_bytes(out, inp, M, r, ngroups):
             + 4 * M * r + 2 * M * out)
 
 
+def dx_gemv_kernel_bytes(out, inp, M, r, ngroups):
+    """Algorithmic bytes of the few-token dX kernel (one pass over the weight
+    rows for dX and dU): codes, scale codes, group constants, dH and B."""
+    return out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * M * out + 2 * r * out
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch (read + write) of `kernel` from the committed
     counter summary, or None when the library's sources have changed since the
@@ -148,7 +154,7 @@ def main():
     ap.add_argument("--workload", default="70b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "train", "copy"], default=None,
+    ap.add_argument("--only", choices=["decode", "decode_bwd", "train", "copy"], default=None,
                     help="profile one pass only (no JSON line); 'copy' runs a plain 512 MiB "
                          "device-to-device copy, the calibration for HBM byte counters")
     args = ap.parse_args()
@@ -203,6 +209,14 @@ def main():
     def decode_step(i):
         F.qlora_linear_forward(qs[i % len(qs)], x1, A, B, scale, ws=ws_f1, out=h1)
 
+    _, u1 = F.qlora_linear_forward(qs[0], x1, A, B, scale, want_u=True, ws=ws_f1, out=h1)
+    dH1 = bf(wl.upstream_grad(c, 1))
+    ws_b1 = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD, out, inp, 1, r), 256),
+                        dtype=torch.uint8, device=dev)
+
+    def decode_bwd_step(i):
+        F.qlora_linear_backward(qs[i % len(qs)], x1, dH1, A, B, scale, u=u1, ws=ws_b1)
+
     def train_step(i):
         _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
         F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
@@ -234,12 +248,14 @@ def main():
     # whole-step timing (no hook), then the dominant kernel with the hook
     K, W = args.steps, args.warmup
     if args.only:
-        step = decode_step if args.only == "decode" else train_step
+        step = {"decode": decode_step, "decode_bwd": decode_bwd_step, "train": train_step}[args.only]
         t, _ = timed(step, K, W)
         print("%s pass: %.4f ms/step over %d steps" % (args.only, t, K), flush=True)
         return
     t_dec, _ = timed(decode_step, K, W)
     _, k_dec = timed(decode_step, K, 1, hook_events=True)
+    t_dbw, _ = timed(decode_bwd_step, K, W)
+    _, k_dbw = timed(decode_bwd_step, K, 1, hook_events=True)
     t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))
     # dominant kernels of the training pass: forward product and dX product
     fwd_k, bwd_k = [], []
@@ -260,6 +276,8 @@ def main():
     kb = gemv_kernel_bytes(out, inp, 1, r, ngroups)
     k_ms = float(np.mean(k_dec))
     achieved = kb / (k_ms * 1e-3) / 1e9
+    kbw = dx_gemv_kernel_bytes(out, inp, 1, r, ngroups)
+    kbw_ms = float(np.mean(k_dbw))
     ffwd, fbwd = train_flops(out, inp, Mtrain, r)
     tflops = (ffwd + fbwd) / (t_tr * 1e-3) / 1e12
     gemm_flops = 2 * Mtrain * out * (inp + r)
@@ -289,6 +307,7 @@ def main():
         },
         "decode_ms": round(t_dec, 5),
         "decode_GBps": round(value, 2),
+        "decode_bwd_ms": round(t_dbw, 5),
         "train_ms_fwd_bwd": round(t_tr, 4),
         "train_TFLOPs": round(tflops, 2),
         "train_frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -297,6 +316,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_gemv1"),
             "kernel": "fused dequant product, M=1", "kernel_ms": round(k_ms, 5),
             "algorithmic_bytes_per_launch": kb,
+        },
+        "roofline_decode_bwd": {
+            "bound": "hbm", "kernel": "dX and dU pass over the weight rows, M=1",
+            "kernel_ms": round(kbw_ms, 5), "algorithmic_bytes_per_launch": kbw,
+            "achieved": round(kbw / (kbw_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kbw / (kbw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_dxv"),
         },
         "roofline_train": {
             "bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -436,7 +436,7 @@ struct BwdPlan {
     int Zdu, Zdb, Zda;
     bool skinny;     // r <= 64: the lora_bwd.hip products
     size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, off_sc,
-        total;
+        off_dxv, total;
 };
 
 BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
@@ -469,6 +469,10 @@ BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     if (nf4::use_big_gemm(M, cols)) {  // fp32 block scales of the register-dequant dX
         p.off_sc = o;
         o += nf4::rd_scales_bytes(rows, cols);
+    }
+    if (nf4::use_bwd_small(rows, cols, M)) {  // the few-token backward
+        p.off_dxv = o;
+        o = nf4::align256(o + nf4::bwd_small_ws_bytes(rows, cols, M, r));
     }
     p.total = o;
     return p;
@@ -578,6 +582,8 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     uint16_t* duh = reinterpret_cast<uint16_t*>(w + bp.off_duh);
     uint16_t* dul = reinterpret_cast<uint16_t*>(w + bp.off_dul);
     float* part = reinterpret_cast<float*>(w + bp.off_part);
+    if (use_bwd_small(out, in, M))
+        return backward_small(q, x, dH, M, A, r, B, scale, u, dX, dA, dB, w + bp.off_dxv, st);
     const bool dh_vec = al16(dH) && (out % 8 == 0);
     if (bp.skinny) {
         uint16_t* bt = reinterpret_cast<uint16_t*>(w + bp.off_bt);

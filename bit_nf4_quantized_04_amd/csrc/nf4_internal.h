@@ -71,6 +71,15 @@ size_t rd_scales_bytes(int64_t rows, int64_t cols);
 bool use_rd(const QView& q, int64_t M, int r, int KL);
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
                const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
+// The backward for a few tokens (M <= kBwdSmallMaxM, bwd_small.hip): fp32
+// rank-r kernels and the transposed dequant-GEMV for dX, with
+// bwd_small_ws_bytes() of workspace.
+constexpr int64_t kBwdSmallMaxM = 16;
+bool use_bwd_small(int64_t rows, int64_t cols, int64_t M);
+size_t bwd_small_ws_bytes(int64_t rows, int64_t cols, int64_t M, int r);
+int backward_small(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M, const uint16_t* A, int r,
+                   const uint16_t* B, float scale, const float* u, uint16_t* dX, float* dA, float* dB, char* ws,
+                   hipStream_t st);
 // dX with the weight dequantized into a row-major LDS tile read transposed
 // (256 x 256 tiles); double quant needs rd_scales_bytes() of workspace.
 bool use_dx_rd(const QView& q, int64_t M, int r, int KL);

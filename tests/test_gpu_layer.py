@@ -84,6 +84,36 @@ def test_backward_small(F, M, out, inp, r):
         U.assert_close("dB", dB.cpu().numpy(), g["dB"])
 
 
+# The few-token backward (M <= 16): one pass over the weight rows for dX and
+# dU.  Ragged rows, several 1024-column slabs and rank-r slabs, r not a
+# multiple of 4, absmax without double quant, a non-power-of-two double-quant
+# group, and enough rows for many row chunks.
+@pytest.mark.parametrize("M,out,inp,r,dq,group", [
+    (1, 96, 128, 4, False, 256),
+    (2, 100, 192, 3, True, 256),
+    (16, 64, 1088, 65, True, 256),
+    (7, 333, 1024, 16, False, 256),
+    (1, 8192, 128, 64, True, 256),
+    (3, 250, 640, 12, True, 100),
+])
+def test_backward_few_tokens(F, M, out, inp, r, dq, group):
+    import torch
+
+    w, x, a, b, dh = _case(M * 29 + out + r, M, out, inp, r)
+    s = 2.0
+    q = F.nf4_quantize(U.f32(w), double_quant=dq, dq_group=group)
+    _, u = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), s, want_u=True)
+    dX, dA, dB = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), s, u=u)
+    _, dA2, dB2 = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), s, u=u, want_dx=False)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=dq, dq_group=group), w.shape, dq_group=group)
+    g = O.backward(wb, x, dh, a, b, s)
+    U.assert_close("dX", U.bf16_to_f64(dX), g["dX"])
+    U.assert_close("dA", dA.cpu().numpy(), g["dA"])
+    U.assert_close("dB", dB.cpu().numpy(), g["dB"])
+    assert torch.equal(dA, dA2) and torch.equal(dB, dB2)
+
+
 def test_zero_B_gives_base_output(F):
     """B = 0: the output is the base product alone (LoRA init in the pages)."""
     import torch

@@ -424,7 +424,7 @@ FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
         return p;
     }
     FwdPlan p = plan_down(rows, cols, M, r);
-    if (nf4::use_big_gemm(M, rows)) {  // fp32 block scales of the register-dequant GEMM
+    if (nf4::use_rd_grid(M, rows) || nf4::use_big_gemm(M, rows)) {  // fp32 block scales of the register-dequant GEMM
         p.off_sc = p.total;
         p.total += nf4::rd_scales_bytes(rows, cols);
     }
@@ -436,7 +436,7 @@ struct BwdPlan {
     int Zdu, Zdb, Zda;
     bool skinny;     // r <= 64: the lora_bwd.hip products
     size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, off_sc,
-        off_dxv, total;
+        off_dxv, off_dxp, total;
 };
 
 BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
@@ -466,9 +466,12 @@ BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     if (size_t(p.Zdb) * rows * r > part) part = size_t(p.Zdb) * rows * r;
     if (size_t(p.Zda) * r * cols > part) part = size_t(p.Zda) * r * cols;
     p.off_part = o; o = nf4::align256(o + part * 4);
-    if (nf4::use_big_gemm(M, cols)) {  // fp32 block scales of the register-dequant dX
-        p.off_sc = o;
-        o += nf4::rd_scales_bytes(rows, cols);
+    if (!nf4::use_bwd_small(rows, cols, M) &&
+        nf4::cdiv(M, 256) * nf4::cdiv(cols, 256) >= 16) {  // register-dequant dX: fp32 block scales,
+        p.off_sc = o;                                       // split partials
+        o = nf4::align256(o + nf4::rd_scales_bytes(rows, cols));
+        p.off_dxp = o;
+        o = nf4::align256(o + nf4::dx_rd_part_bytes(M, rows, cols));
     }
     if (nf4::use_bwd_small(rows, cols, M)) {  // the few-token backward
         p.off_dxv = o;
@@ -536,22 +539,18 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {
-        if (use_big_gemm(M, q.rows)) {
-            if (use_rd(q, M, 0, 0))
-                return forward_rd(q, x, M, nullptr, 0, nullptr, 0, h, reinterpret_cast<float*>(w + fp.off_sc), st);
-            return forward_big(q, x, M, nullptr, 0, nullptr, 0, h, st);
-        }
+        if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0))
+            return forward_rd(q, x, M, nullptr, 0, nullptr, 0, h, reinterpret_cast<float*>(w + fp.off_sc), st);
+        if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, nullptr, 0, nullptr, 0, h, st);
         return gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1, true);
     }
     float* u = u_out ? u_out : reinterpret_cast<float*>(w + fp.off_u);
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
     int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext);
     if (rc) return rc;
-    if (use_big_gemm(M, q.rows)) {
-        if (use_rd(q, M, r, ext_cols(r)))
-            return forward_rd(q, x, M, ext, ext_cols(r), B, r, h, reinterpret_cast<float*>(w + fp.off_sc), st);
-        return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
-    }
+    if (use_rd_grid(M, q.rows) && use_rd(q, M, r, ext_cols(r)))
+        return forward_rd(q, x, M, ext, ext_cols(r), B, r, h, reinterpret_cast<float*>(w + fp.off_sc), st);
+    if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};
     return gemm(st, M, q.rows, lx, lw, q.cols, le, lb, ext_cols(r), OutBF16{h, q.rows}, 1, true);
@@ -634,8 +633,9 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     }
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
-        if (use_big_gemm(M, in) && use_dx_rd(q, M, r, KL))
-            rc = dx_rd(q, dH, M, duext, KL, A, r, dX, reinterpret_cast<float*>(w + bp.off_sc), st);
+        if (use_dx_rd(q, M, r, KL))
+            rc = dx_rd(q, dH, M, duext, KL, A, r, dX, reinterpret_cast<float*>(w + bp.off_sc),
+                       reinterpret_cast<float*>(w + bp.off_dxp), st);
         else if (use_big_gemm(M, in))
             rc = dx_big(q, dH, M, duext, KL, A, r, dX, st);
         else

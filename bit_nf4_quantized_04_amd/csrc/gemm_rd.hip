@@ -436,9 +436,11 @@ struct DxArgs {
     const uint16_t* dh;    // [M][out]
     const uint16_t* ext;   // [M][KL] (dU hi | lo), or null
     const uint16_t* A;     // [r][in]
-    uint16_t* dx;          // [M][in]
+    uint16_t* dx;          // [M][in] (one split)
+    float* part;           // [nsplit][M][in] fp32 partials (several splits)
     int64_t M, out, in;
     int KL, r;
+    int spl;               // weight-row steps per split (a multiple of four)
 };
 
 // dH tile layout: row m of 4 chunks, chunk c stored at c ^ ((m >> 2) & 3)
@@ -565,11 +567,11 @@ __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, 
 // ring indices are static (the launcher guarantees a multiple of four
 // steps).  The buffers are separate arrays so that the compiler can see that
 // a DMA into one never overlaps reads of another.
-__device__ __forceinline__ void dx_loop(const DxCtx& c, uint4* __restrict__ B0, uint4* __restrict__ B1,
-                                        uint4* __restrict__ B2, uint4* __restrict__ B3,
+__device__ __forceinline__ void dx_loop(const DxCtx& c, int sb, int se, uint4* __restrict__ B0,
+                                        uint4* __restrict__ B1, uint4* __restrict__ B2, uint4* __restrict__ B3,
                                         uint16_t* __restrict__ W0, uint16_t* __restrict__ W1,
                                         f32x16_t (&acc)[8][2]) {
-    for (int t = 0; t < c.S1; t += 4) {
+    for (int t = sb; t < se; t += 4) {
         dx_step(c, t, B0, B1, B3, W0, W1, acc);
         dx_step(c, t + 1, B1, B2, B0, W1, W0, acc);
         dx_step(c, t + 2, B2, B3, B1, W0, W1, acc);
@@ -593,10 +595,16 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     const int64_t gm = (nMt - first < G) ? (nMt - first) : G;
     const int64_t tm = first + (lin % gsz) % gm, tn = (lin % gsz) / gm;
     const int64_t m0 = tm * RM, i0 = tn * RN;
+    // split z of the reduction: weight-row steps [sb, se); the last split
+    // also takes the rank-r steps
+    const int z = int(blockIdx.y);
+    const bool last = z == int(gridDim.y) - 1;
 
     DxCtx c{a};
     c.S1 = int(a.out / DK);
     c.S = c.S1 + (a.ext ? a.KL / DK : 0);
+    const int sb = z * a.spl;
+    const int se = (sb + a.spl < c.S1) ? sb + a.spl : c.S1;
     c.w = w;
     c.lane = lane;
     c.tid = tid;
@@ -631,22 +639,25 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int S1 = c.S1, S = c.S;
-    // ---- prologue: steps 0, 1, 2 (dH tile, then staging) in flight
-    c.hdma(0, h0);
-    c.sdma(0, h0);
-    c.hdma(1 < S ? 1 : S - 1, h1);
-    c.sdma(1 < S1 ? 1 : S1 - 1, h1);
-    c.hdma(2 < S ? 2 : S - 1, h2);
-    c.sdma(2 < S1 ? 2 : S1 - 1, h2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));  // step 0
+    // ---- prologue: steps sb, sb+1, sb+2 (dH tile, then staging) in flight
+    c.hdma(sb, h0);
+    c.sdma(sb, h0);
+    c.hdma(sb + 1 < S ? sb + 1 : S - 1, h1);
+    c.sdma(sb + 1 < S1 ? sb + 1 : S1 - 1, h1);
+    c.hdma(sb + 2 < S ? sb + 2 : S - 1, h2);
+    c.sdma(sb + 2 < S1 ? sb + 2 : S1 - 1, h2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));  // step sb
     c.dequant(h0, wt0);
     __syncthreads();
 
-    dx_loop(c, h0, h1, h2, h3, wt0, wt1, acc);
+    dx_loop(c, sb, se, h0, h1, h2, h3, wt0, wt1, acc);
+    // the loop's last steps prefetched past the split: let those DMAs land
+    // before the workgroup can end
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- rank-r steps: dH-side tiles from the ring (the first three were
-    // DMA'd by the loop), the B rows copied from A
-    for (int s = S1; s < S; ++s) {
+    // ---- rank-r steps (last split): dH-side tiles from the ring (the first
+    // three were DMA'd by the loop), the B rows copied from A
+    for (int s = S1; s < (last ? S : S1); ++s) {
         const int k = s & 3;
         uint4* ht = k == 0 ? h0 : k == 1 ? h1 : k == 2 ? h2 : h3;
         if (s + 3 < S) c.hdma(s + 3, k == 0 ? h3 : k == 1 ? h0 : k == 2 ? h1 : h2);
@@ -664,6 +675,8 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     }
 
     // D layout: lane holds column lane%32 and rows 8(v/4) + 4(lane/32) + v%4
+    float* pz = a.part + int64_t(z) * M * N;
+    const bool split = gridDim.y > 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t n = i0 + 64 * w + 32 * j + (lane & 31);
@@ -673,8 +686,29 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M) a.dx[m * N + n] = to_bf16(acc[i][j][v]);
+                if (m < M) {
+                    if (split)
+                        pz[m * N + n] = acc[i][j][v];
+                    else
+                        a.dx[m * N + n] = to_bf16(acc[i][j][v]);
+                }
             }
+    }
+}
+
+// dX = bf16 of the sum of the split partials, in split order
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int Z, int64_t n,
+                                                   uint16_t* __restrict__ out) {
+    for (int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4; i < n; i += int64_t(gridDim.x) * 1024) {
+        float4 a = *reinterpret_cast<const float4*>(part + i);
+        for (int zz = 1; zz < Z; ++zz) {
+            const float4 b = *reinterpret_cast<const float4*>(part + int64_t(zz) * n + i);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        *reinterpret_cast<uint2*>(out + i) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
     }
 }
 
@@ -716,23 +750,50 @@ int block_scales(const QView& q, float* scale_ws, const float** scales, hipStrea
     return NF4_OK;
 }
 
+bool use_rd_grid(int64_t M, int64_t N) { return cdiv(M, RM) * cdiv(N, RN) >= 32; }
+
 bool use_dx_rd(const QView& q, int64_t M, int r, int KL) {
     // whole steps of 32 weight rows in fours, whole 256-column tiles, 32-bit offsets
-    return q.rows % (4 * DK) == 0 && q.cols % RN == 0 && (r == 0 || KL % DK == 0) &&
-           q.rows * q.cols / 2 < (int64_t(1) << 32) && M * q.rows * 2 < (int64_t(1) << 32) &&
-           (r == 0 || M * KL * 2 < (int64_t(1) << 32));
+    return cdiv(M, RM) * cdiv(q.cols, RN) >= 16 && q.rows % (4 * DK) == 0 && q.cols % RN == 0 &&
+           (r == 0 || KL % DK == 0) && q.rows * q.cols / 2 < (int64_t(1) << 32) &&
+           M * q.rows * 2 < (int64_t(1) << 32) && (r == 0 || M * KL * 2 < (int64_t(1) << 32));
+}
+
+// Splits of the dX reduction: enough workgroups for the GPU when the output
+// tiles alone are too few, each split a whole number of four-step groups.
+int dx_splits(int64_t M, int64_t rows, int64_t cols) {
+    const int64_t T = cdiv(M, RM) * cdiv(cols, RN);
+    int64_t Z = T >= 192 ? 1 : std::min<int64_t>(8, std::max<int64_t>(1, 256 / T));
+    const int64_t S1 = rows / DK;
+    const int64_t spl = cdiv(cdiv(S1, Z), 4) * 4;
+    return int(cdiv(S1, spl));
+}
+
+size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols) {
+    const int Z = dx_splits(M, rows, cols);
+    return Z > 1 ? align256(size_t(Z) * size_t(M) * size_t(cols) * 4) : 0;
 }
 
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
-          int r, uint16_t* dX, float* scale_ws, hipStream_t st) {
+          int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st) {
     const float* scales;
     int rc = block_scales(q, scale_ws, &scales, st);
     if (rc) return rc;
-    DxArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, dH, r > 0 ? duext : nullptr, A, dX,
-             M, q.rows, q.cols, KL, r};
+    const int Z = dx_splits(M, q.rows, q.cols);
+    const int S1 = int(q.rows / DK);
+    const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);
+    DxArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, dH, r > 0 ? duext : nullptr, A, dX, part_ws,
+             M, q.rows, q.cols, KL, r, spl};
     const int64_t T = cdiv(M, RM) * cdiv(q.cols, RN);
-    launch_dominant(k_dx_rd, dim3(unsigned(T)), dim3(RT), 0, st, a);
-    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+    launch_dominant(k_dx_rd, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
+    if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    if (Z > 1) {
+        const int64_t n = M * q.cols;  // a multiple of 256
+        hipLaunchKernelGGL(k_split_sum, dim3(unsigned(std::min<int64_t>(cdiv(n, 1024), 8192))), dim3(256), 0, st,
+                           part_ws, Z, n, dX);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    }
+    return NF4_OK;
 }
 
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,

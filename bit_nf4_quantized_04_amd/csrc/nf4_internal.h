@@ -82,9 +82,14 @@ int backward_small(const QView& q, const uint16_t* x, const uint16_t* dH, int64_
                    hipStream_t st);
 // dX with the weight dequantized into a row-major LDS tile read transposed
 // (256 x 256 tiles); double quant needs rd_scales_bytes() of workspace.
+// (Both take grids from 16-32 tiles of 256 x 256 up; dX splits its
+// reduction when the tiles are too few to fill the GPU, with
+// dx_rd_part_bytes() of workspace for the fp32 partials.)
+bool use_rd_grid(int64_t M, int64_t N);
 bool use_dx_rd(const QView& q, int64_t M, int r, int KL);
+size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols);
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
-          int r, uint16_t* dX, float* scale_ws, hipStream_t st);
+          int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st);
 int dx_big(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL,
            const uint16_t* A, int r, uint16_t* dX, hipStream_t st);
 // Skinny rank-r products (lora_bwd.hip), r <= 64: fp32 partials over Z

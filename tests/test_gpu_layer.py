@@ -238,7 +238,9 @@ def test_multi_adapter_workload(F):
 
 # Shapes that take the large-tile (256 x 256) kernels: at least 512 output
 # tiles, ragged in every dimension, and cheap for the oracle.
-@pytest.mark.parametrize("M,out,inp,r", [(4000, 8200, 192, 16), (4096, 8192, 128, 0)])
+# (600, 4096, 1024, 8): 48 tiles of 256 x 256, the register-dequant kernel
+# on a grid smaller than the GPU.
+@pytest.mark.parametrize("M,out,inp,r", [(4000, 8200, 192, 16), (4096, 8192, 128, 0), (600, 4096, 1024, 8)])
 def test_forward_large_tiles(F, M, out, inp, r):
     import torch
 
@@ -256,7 +258,9 @@ def test_forward_large_tiles(F, M, out, inp, r):
     U.assert_close("h", U.bf16_to_f64(h), href)
 
 
-@pytest.mark.parametrize("M,out,inp,r", [(4000, 500, 8256, 16), (4096, 256, 8192, 64)])
+# (1000, 1024, 2048, 24): 32 dX tiles, so the reduction over the weight rows
+# is split eight ways (the rank-r steps in the last split), ragged M.
+@pytest.mark.parametrize("M,out,inp,r", [(4000, 500, 8256, 16), (4096, 256, 8192, 64), (1000, 1024, 2048, 24)])
 def test_backward_large_tiles(F, M, out, inp, r):
     import torch
 

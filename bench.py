@@ -217,6 +217,25 @@ def main():
     def decode_bwd_step(i):
         F.qlora_linear_backward(qs[i % len(qs)], x1, dH1, A, B, scale, u=u1, ws=ws_b1)
 
+    # the multi-adapter forward (its own workload: 64 adapters on a 4096 x 4096 base)
+    cm = 5
+    shm = wl.SHAPES[cm]
+    Mm = max(shm["M"]) if isinstance(shm["M"], (list, tuple)) else shm["M"]
+    wtm = torch.from_numpy(wl.weight(cm)).to(dev)
+    qm = F.nf4_quantize(wtm, double_quant=True)
+    del wtm
+    abm, bbm = wl.adapter_bank(cm)
+    xm = bf(wl.activations(cm, Mm))
+    Abm, Bbm = bf(abm), bf(bbm)
+    idsm = torch.from_numpy(wl.adapter_ids(cm, Mm, shm["n_adapters"])).to(dev)
+    scm = torch.full((shm["n_adapters"],), shm["alpha"] / shm["r"], dtype=torch.float32, device=dev)
+    hm = torch.empty((Mm, shm["out"]), dtype=torch.bfloat16, device=dev)
+    wsm = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD_MULTI, shm["out"], shm["inp"], Mm, shm["r"],
+                                                  shm["n_adapters"]), 256), dtype=torch.uint8, device=dev)
+
+    def multi_step(i):
+        F.qlora_linear_forward_multi(qm, xm, Abm, Bbm, scm, idsm, ws=wsm, out=hm)
+
     def train_step(i):
         _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
         F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
@@ -257,6 +276,8 @@ def main():
     t_dbw, _ = timed(decode_bwd_step, K, W)
     _, k_dbw = timed(decode_bwd_step, K, 1, hook_events=True)
     t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))
+    t_mu, _ = timed(multi_step, K, W)
+    mu_flops = 2 * Mm * shm["out"] * shm["inp"] + 2 * Mm * shm["r"] * (shm["inp"] + shm["out"])
     # dominant kernels of the training pass: forward product and dX product
     fwd_k, bwd_k = [], []
 
@@ -316,6 +337,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_gemv1"),
             "kernel": "fused dequant product, M=1", "kernel_ms": round(k_ms, 5),
             "algorithmic_bytes_per_launch": kb,
+        },
+        "multi_adapter": {
+            "workload": "%d adapters r=%d on %d->%d NF4 base, %d tokens" % (
+                shm["n_adapters"], shm["r"], shm["inp"], shm["out"], Mm),
+            "ms": round(t_mu, 4), "TFLOPs": round(mu_flops / (t_mu * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(mu_flops / (t_mu * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "roofline_decode_bwd": {
             "bound": "hbm", "kernel": "dX and dU pass over the weight rows, M=1",

@@ -523,7 +523,9 @@ int zero_f32(float* p, int64_t n, hipStream_t st) {
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters) {
     if (op == QLORA_OP_FORWARD) return plan_forward(rows, cols, M, r).total;
     if (op == QLORA_OP_BACKWARD) return plan_backward(rows, cols, M, r).total;
-    if (op == QLORA_OP_FORWARD_MULTI) return align256(size_t(M) * (r > 0 ? r : 0) * 4);
+    if (op == QLORA_OP_FORWARD_MULTI)  // su, then the fp32 block scales of the register-dequant kernel
+        return align256(size_t(M) * (r > 0 ? r : 0) * 4) +
+               (nf4::use_rd_grid(M, rows) ? nf4::rd_scales_bytes(rows, cols) : 0);
     (void)n_adapters;
     return 0;
 }
@@ -656,6 +658,9 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
     hipLaunchKernelGGL(k_multi_down, dim3(unsigned(M)), dim3(256), 0, st, x, q.cols, Ab, n, r,
                        scales, ids, su);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0) && al16(Bb) && al16(ws))
+        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h,
+                                reinterpret_cast<float*>(static_cast<char*>(ws) + align256(size_t(M) * r * 4)), st);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     return gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
                 OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1, true);

@@ -128,7 +128,40 @@ struct FwdArgs {
     uint16_t* h;           // [M][N]
     int64_t M, N, K;
     int KL, r;
+    // multi-adapter epilogue (su null: none): h[m][n] += sum_j su[m][j] Bb[ids[m]][n][j]
+    const float* su;       // [M][rm] s_id * x A_id^T
+    const int32_t* ids;    // [M]; an id outside [0, n_ad) adds nothing
+    const uint16_t* Bb;    // [n_ad][N][rm]
+    int n_ad, rm;
 };
+
+// The gathered rank-r term of one output of the multi-adapter forward, fp32.
+__device__ __forceinline__ float multi_term(const FwdArgs& a, int64_t m, int64_t n) {
+    const int id = a.ids[m];
+    if (id < 0 || id >= a.n_ad) return 0.0f;
+    const int rm = a.rm;
+    const float* s = a.su + m * rm;
+    const uint16_t* b = a.Bb + (int64_t(id) * a.N + n) * rm;
+    float l = 0.0f;
+    if ((rm & 7) == 0) {  // 16-byte rows of B, 32-byte rows of su (the launcher checks alignment)
+        for (int j = 0; j < rm; j += 8) {
+            const uint4 bv = *reinterpret_cast<const uint4*>(b + j);
+            const float4 s0 = *reinterpret_cast<const float4*>(s + j);
+            const float4 s1 = *reinterpret_cast<const float4*>(s + j + 4);
+            l = __builtin_fmaf(s0.x, bf16_lo(bv.x), l);
+            l = __builtin_fmaf(s0.y, bf16_hi(bv.x), l);
+            l = __builtin_fmaf(s0.z, bf16_lo(bv.y), l);
+            l = __builtin_fmaf(s0.w, bf16_hi(bv.y), l);
+            l = __builtin_fmaf(s1.x, bf16_lo(bv.z), l);
+            l = __builtin_fmaf(s1.y, bf16_hi(bv.z), l);
+            l = __builtin_fmaf(s1.z, bf16_lo(bv.w), l);
+            l = __builtin_fmaf(s1.w, bf16_hi(bv.w), l);
+        }
+    } else {
+        for (int j = 0; j < rm; ++j) l = __builtin_fmaf(s[j], bf16_f(b[j]), l);
+    }
+    return l;
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -278,6 +311,7 @@ __device__ __forceinline__ void nf4_step(const FwdCtx& c, int t, const uint4* cu
     interleave();
 }
 
+template <bool MULTI>
 __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     // the ring of x tiles and the two weight slots: separate arrays, so that
     // the compiler can see that a DMA into one never overlaps reads of another
@@ -389,17 +423,40 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 
     // D layout of the 32x32 MFMA: lane holds column lane%32 and rows
     // 8*(v/4) + 4*(lane/32) + v%4, v = 0..15.
+    if constexpr (!MULTI) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + 64 * w + 32 * j + c.nl;
-        if (n >= N) continue;
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + 64 * w + 32 * j + c.nl;
+            if (n >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * c.hh + (v & 3);
-                if (m < M) a.h[m * N + n] = to_bf16(acc[i][j][v]);
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * c.hh + (v & 3);
+                    if (m < M) a.h[m * N + n] = to_bf16(acc[i][j][v]);
+                }
+        }
+    } else {
+        // Gathered rank-r term: each 32-row slab of the wave's accumulators
+        // goes through LDS (the x ring is free now), then lane l finishes
+        // column 64w + l row by row, so the token's id and su row are
+        // wave-uniform and the B_id rows are read contiguously.
+        __syncthreads();  // every wave is past its last read of the x ring
+        float* stg = reinterpret_cast<float*>(xs0) + w * (32 * 64);
+        const int64_t n = n0 + 64 * w + lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    stg[(8 * (v >> 2) + 4 * c.hh + (v & 3)) * 64 + 32 * j + c.nl] = acc[i][j][v];
+#pragma unroll 1
+            for (int rr = 0; rr < 32; ++rr) {
+                const int64_t m = m0 + 32 * i + rr;
+                if (m < M && n < N) a.h[m * N + n] = to_bf16(stg[rr * 64 + lane] + multi_term(a, m, n));
             }
+        }
     }
 }
 
@@ -810,9 +867,21 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
         scales = scale_ws;
     }
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, r > 0 ? ext : nullptr, B, h,
-              M, q.rows, q.cols, KL, r};
+              M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
-    launch_dominant(k_fwd_rd, dim3(unsigned(T)), dim3(RT), 0, st, a);
+    launch_dominant(k_fwd_rd<false>, dim3(unsigned(T)), dim3(RT), 0, st, a);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
+                     const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, hipStream_t st) {
+    const float* scales;
+    int rc = block_scales(q, scale_ws, &scales, st);
+    if (rc) return rc;
+    FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, nullptr, nullptr, h,
+              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r};
+    const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
+    launch_dominant(k_fwd_rd<true>, dim3(unsigned(T)), dim3(RT), 0, st, a);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

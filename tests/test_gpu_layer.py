@@ -213,6 +213,29 @@ def test_multi_adapter_small(F):
     U.assert_close("h", U.bf16_to_f64(h), href)
 
 
+def test_multi_adapter_large_tiles(F):
+    """The multi-adapter forward on the 256 x 256 register-dequant kernel (48
+    tiles): ragged M, invalid ids, r not a multiple of 8 (the scalar gather)."""
+    import torch
+
+    rng = np.random.default_rng(23)
+    out, inp, r, n, M = 4096, 512, 6, 5, 700
+    w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
+    x = _bits(rng, (M, inp), 1.0)
+    ab = _bits(rng, (n, r, inp), 0.05)
+    bb = _bits(rng, (n, out, r), 0.05)
+    scales = np.array([2.0, 0.5, 1.0, 4.0, 0.25], dtype=np.float32)
+    ids = rng.integers(-1, n + 1, size=M).astype(np.int32)
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    h = F.qlora_linear_forward_multi(q, U.bf(x), U.bf(ab), U.bf(bb),
+                                     torch.from_numpy(scales).to(U.dev()),
+                                     torch.from_numpy(ids).to(U.dev()))
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    href = O.forward_multi(wb, x, ab, bb, scales.astype(np.float64), ids)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+
+
 def test_multi_adapter_workload(F):
     """64 adapters, r = 16, 2048 tokens with uniform ids on the 4096 x 4096 base."""
     import torch

@@ -525,7 +525,9 @@ size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int
     if (op == QLORA_OP_BACKWARD) return plan_backward(rows, cols, M, r).total;
     if (op == QLORA_OP_FORWARD_MULTI)  // su, then the fp32 block scales of the register-dequant kernel
         return align256(size_t(M) * (r > 0 ? r : 0) * 4) +
-               (nf4::use_rd_grid(M, rows) ? nf4::rd_scales_bytes(rows, cols) : 0);
+               (nf4::use_rd_grid(M, rows)
+                    ? align256(nf4::rd_scales_bytes(rows, cols)) + nf4::fwd_multi_part_bytes(M, rows, cols)
+                    : 0);
     (void)n_adapters;
     return 0;
 }
@@ -659,8 +661,11 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
                        scales, ids, su);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0) && al16(Bb) && al16(ws))
-        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h,
-                                reinterpret_cast<float*>(static_cast<char*>(ws) + align256(size_t(M) * r * 4)), st);
+    {
+        char* sc = static_cast<char*>(ws) + align256(size_t(M) * r * 4);
+        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h, reinterpret_cast<float*>(sc),
+                                reinterpret_cast<float*>(sc + align256(rd_scales_bytes(q.rows, q.cols))), st);
+    }
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     return gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
                 OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1, true);

@@ -133,11 +133,15 @@ struct FwdArgs {
     const int32_t* ids;    // [M]; an id outside [0, n_ad) adds nothing
     const uint16_t* Bb;    // [n_ad][N][rm]
     int n_ad, rm;
+    // split reduction (gridDim.y > 1): fp32 partials [nsplit][M][N], split z
+    // taking weight steps [z*spl, z*spl + spl) (and the rank-r steps if last)
+    float* part;
+    int spl;
 };
 
-// The gathered rank-r term of one output of the multi-adapter forward, fp32.
-__device__ __forceinline__ float multi_term(const FwdArgs& a, int64_t m, int64_t n) {
-    const int id = a.ids[m];
+// The gathered rank-r term of one output of the multi-adapter forward, fp32
+// (id: the token's adapter).
+__device__ __forceinline__ float multi_term(const FwdArgs& a, int id, int64_t m, int64_t n) {
     if (id < 0 || id >= a.n_ad) return 0.0f;
     const int rm = a.rm;
     const float* s = a.su + m * rm;
@@ -370,22 +374,26 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int S1 = c.S1, S = c.S;
+    const int z = int(blockIdx.y);
+    const bool last = z == int(gridDim.y) - 1;
+    const int sb = z * a.spl;
+    const int se = (sb + a.spl < S1) ? sb + a.spl : S1;
     // ---- prologue, in the issue order of the steady state: x tile s, then
-    // weights s, for s = 0, 1, 2 (weights 2 go into slot 0 once weights 0
-    // are in registers)
-    c.xdma(0, xs0);
-    c.wdma(0, wb0);
-    c.xdma(1 < S ? 1 : S - 1, xs1);
-    c.wdma(1 < S1 ? 1 : S1 - 1, wb1);
-    c.xdma(2 < S ? 2 : S - 1, xs2);
+    // weights s, for s = sb, sb+1, sb+2 (weights sb+2 go into slot 0 once
+    // weights sb are in registers)
+    c.xdma(sb, xs0);
+    c.wdma(sb, wb0);
+    c.xdma(sb + 1 < S ? sb + 1 : S - 1, xs1);
+    c.wdma(sb + 1 < S1 ? sb + 1 : S1 - 1, wb1);
+    c.xdma(sb + 2 < S ? sb + 2 : S - 1, xs2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * VM_XTILE + VM_WSLOT));
-    __syncthreads();  // x tile 0 and the step-0 weights ready
+    __syncthreads();  // x tile sb and the step-sb weights ready
     uint4 cw[2], cw2[2];
     Planes pl[2], pl2[2];
     {
         float sc[2];
         c.wread(wb0, cw, sc);
-        c.wdma(2 < S1 ? 2 : S1 - 1, wb0);
+        c.wdma(sb + 2 < S1 ? sb + 2 : S1 - 1, wb0);
         pl[0] = make_planes(sc[0]);
         pl[1] = make_planes(sc[1]);
     }
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 
     // four steps per iteration so every ring index is static (the launcher
     // guarantees S1 % 4 == 0)
-    for (int t = 0; t < S1; t += 4) {
+    for (int t = sb; t < se; t += 4) {
         nf4_step(c, t, xs0, xs1, xs3, wb1, acc, fa, ba, cw, pl, cw2, pl2);
         nf4_step(c, t + 1, xs1, xs2, xs0, wb0, acc, fa, ba, cw2, pl2, cw, pl);
         nf4_step(c, t + 2, xs2, xs3, xs1, wb1, acc, fa, ba, cw, pl, cw2, pl2);
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     // ring, the B operand gathered from global memory
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int s = S1; s < S; ++s) {
+    for (int s = S1; s < (last ? S : S1); ++s) {
         const int k = s & 3;
         const uint4* tl = k == 0 ? xs0 : k == 1 ? xs1 : k == 2 ? xs2 : xs3;
 #pragma unroll
@@ -423,7 +431,21 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 
     // D layout of the 32x32 MFMA: lane holds column lane%32 and rows
     // 8*(v/4) + 4*(lane/32) + v%4, v = 0..15.
-    if constexpr (!MULTI) {
+    if (gridDim.y > 1) {  // one split of the reduction: fp32 partials
+        float* pz = a.part + int64_t(z) * M * N;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + 64 * w + 32 * j + c.nl;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * c.hh + (v & 3);
+                    if (m < M) pz[m * N + n] = acc[i][j][v];
+                }
+        }
+    } else if constexpr (!MULTI) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t n = n0 + 64 * w + 32 * j + c.nl;
@@ -451,10 +473,14 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     stg[(8 * (v >> 2) + 4 * c.hh + (v & 3)) * 64 + 32 * j + c.nl] = acc[i][j][v];
-#pragma unroll 1
+            // the slab's 32 ids, one per lane, read back wave-uniform
+            const int64_t mi = m0 + 32 * i + (lane & 31);
+            const int idv = mi < M ? a.ids[mi] : -1;
+#pragma unroll 8
             for (int rr = 0; rr < 32; ++rr) {
                 const int64_t m = m0 + 32 * i + rr;
-                if (m < M && n < N) a.h[m * N + n] = to_bf16(stg[rr * 64 + lane] + multi_term(a, m, n));
+                const int id = __builtin_amdgcn_readlane(idv, rr);
+                if (m < M && n < N) a.h[m * N + n] = to_bf16(stg[rr * 64 + lane] + multi_term(a, id, m, n));
             }
         }
     }
@@ -769,6 +795,20 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
     }
 }
 
+// The multi-adapter forward after a split reduction: h[m][n] = bf16( the
+// partials summed in split order + the gathered rank-r term ).  A wave takes
+// 64 consecutive columns of one row, so the token's id and su row are
+// wave-uniform and the B_id row segment is contiguous.
+__global__ __launch_bounds__(256) void k_multi_fin(FwdArgs a, int Z) {
+    const int64_t M = a.M, N = a.N, n = M * N;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+        const int64_t m = i / N, col = i % N;
+        float v = a.part[i];
+        for (int zz = 1; zz < Z; ++zz) v += a.part[int64_t(zz) * n + i];
+        a.h[i] = to_bf16(v + multi_term(a, a.ids[m], m, col));
+    }
+}
+
 // fp32 block scales of a double-quantized weight: fl32(fl32(q_b/127) * c_g).
 template <bool GSH>
 __global__ __launch_bounds__(256) void k_block_scales(nf4::QView q, int64_t nb, float* __restrict__ out) {
@@ -867,22 +907,47 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
         scales = scale_ws;
     }
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, r > 0 ? ext : nullptr, B, h,
-              M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0};
+              M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0, nullptr, int(q.cols / RKS)};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
     launch_dominant(k_fwd_rd<false>, dim3(unsigned(T)), dim3(RT), 0, st, a);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
+// Splits of the forward reduction for the multi-adapter pass: enough
+// workgroups for the GPU when the output tiles alone are too few.
+int fwd_multi_splits(int64_t M, int64_t rows, int64_t cols) {
+    const int64_t T = cdiv(M, RM) * cdiv(rows, RN);
+    const int64_t Z = T >= 192 ? 1 : std::min<int64_t>(4, std::max<int64_t>(1, 256 / T));
+    const int64_t S1 = cols / RKS;
+    const int64_t spl = cdiv(cdiv(S1, Z), 4) * 4;
+    return int(cdiv(S1, spl));
+}
+
+size_t fwd_multi_part_bytes(int64_t M, int64_t rows, int64_t cols) {
+    const int Z = fwd_multi_splits(M, rows, cols);
+    return Z > 1 ? align256(size_t(Z) * size_t(M) * size_t(rows) * 4) : 0;
+}
+
 int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
-                     const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, hipStream_t st) {
+                     const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, float* part_ws,
+                     hipStream_t st) {
     const float* scales;
     int rc = block_scales(q, scale_ws, &scales, st);
     if (rc) return rc;
+    const int Z = fwd_multi_splits(M, q.rows, q.cols);
+    const int S1 = int(q.cols / RKS);
+    const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, nullptr, nullptr, h,
-              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r};
+              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
-    launch_dominant(k_fwd_rd<true>, dim3(unsigned(T)), dim3(RT), 0, st, a);
-    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+    launch_dominant(k_fwd_rd<true>, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
+    if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    if (Z > 1) {
+        hipLaunchKernelGGL(k_multi_fin, dim3(unsigned(std::min<int64_t>(cdiv(M * q.rows, 256), 8192))), dim3(256), 0,
+                           st, a, Z);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    }
+    return NF4_OK;
 }
 
 }  // namespace nf4

@@ -88,8 +88,12 @@ int backward_small(const QView& q, const uint16_t* x, const uint16_t* dH, int64_
 bool use_rd_grid(int64_t M, int64_t N);
 // The multi-adapter forward on the same kernel: no rank-r K steps, the
 // gathered term s_id u B_id added in the epilogue (su 16-byte aligned).
+// On a small grid its reduction is split (fwd_multi_part_bytes() of
+// workspace for the fp32 partials) and the gather moves to the partial sum.
+size_t fwd_multi_part_bytes(int64_t M, int64_t rows, int64_t cols);
 int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
-                     const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, hipStream_t st);
+                     const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, float* part_ws,
+                     hipStream_t st);
 bool use_dx_rd(const QView& q, int64_t M, int r, int KL);
 size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols);
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,

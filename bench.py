@@ -236,6 +236,25 @@ def main():
     def multi_step(i):
         F.qlora_linear_forward_multi(qm, xm, Abm, Bbm, scm, idsm, ws=wsm, out=hm)
 
+    # the 7B MLP projection's training pass (its own workload, M = 2048)
+    c7 = WORKLOADS["7b"]
+    sh7 = wl.SHAPES[c7]
+    M7 = max(sh7["M"])
+    q7 = F.nf4_quantize(torch.from_numpy(wl.weight(c7)).to(dev), double_quant=True)
+    a7, b7 = wl.adapters(c7)
+    A7, B7 = bf(a7), bf(b7)
+    x7, dH7 = bf(wl.activations(c7, M7)), bf(wl.upstream_grad(c7, M7))
+    s7 = sh7["alpha"] / sh7["r"]
+    wsf7 = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, sh7["out"], sh7["inp"], M7, sh7["r"]), 256),
+                       dtype=torch.uint8, device=dev)
+    wsb7 = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD, sh7["out"], sh7["inp"], M7, sh7["r"]), 256),
+                       dtype=torch.uint8, device=dev)
+    h7 = torch.empty((M7, sh7["out"]), dtype=torch.bfloat16, device=dev)
+
+    def train7_step(i):
+        _, u = F.qlora_linear_forward(q7, x7, A7, B7, s7, want_u=True, ws=wsf7, out=h7)
+        F.qlora_linear_backward(q7, x7, dH7, A7, B7, s7, u=u, ws=wsb7)
+
     def train_step(i):
         _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
         F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
@@ -277,6 +296,8 @@ def main():
     _, k_dbw = timed(decode_bwd_step, K, 1, hook_events=True)
     t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))
     t_mu, _ = timed(multi_step, K, W)
+    t_7b, _ = timed(train7_step, K, W)
+    f7 = sum(train_flops(sh7["out"], sh7["inp"], M7, sh7["r"]))
     mu_flops = 2 * Mm * shm["out"] * shm["inp"] + 2 * Mm * shm["r"] * (shm["inp"] + shm["out"])
     # dominant kernels of the training pass: forward product and dX product
     fwd_k, bwd_k = [], []
@@ -337,6 +358,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_gemv1"),
             "kernel": "fused dequant product, M=1", "kernel_ms": round(k_ms, 5),
             "algorithmic_bytes_per_launch": kb,
+        },
+        "train_7b": {
+            "workload": "7B MLP %d->%d NF4 + double quant, r=%d, M=%d, forward + backward" % (
+                sh7["inp"], sh7["out"], sh7["r"], M7),
+            "ms": round(t_7b, 4), "TFLOPs": round(f7 / (t_7b * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(f7 / (t_7b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "multi_adapter": {
             "workload": "%d adapters r=%d on %d->%d NF4 base, %d tokens" % (

@@ -92,10 +92,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int64_t N = q.rows, K = q.cols;
     const int nkb = int(K / 64);
     const int nbs = (r + 63) / 64;  // rank-r slabs
-    const int tok = int(blockIdx.x % unsigned(M));
-    const int rest = int(blockIdx.x / unsigned(M));
-    const int slab = rest % (nslab + nbs), chunk = rest / (nslab + nbs);
     const int nchunk = int((N + rows_chunk - 1) / rows_chunk);
+    // XCD-aware order (workgroups are dealt round-robin to the 8 XCDs): each
+    // XCD walks a contiguous run of work items, so the slabs of one row
+    // chunk share that XCD's L2 for the chunk's scale-code lines.  The grid
+    // is padded to a multiple of 8; the padding exits at once.
+    const int items = M * (nslab + nbs) * nchunk;
+    const int per = int(gridDim.x) / 8;
+    const int lin = int(blockIdx.x % 8u) * per + int(blockIdx.x / 8u);
+    if (lin >= items) return;
+    const int tok = lin % M;
+    const int rest = lin / M;
+    const int slab = rest % (nslab + nbs), chunk = rest / (nslab + nbs);
     const int64_t row0 = int64_t(chunk) * rows_chunk;
     const int64_t row_end = (row0 + rows_chunk < N) ? row0 + rows_chunk : N;
     float* prow = part + (int64_t(tok) * nchunk + chunk) * pstride;
@@ -429,7 +437,7 @@ int backward_small(const QView& q, const uint16_t* x, const uint16_t* dH, int64_
     // one pass over the weight rows: dX partials (dH Wb) and dU partials (dH
     // B); without dX only the rank-r slabs run
     const int nsl = dX ? p.nslab : 0;
-    const dim3 grid(unsigned(M * (nsl + cdiv(r, 64)) * p.nchunk));
+    const dim3 grid(unsigned(cdiv(M * (nsl + cdiv(r, 64)) * p.nchunk, 8) * 8));
     if (q.dq) {
         if (q.gshift >= 0)
             launch_dominant(k_dxv<true, true>, grid, dim3(256), 0, st, q, dH, int(M), nsl, p.rows_chunk, B, r, ps,

@@ -213,18 +213,21 @@ def test_multi_adapter_small(F):
     U.assert_close("h", U.bf16_to_f64(h), href)
 
 
-def test_multi_adapter_large_tiles(F):
-    """The multi-adapter forward on the 256 x 256 register-dequant kernel (48
-    tiles): ragged M, invalid ids, r not a multiple of 8 (the scalar gather)."""
+@pytest.mark.parametrize("M,out,inp,r,n", [
+    (700, 4096, 512, 6, 5),   # split reduction, gather in the partial sum, scalar gather (r % 8)
+    (500, 4096, 256, 16, 9),  # one split: the gather in the kernel's epilogue, 16-byte gather
+])
+def test_multi_adapter_large_tiles(F, M, out, inp, r, n):
+    """The multi-adapter forward on the 256 x 256 register-dequant kernel:
+    ragged M, invalid ids."""
     import torch
 
-    rng = np.random.default_rng(23)
-    out, inp, r, n, M = 4096, 512, 6, 5, 700
+    rng = np.random.default_rng(23 + M)
     w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
     x = _bits(rng, (M, inp), 1.0)
     ab = _bits(rng, (n, r, inp), 0.05)
     bb = _bits(rng, (n, out, r), 0.05)
-    scales = np.array([2.0, 0.5, 1.0, 4.0, 0.25], dtype=np.float32)
+    scales = (2.0 ** rng.integers(-2, 3, size=n)).astype(np.float32)
     ids = rng.integers(-1, n + 1, size=M).astype(np.int32)
     q = F.nf4_quantize(U.f32(w), double_quant=True)
     h = F.qlora_linear_forward_multi(q, U.bf(x), U.bf(ab), U.bf(bb),

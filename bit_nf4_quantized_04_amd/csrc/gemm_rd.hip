@@ -526,6 +526,16 @@ struct DxArgs {
     int spl;               // weight-row steps per split (a multiple of four)
 };
 
+// W tile layout: row-major with a 576-byte row stride, and the 16-byte chunk
+// cc (8 weights) of row `row` stored at position cc ^ wt_swizzle(row, cc).
+// The XOR touches the two low bits of cc only and depends on row mod 4 and
+// bit 4 of cc, so moving 4 or 16 rows or 4 chunks (32 columns) moves the
+// address by a constant (the transposed reads use immediate offsets), while
+// the dequantizing threads' 16-byte stores (a 16-lane group: two rows, eight
+// chunk positions) and the transposed 8-byte reads both hit 64 distinct
+// banks.
+__device__ __forceinline__ int wt_swizzle(int row, int cc) { return (row + 2 * ((cc >> 4) & 1)) & 3; }
+
 // dH tile layout: row m of 4 chunks, chunk c stored at c ^ ((m >> 2) & 3)
 // (sixteen consecutive rows then hit sixteen distinct bank groups)
 __device__ __forceinline__ int dpos(int m, int c) { return m * 4 + (c ^ ((m >> 2) & 3)); }
@@ -570,9 +580,11 @@ struct DxCtx {
         lookup8(dk, p, cw.z, o[2]);
         lookup8(dk, p, cw.w, o[3]);
         const int unit = tid >> 1, half = tid & 1;
-        uint16_t* dst = wt + (unit >> 2) * WTS + 64 * (unit & 3) + 32 * half;
+        const int row = unit >> 2, q = unit & 3;
+        uint16_t* dst = wt + row * WTS + 64 * q + 32 * half;
+        const int f = wt_swizzle(row, 8 * q);  // the same for the thread's four chunks
 #pragma unroll
-        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4_t*>(dst + 8 * d) = o[d];
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4_t*>(dst + 8 * (d ^ f)) = o[d];
     }
     // rank-r rows of the B operand: row c of the extension (c < 2r) is A[c mod r]
     __device__ __forceinline__ void afill(int s, int64_t i0, uint16_t* wt) const {
@@ -584,7 +596,7 @@ struct DxCtx {
             const int c = (s - S1) * DK + row;
             uint4 v = make_uint4(0, 0, 0, 0);
             if (c < 2 * r) v = *reinterpret_cast<const uint4*>(a.A + int64_t(c % r) * a.in + i0 + 8 * ch);
-            *reinterpret_cast<uint4*>(wt + row * WTS + 8 * ch) = v;
+            *reinterpret_cast<uint4*>(wt + row * WTS + 8 * (ch ^ wt_swizzle(row, ch))) = v;
         }
     }
     __device__ __forceinline__ void aread(const uint4* ht, int sl, Frag& f) const {
@@ -700,7 +712,8 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
         const int qq = lane >> 4, i = lane & 15;
         const int col = 64 * w + 16 * (qq & 1) + 4 * (i & 3);
         const int rw = 8 * (qq >> 1) + (i >> 2);
-        c.tro = uint32_t((rw * WTS + col) * 2);
+        const int cc = col >> 3;
+        c.tro = uint32_t((rw * WTS + 8 * (cc ^ wt_swizzle(rw, cc)) + (col & 7)) * 2);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

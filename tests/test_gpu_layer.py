@@ -301,6 +301,28 @@ def test_backward_large_tiles(F, M, out, inp, r):
     U.assert_close("dB", dB.cpu().numpy(), g["dB"])
 
 
+# The register-dequant kernels with absmax scales (no double quant) and with a
+# double-quant group that is not a power of two (the fp32 block scales are
+# decoded by division then).
+@pytest.mark.parametrize("dq,group", [(False, 256), (True, 100)])
+def test_large_tiles_scale_formats(F, dq, group):
+    import torch
+
+    M, out, inp, r = 600, 4096, 2048, 8  # 48 forward tiles; 24 dX tiles, split eight ways
+    w, x, a, b, dh = _case(M + out + group, M, out, inp, r)
+    q = F.nf4_quantize(U.f32(w), double_quant=dq, dq_group=group)
+    h, u = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), 2.0, want_u=True)
+    dX, dA, dB = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), 2.0, u=u)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=dq, dq_group=group), w.shape, dq_group=group)
+    href, _ = O.forward(wb, x, a, b, 2.0)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+    g = O.backward(wb, x, dh, a, b, 2.0)
+    U.assert_close("dX", U.bf16_to_f64(dX), g["dX"])
+    U.assert_close("dA", dA.cpu().numpy(), g["dA"])
+    U.assert_close("dB", dB.cpu().numpy(), g["dB"])
+
+
 def test_70b_workload_full_size_sampled(F):
     """The 70B MLP projection 8192 -> 28672 at full size, in the launch
     configurations the benchmark times: decode (M = 1) forward and backward,

@@ -23,6 +23,9 @@ Sources (cited by page title and section):
   section "Pillar 2: Double Quantization (DQ)" (8-bit scales, groups of 256).
 * Same page, section "The Real-World Bottleneck: Multi-Tenant AI at Scale":
   one resident base with a per-request adapter chosen by client id.
+* "How Fine-Tuning LLMs with LoRA and QLoRA Works" (instagit), FAQ on merging
+  adapters into the base weights (W + (alpha/r) B A), and "QLoRA explained",
+  section "Merging and deploying" (a standalone 16-bit model): ``merge``.
 
 Precision: every step the method states in float32 is computed with NumPy
 float32 elementwise operations (each one IEEE round-to-nearest-even).  All
@@ -327,6 +330,34 @@ def backward64(wb, x, dh, a, b, scale: float):
 def backward(wb, x_bits, dh_bits, a_bits, b_bits, scale: float):
     """The layer backward on bf16 inputs (bit patterns); float64 results."""
     return backward64(wb, _bf(x_bits), _bf(dh_bits), _bf(a_bits), _bf(b_bits), scale)
+
+
+def merge(wb, a_bits, b_bits, scale: float) -> np.ndarray:
+    """The merged 16-bit weight W_new = Wb + (alpha/r) B A as bf16 bit patterns.
+
+    "How Fine-Tuning LLMs with LoRA and QLoRA Works", FAQ on merging adapters
+    back into the base weights (W + (alpha/r) B A); "QLoRA explained",
+    "Merging and deploying" (a standalone 16-bit model).  READING: W is the
+    layer's dequantized bf16 weight Wb; the sum is exact (float64 here) and
+    rounded once to bf16.  Re-quantizing the merged weight is not done.
+    """
+    m = np.asarray(wb, dtype=np.float64) + float(scale) * (_bf(b_bits) @ _bf(a_bits))
+    return _rne_bf16_bits_f64(m)
+
+
+def _rne_bf16_bits_f64(v) -> np.ndarray:
+    """float64 -> bf16 bit patterns, round to nearest even, in one step.
+
+    A float64 value is rounded directly to a multiple of its bf16 quantum
+    (rounding it to float32 first could round twice): with v = m 2^e,
+    0.5 <= |m| < 1, the quantum is 2^(e-8) for normal bf16 values and
+    2^-133 below the normal range.  Finite inputs within the bf16 range.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    quantum = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = (np.round(v / quantum) * quantum).astype(np.float32)  # exact: a bf16 value
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def forward_multi(wb, x_bits, a_bank_bits, b_bank_bits, scales, ids):

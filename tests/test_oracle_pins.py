@@ -346,6 +346,79 @@ def test_merge_identity():
     np.testing.assert_allclose(x @ merged.T, h, rtol=1e-12, atol=1e-14)
 
 
+def _nearest_bf16_bits_exact(q) -> int:
+    """Brute force: the bf16 value nearest to the rational q (ties to an even
+    mantissa), found by comparing exact distances to the bf16 grid points
+    around it."""
+    import struct
+    from fractions import Fraction
+
+    f = float(q)
+    hi16 = struct.unpack("<I", struct.pack("<f", f))[0] >> 16
+    best = None
+    for cand in range(max(hi16 - 2, 0), hi16 + 3):
+        if (cand & 0x7F80) == 0x7F80:
+            continue
+        val = Fraction(struct.unpack("<f", struct.pack("<I", cand << 16))[0])
+        key = (abs(val - q), cand & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return best[1]
+
+
+def test_merge_by_exact_rational_arithmetic():
+    """The merged bf16 weight against exact rational sums, rounded by brute
+    force (mixed signs, so the bit-pattern neighbours cover both sides)."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(21)
+    out, inp, r = 5, 64, 3
+    w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    a = O.rne_bf16_bits((rng.standard_normal((r, inp)) * 0.1).astype(np.float32))
+    b = O.rne_bf16_bits((rng.standard_normal((out, r)) * 0.1).astype(np.float32))
+    s = 0.5
+    got = O.merge(wb, a, b, s)
+    af, bf = O._bf(a), O._bf(b)
+    for o in range(out):
+        for i in range(inp):
+            q = Fraction(wb[o, i]) + Fraction(s) * sum(Fraction(bf[o, j]) * Fraction(af[j, i]) for j in range(r))
+            if q < 0:
+                want = _nearest_bf16_bits_exact(-q) | 0x8000
+            else:
+                want = _nearest_bf16_bits_exact(q)
+            assert int(got[o, i]) == want, (o, i, hex(int(got[o, i])), hex(want))
+
+
+def test_merge_without_adapter_is_the_dequantized_weight():
+    rng = np.random.default_rng(22)
+    w = (rng.standard_normal((8, 128)) * 0.02).astype(np.float32)
+    qt = O.quantize(w, double_quant=True)
+    wb = O.compute_weight(qt, w.shape)
+    a = O.rne_bf16_bits(rng.standard_normal((4, 128)).astype(np.float32))
+    b = O.rne_bf16_bits(rng.standard_normal((8, 4)).astype(np.float32))
+    want = O.dequantize_bf16_bits(qt, w.shape)
+    np.testing.assert_array_equal(O.merge(wb, a, np.zeros_like(b), 2.0), want)
+    np.testing.assert_array_equal(O.merge(wb, a, b, 0.0), want)
+
+
+def test_merged_weight_reproduces_the_forward():
+    """x Wm^T with the merged bf16 weight equals the unmerged forward up to the
+    rounding of the merged weight: each merged entry is within half a bf16
+    ulp (2^-8 of its magnitude) of Wb + s B A, so the output error is at most
+    |x| (2^-8 |Wb + s B A|)^T."""
+    wb, x, a, b = _small_layer(6, M=4)
+    s = 2.0
+    ab, bb = O.rne_bf16_bits(a.astype(np.float32)), O.rne_bf16_bits(b.astype(np.float32))
+    wm = O.bf16_bits_to_f32(O.merge(wb, ab, bb, s)).astype(np.float64)
+    exact = wb + s * (O._bf(bb) @ O._bf(ab))
+    assert np.all(np.abs(wm - exact) <= 2.0 ** -8 * np.abs(exact))
+    h, _ = O.forward64(wb, x, a, b, s)
+    bound = np.abs(x) @ (2.0 ** -8 * np.abs(exact)).T
+    assert np.all(np.abs(x @ wm.T - h) <= bound + 1e-12)
+    assert np.abs(x @ wm.T - h).max() > 0  # the rounding is visible, the bound is not vacuous
+
+
 def test_single_token_is_a_matrix_vector_product():
     wb, x, a, b = _small_layer(3, M=1)
     h, u = O.forward64(wb, x, a, b, 2.0)

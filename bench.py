@@ -255,6 +255,11 @@ def main():
         _, u = F.qlora_linear_forward(q7, x7, A7, B7, s7, want_u=True, ws=wsf7, out=h7)
         F.qlora_linear_backward(q7, x7, dH7, A7, B7, s7, u=u, ws=wsb7)
 
+    wm = torch.empty((out, inp), dtype=torch.bfloat16, device=dev)
+
+    def merge_step(i):
+        F.qlora_merge(qs[i % len(qs)], A, B, scale, out=wm)
+
     def train_step(i):
         _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
         F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
@@ -297,6 +302,8 @@ def main():
     t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))
     t_mu, _ = timed(multi_step, K, W)
     t_7b, _ = timed(train7_step, K, W)
+    t_mg, _ = timed(merge_step, K, W)
+    mg_bytes = out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * r * (inp + out) + 2 * out * inp
     f7 = sum(train_flops(sh7["out"], sh7["inp"], M7, sh7["r"]))
     mu_flops = 2 * Mm * shm["out"] * shm["inp"] + 2 * Mm * shm["r"] * (shm["inp"] + shm["out"])
     # dominant kernels of the training pass: forward product and dX product
@@ -364,6 +371,11 @@ def main():
                 sh7["inp"], sh7["out"], sh7["r"], M7),
             "ms": round(t_7b, 4), "TFLOPs": round(f7 / (t_7b * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(f7 / (t_7b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+        "merge": {
+            "workload": "adapter merged into the bf16 base weight, %d x %d, r=%d" % (out, inp, r),
+            "ms": round(t_mg, 4), "GBps": round(mg_bytes / (t_mg * 1e-3) / 1e9, 2),
+            "frac_hbm_peak": round(mg_bytes / (t_mg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "multi_adapter": {
             "workload": "%d adapters r=%d on %d->%d NF4 base, %d tokens" % (

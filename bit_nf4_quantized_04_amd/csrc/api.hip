@@ -213,4 +213,15 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
                               static_cast<hipStream_t>(stream));
 }
 
+int qlora_merge(const nf4_tensor* W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                uint16_t* W_out, void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (r < 1 || r > 256 || !isfinite(scale)) return NF4_EINVAL;
+    if (v.rows == 0 || v.cols == 0) return NF4_EINVAL;
+    if (bad_ptr(A) || bad_ptr(B) || bad_ptr(W_out)) return NF4_EINVAL;
+    return nf4::merge_adapter(v, A, B, r, scale, W_out, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -71,6 +71,9 @@ size_t rd_scales_bytes(int64_t rows, int64_t cols);
 bool use_rd(const QView& q, int64_t M, int r, int KL);
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
                const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
+// The adapter merged into the bf16 base weight (merge.hip).
+int merge_adapter(const QView& q, const uint16_t* A, const uint16_t* B, int r, float scale, uint16_t* W_out,
+                  hipStream_t st);
 // The backward for a few tokens (M <= kBwdSmallMaxM, bwd_small.hip): fp32
 // rank-r kernels and the transposed dequant-GEMV for dX, with
 // bwd_small_ws_bytes() of workspace.

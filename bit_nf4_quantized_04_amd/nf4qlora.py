@@ -64,6 +64,7 @@ _SIGS = {
                                              C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "qlora_linear_backward": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, _I64, _P, _P, C.c_int32,
                                         C.c_float, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "qlora_merge": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, C.c_int32, C.c_float, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -293,3 +294,16 @@ def qlora_linear_backward(w: NF4Weight, x, dH, A, B, scale: float, u=None, want_
                                       float(scale), _ptr(u), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                       ws.numel(), _stream(stream)), "qlora_linear_backward")
     return dX, dA, dB
+
+
+def qlora_merge(w: NF4Weight, A, B, scale: float, out=None, stream=None):
+    """The merged bf16 weight [rows, cols] = Wb + scale * B A."""
+    import torch
+
+    r = A.shape[0]
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=A.device)
+    t = w.c_struct()
+    _check(_lib.qlora_merge(C.byref(t), _ptr(A), _ptr(B), r, float(scale), _ptr(out), _stream(stream)),
+           "qlora_merge")
+    return out

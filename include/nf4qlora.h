@@ -19,7 +19,10 @@
  *       quantization" (scales divided by their absmax, times 127, rounded to
  *       int8), "The LoRA adapter path" (layout x W^T, (x A^T) B^T * scale; the
  *       dequantized weight is cast to bfloat16 and receives no gradient),
- *       "Common misconceptions" (the 16 NF4 levels).
+ *       "Common misconceptions" (the 16 NF4 levels), "Merging and deploying"
+ *       (the adapter fused into a standalone 16-bit model).
+ *  [P4] "How Fine-Tuning LLMs with LoRA and QLoRA Works", FAQ on merging
+ *       adapters into the base weights (W_new = W + (alpha/r) B A).
  *  [P5] "Parameter-Efficient Fine-Tuning: From LoRA to QLoRA", "Pillar 1"
  *       (level table, worked example, two codes per byte, first element in
  *       the high nibble), "Pillar 2" (8-bit scales in groups of 256), "The
@@ -167,6 +170,18 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
                           const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                           const float* u, uint16_t* dX, float* dA, float* dB,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* Merge the adapter into the base weight for a standalone 16-bit model [P3
+ * "Merging and deploying"; P4 FAQ on merging, W_new = W + (alpha/r) B A]:
+ *   W_out[o][i] = bf16( Wb[o][i] + scale * sum_j B[o][j] A[j][i] )
+ * Wb is the layer's dequantized bf16 weight.  W: rows = out, cols = in
+ * (cols % 64 == 0); A bf16 [r, in]; B bf16 [out, r]; W_out bf16 [out, in],
+ * overwritten, not aliasing the inputs.  1 <= r <= 256.  The rank-r product
+ * uses bf16 operands with fp32 accumulation; Wb + scale * (B A) is formed in
+ * fp32 and rounded to bf16 (nearest even).  Needs no workspace.  The merged
+ * weight is not re-quantized. */
+int qlora_merge(const nf4_tensor* W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                uint16_t* W_out, void* stream);
 
 /* Profiling hook (for benchmarks; not thread-safe).  When both are non-NULL,
  * `start` and `stop` (hipEvent_t handles owned by the caller) are recorded on

@@ -323,6 +323,35 @@ def test_large_tiles_scale_formats(F, dq, group):
     U.assert_close("dB", dB.cpu().numpy(), g["dB"])
 
 
+# The adapter merged into the bf16 base weight: ragged rows and column tiles,
+# r not a multiple of 8, r over one 64-row chunk, absmax scales, a
+# non-power-of-two double-quant group.
+@pytest.mark.parametrize("out,inp,r,dq,group", [
+    (200, 320, 8, True, 256),
+    (130, 192, 3, True, 256),
+    (1000, 2048, 64, True, 256),
+    (96, 1088, 70, False, 256),
+    (250, 640, 12, True, 100),
+])
+def test_merge(F, out, inp, r, dq, group):
+    import torch
+
+    w, _, a, b, _ = _case(out * 3 + r, 1, out, inp, r)
+    q = F.nf4_quantize(U.f32(w), double_quant=dq, dq_group=group)
+    s = 2.0
+    wm = F.qlora_merge(q, U.bf(a), U.bf(b), s)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=dq, dq_group=group), w.shape, dq_group=group)
+    ref = O.bf16_bits_to_f32(O.merge(wb, a, b, s)).astype(np.float64)
+    U.assert_close("merged", U.bf16_to_f64(wm), ref)
+    # without the adapter the merge is the bit-exact bf16 dequantization
+    wz = F.qlora_merge(q, U.bf(a), U.bf(np.zeros_like(b)), s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(wz.view(torch.int16).cpu().numpy().view(np.uint16),
+                                  O.rne_bf16_bits(O.dequantize(O.quantize(w, double_quant=dq, dq_group=group),
+                                                               w.shape, dq_group=group)))
+
+
 def test_70b_workload_full_size_sampled(F):
     """The 70B MLP projection 8192 -> 28672 at full size, in the launch
     configurations the benchmark times: decode (M = 1) forward and backward,

@@ -26,6 +26,10 @@ Sources (cited by page title and section):
 * "How Fine-Tuning LLMs with LoRA and QLoRA Works" (instagit), FAQ on merging
   adapters into the base weights (W + (alpha/r) B A), and "QLoRA explained",
   section "Merging and deploying" (a standalone 16-bit model): ``merge``.
+* "QLoRA Specification for EMEP Fine-Tuning" ("GPU Orchestration": adapters
+  and optimizer state in full precision), "QLoRA explained" ("Paged
+  optimizers": the Adam moments of the LoRA parameters paged to host memory):
+  ``adamw_step``.
 
 Precision: every step the method states in float32 is computed with NumPy
 float32 elementwise operations (each one IEEE round-to-nearest-even).  All
@@ -384,6 +388,37 @@ def forward_multi(wb, x_bits, a_bank_bits, b_bank_bits, scales, ids):
 # Storage accounting ("From LoRA to QLoRA", worked example memory footprint and
 # Pillar 2 bits-per-parameter).
 # ---------------------------------------------------------------------------
+def adamw_step(p, g, m, v, step: int, lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float):
+    """One AdamW step on the adapter parameters, in float64.  Returns (p, m, v).
+
+    The pages train only the adapters with AdamW and keep the adapters and
+    their optimizer state (the Adam moments) in full precision, the moments
+    possibly paged to host memory ("QLoRA Specification for EMEP
+    Fine-Tuning", "GPU Orchestration"; "QLoRA explained", "Paged
+    optimizers"; "QLoRA Finetuner", the AdamW example).  READING: the update
+    rule is not printed; it is the published AdamW (decoupled weight decay,
+    bias-corrected moments), step counted from 1:
+        p <- p - lr*wd*p
+        m <- beta1*m + (1-beta1)*g,   v <- beta2*v + (1-beta2)*g^2
+        p <- p - lr * (m / (1-beta1^t)) / (sqrt(v / (1-beta2^t)) + eps)
+    The 8-bit variant of the states is not taken (its encoding is not on the
+    pages).
+    """
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    t = int(step)
+    p = p - lr * weight_decay * p
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** t)
+    vhat = v / (1.0 - beta2 ** t)
+    p = p - lr * mhat / (np.sqrt(vhat) + eps)
+    return p, m, v
+
+
 def storage_bytes(numel: int, double_quant: bool, block_size: int = BLOCK_SIZE,
                   dq_group: int = DQ_GROUP):
     """(code bytes, first-level scale bytes stored, second-level bytes)."""

@@ -484,6 +484,48 @@ def test_multi_adapter_reduces_to_single_adapter():
     np.testing.assert_allclose(h[bad], O._bf(xb[bad]) @ wb.T, rtol=1e-12, atol=1e-14)
 
 
+# ------------------------------------------------------------- AdamW step
+def test_adamw_matches_torch():
+    """The library routine as the pin: torch.optim.AdamW (float64, CPU) over
+    several steps with weight decay."""
+    import torch
+
+    rng = np.random.default_rng(30)
+    n = 257
+    p0 = rng.standard_normal(n)
+    grads = [rng.standard_normal(n) * 1e-2 for _ in range(5)]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    tp = torch.nn.Parameter(torch.tensor(p0.copy(), dtype=torch.float64))
+    opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    p, m, v = p0.copy(), np.zeros(n), np.zeros(n)
+    for t, g in enumerate(grads, start=1):
+        tp.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        p, m, v = O.adamw_step(p, g, m, v, t, **hp)
+        np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-13, atol=1e-15)
+    st = opt.state[tp]
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-13)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-13)
+
+
+def test_adamw_closed_forms():
+    """With a constant gradient the bias-corrected moments are exactly g and
+    g^2 at every step, so each step moves p by lr*g/(|g| + eps) (plus the
+    decay); the first step from zero moments is the same closed form."""
+    g = np.array([0.5, -2.0, 1e-3, 0.0])
+    lr, eps, wd = 1e-2, 1e-8, 0.1
+    p = np.array([1.0, -1.0, 0.25, 3.0])
+    m = v = np.zeros(4)
+    want = p.copy()
+    for t in range(1, 6):
+        p, m, v = O.adamw_step(p, g, m, v, t, lr, 0.9, 0.999, eps, wd)
+        want = want * (1 - lr * wd) - lr * g / (np.abs(g) + eps)
+        np.testing.assert_allclose(p, want, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(m, g * (1 - 0.9 ** 5), rtol=1e-12)
+    np.testing.assert_allclose(v, g * g * (1 - 0.999 ** 5), rtol=1e-12)
+
+
 def test_tolerance_helper():
     ref = np.array([1.0, -2.0, 0.0, 3.0])
     ok, worst = O.tolerance_ok(ref * (1 + 5e-3), ref)

@@ -260,6 +260,16 @@ def main():
     def merge_step(i):
         F.qlora_merge(qs[i % len(qs)], A, B, scale, out=wm)
 
+    # one AdamW step on the layer's adapters (A and B together), fp32 state in HBM
+    n_ad = r * (inp + out)
+    pa = torch.randn(n_ad, device=dev)
+    ga = torch.randn(n_ad, device=dev) * 1e-3
+    ma, va = torch.zeros(n_ad, device=dev), torch.zeros(n_ad, device=dev)
+    pab = torch.empty(n_ad, dtype=torch.bfloat16, device=dev)
+
+    def adamw_step(i):
+        F.qlora_adamw_step(pa, ga, ma, va, i + 1, 1e-4, 0.9, 0.999, 1e-8, 0.01, p_bf16=pab)
+
     def train_step(i):
         _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ft, out=ht)
         F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_bt)
@@ -303,6 +313,8 @@ def main():
     t_mu, _ = timed(multi_step, K, W)
     t_7b, _ = timed(train7_step, K, W)
     t_mg, _ = timed(merge_step, K, W)
+    t_ad, _ = timed(adamw_step, K, W)
+    ad_bytes = 30 * n_ad  # p, m, v read and written, g read, the bf16 copy written
     mg_bytes = out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * r * (inp + out) + 2 * out * inp
     f7 = sum(train_flops(sh7["out"], sh7["inp"], M7, sh7["r"]))
     mu_flops = 2 * Mm * shm["out"] * shm["inp"] + 2 * Mm * shm["r"] * (shm["inp"] + shm["out"])
@@ -376,6 +388,11 @@ def main():
             "workload": "adapter merged into the bf16 base weight, %d x %d, r=%d" % (out, inp, r),
             "ms": round(t_mg, 4), "GBps": round(mg_bytes / (t_mg * 1e-3) / 1e9, 2),
             "frac_hbm_peak": round(mg_bytes / (t_mg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "adamw_step": {
+            "workload": "AdamW on the layer's adapters, %d fp32 parameters" % n_ad,
+            "ms": round(t_ad, 4), "GBps": round(ad_bytes / (t_ad * 1e-3) / 1e9, 2),
+            "frac_hbm_peak": round(ad_bytes / (t_ad * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "multi_adapter": {
             "workload": "%d adapters r=%d on %d->%d NF4 base, %d tokens" % (

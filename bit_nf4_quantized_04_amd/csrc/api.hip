@@ -224,4 +224,17 @@ int qlora_merge(const nf4_tensor* W, const uint16_t* A, const uint16_t* B, int32
     return nf4::merge_adapter(v, A, B, r, scale, W_out, static_cast<hipStream_t>(stream));
 }
 
+int qlora_adamw_step(float* p, const float* g, float* m, float* v, uint16_t* p_bf16, int64_t n,
+                     int32_t step, float lr, float beta1, float beta2, float eps,
+                     float weight_decay, void* stream) {
+    if (n < 0 || step < 1) return NF4_EINVAL;
+    if (!isfinite(lr) || !isfinite(beta1) || !isfinite(beta2) || !isfinite(eps) || !isfinite(weight_decay))
+        return NF4_EINVAL;
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f)) return NF4_EINVAL;
+    if (n == 0) return NF4_OK;
+    if (bad_ptr(p) || bad_ptr(g) || bad_ptr(m) || bad_ptr(v) || (p_bf16 && !al16(p_bf16))) return NF4_EINVAL;
+    return nf4::adamw_step(p, g, m, v, p_bf16, n, step, lr, beta1, beta2, eps, weight_decay,
+                           static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

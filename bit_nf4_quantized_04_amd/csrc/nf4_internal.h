@@ -71,6 +71,9 @@ size_t rd_scales_bytes(int64_t rows, int64_t cols);
 bool use_rd(const QView& q, int64_t M, int r, int KL);
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
                const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
+// One AdamW step on adapter parameters (adamw.hip).
+int adamw_step(float* p, const float* g, float* m, float* v, uint16_t* pb, int64_t n, int step, float lr,
+               float beta1, float beta2, float eps, float weight_decay, hipStream_t st);
 // The adapter merged into the bf16 base weight (merge.hip).
 int merge_adapter(const QView& q, const uint16_t* A, const uint16_t* B, int r, float scale, uint16_t* W_out,
                   hipStream_t st);

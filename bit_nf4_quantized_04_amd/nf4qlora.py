@@ -65,6 +65,8 @@ _SIGS = {
     "qlora_linear_backward": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, _I64, _P, _P, C.c_int32,
                                         C.c_float, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "qlora_merge": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, C.c_int32, C.c_float, _P, _P]),
+    "qlora_adamw_step": (C.c_int, [_P, _P, _P, _P, _P, _I64, C.c_int32, C.c_float, C.c_float, C.c_float,
+                                   C.c_float, C.c_float, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -307,3 +309,13 @@ def qlora_merge(w: NF4Weight, A, B, scale: float, out=None, stream=None):
     _check(_lib.qlora_merge(C.byref(t), _ptr(A), _ptr(B), r, float(scale), _ptr(out), _stream(stream)),
            "qlora_merge")
     return out
+
+
+def qlora_adamw_step(p, g, m, v, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.0, p_bf16=None, stream=None):
+    """One AdamW step in place on fp32 p, m, v (m, v may be pinned host
+    tensors); g fp32; p_bf16 (optional) receives bf16(p)."""
+    n = p.numel()
+    _check(_lib.qlora_adamw_step(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(p_bf16), n, int(step), float(lr),
+                                 float(beta1), float(beta2), float(eps), float(weight_decay), _stream(stream)),
+           "qlora_adamw_step")

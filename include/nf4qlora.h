@@ -14,12 +14,14 @@
  *       Quantization" (64-element blocks, absmax scale, division by the scale,
  *       nearest of 16 levels, dequantization as scale times level).
  *  [P2] "QLoRA Specification for EMEP Fine-Tuning", "Hyperparameters"
- *       (quant type nf4, double quant on, compute dtype bfloat16).
+ *       (quant type nf4, double quant on, compute dtype bfloat16), "GPU
+ *       Orchestration" (adapters and optimizer state in full precision).
  *  [P3] "QLoRA explained: fine-tuning in 4-bit precision", "Double
  *       quantization" (scales divided by their absmax, times 127, rounded to
  *       int8), "The LoRA adapter path" (layout x W^T, (x A^T) B^T * scale; the
  *       dequantized weight is cast to bfloat16 and receives no gradient),
- *       "Common misconceptions" (the 16 NF4 levels), "Merging and deploying"
+ *       "Common misconceptions" (the 16 NF4 levels), "Paged optimizers" (the
+ *       Adam moments of the adapters paged to host memory), "Merging and deploying"
  *       (the adapter fused into a standalone 16-bit model).
  *  [P4] "How Fine-Tuning LLMs with LoRA and QLoRA Works", FAQ on merging
  *       adapters into the base weights (W_new = W + (alpha/r) B A).
@@ -182,6 +184,21 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
  * weight is not re-quantized. */
 int qlora_merge(const nf4_tensor* W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                 uint16_t* W_out, void* stream);
+
+/* One AdamW step on adapter parameters (only the adapters train; they and
+ * their optimizer state stay in full precision, the state possibly paged to
+ * host memory) [P2 "GPU Orchestration"; P3 "Paged optimizers"].  The rule is
+ * the published AdamW, t = step >= 1:
+ *   p <- p - lr*wd*p;  m <- b1*m + (1-b1)*g;  v <- b2*v + (1-b2)*g^2;
+ *   p <- p - lr * (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps)
+ * p, m, v fp32 [n], updated in place; g fp32 [n] (e.g. dA or dB of the
+ * backward); p_bf16 [n] (may be NULL) receives bf16(p) for the next layer
+ * call.  m and v may be device memory or pinned host memory from
+ * hipHostMalloc (paged optimizer state): the kernel updates them in place.
+ * fp32 arithmetic.  n == 0 is a no-op. */
+int qlora_adamw_step(float* p, const float* g, float* m, float* v, uint16_t* p_bf16, int64_t n,
+                     int32_t step, float lr, float beta1, float beta2, float eps,
+                     float weight_decay, void* stream);
 
 /* Profiling hook (for benchmarks; not thread-safe).  When both are non-NULL,
  * `start` and `stop` (hipEvent_t handles owned by the caller) are recorded on

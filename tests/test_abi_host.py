@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(F):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = C.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -139,3 +139,23 @@ def test_workspace_sizes_are_monotone(F):
     assert F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 16, 0) == 0
     assert F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD, 4096, 4096, 16, 16) > a
     assert F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 16, 999) == 0
+
+
+def test_adamw_and_merge_argument_errors(F):
+    lib = F._lib
+    ad = lambda p, n, step, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8: lib.qlora_adamw_step(
+        p, FAKE, FAKE, FAKE, None, n, step, lr, b1, b2, eps, 0.0, None)
+    assert ad(FAKE, -1, 1) == F.NF4_EINVAL
+    assert ad(FAKE, 10, 0) == F.NF4_EINVAL  # steps count from 1
+    assert ad(FAKE, 10, 1, b1=1.0) == F.NF4_EINVAL
+    assert ad(FAKE, 10, 1, eps=0.0) == F.NF4_EINVAL
+    assert ad(FAKE, 10, 1, lr=float("inf")) == F.NF4_EINVAL
+    assert ad(None, 10, 1) == F.NF4_EINVAL
+    assert ad(None, 0, 1) == F.NF4_OK  # n == 0: no-op, nothing touched
+    t = _tensor(F)
+    mg = lambda tt, r, out: lib.qlora_merge(C.byref(tt), FAKE, FAKE, r, 2.0, out, None)
+    assert mg(t, 0, FAKE) == F.NF4_EINVAL
+    assert mg(t, 257, FAKE) == F.NF4_EINVAL
+    assert mg(t, 4, None) == F.NF4_EINVAL
+    assert mg(_tensor(F, codes=None), 4, FAKE) == F.NF4_EINVAL
+

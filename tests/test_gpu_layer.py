@@ -3,6 +3,8 @@ oracle, elementwise within |err| <= 1e-2|ref| + 1e-3 rms(ref)."""
 
 import sys
 
+import ctypes as C
+
 import numpy as np
 import pytest
 
@@ -350,6 +352,75 @@ def test_merge(F, out, inp, r, dq, group):
     np.testing.assert_array_equal(wz.view(torch.int16).cpu().numpy().view(np.uint16),
                                   O.rne_bf16_bits(O.dequantize(O.quantize(w, double_quant=dq, dq_group=group),
                                                                w.shape, dq_group=group)))
+
+
+class _DevView:
+    """A device address standing for a pinned host tensor (for the binding)."""
+
+    def __init__(self, ptr, t):
+        self.ptr, self.t = ptr, t
+
+    def data_ptr(self):
+        return self.ptr
+
+    def numel(self):
+        return self.t.numel()
+
+
+@pytest.mark.parametrize("host_state", [False, True])
+def test_adamw_steps(F, host_state):
+    """Five AdamW steps on a ragged parameter vector against the oracle; the
+    moments in device memory or in pinned host memory (paged optimizer
+    state); the bf16 copy of the parameters."""
+    import torch
+
+    rng = np.random.default_rng(31 + host_state)
+    n = 12345
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    hp32 = {k: float(np.float32(x)) for k, x in hp.items()}
+    p0 = rng.standard_normal(n).astype(np.float32)
+    p = torch.from_numpy(p0.copy()).to(U.dev())
+    if host_state:
+        m = torch.zeros(n, dtype=torch.float32).pin_memory()
+        v = torch.zeros(n, dtype=torch.float32).pin_memory()
+        # the kernel gets the device address of the pinned pages
+        rt = F.HipEvents().rt
+        rt.hipHostGetDevicePointer.argtypes = [C.POINTER(C.c_void_p), C.c_void_p, C.c_uint]
+        dev_ptrs = []
+        for t in (m, v):
+            dp = C.c_void_p()
+            if rt.hipHostGetDevicePointer(C.byref(dp), C.c_void_p(t.data_ptr()), 0) != 0 or not dp.value:
+                pytest.skip("pinned host memory is not mapped for the device")
+            dev_ptrs.append(_DevView(dp.value, t))
+        mk, vk = dev_ptrs
+    else:
+        m = torch.zeros(n, dtype=torch.float32, device=U.dev())
+        v = torch.zeros(n, dtype=torch.float32, device=U.dev())
+        mk, vk = m, v
+    pb = torch.empty(n, dtype=torch.bfloat16, device=U.dev())
+    rp, rm, rv = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in range(1, 6):
+        g = (rng.standard_normal(n) * 10.0 ** rng.integers(-4, 1)).astype(np.float32)
+        F.qlora_adamw_step(p, torch.from_numpy(g).to(U.dev()), mk, vk, t, p_bf16=pb, **hp)
+        torch.cuda.synchronize()
+        # the oracle steps from the GPU's fp32 state, so errors do not compound
+        # (with the hyperparameters as the call receives them: float32)
+        rp, rm, rv = O.adamw_step(p_prev if t > 1 else rp, g, m_prev if t > 1 else rm,
+                                  v_prev if t > 1 else rv, t, **hp32)
+        gp, gm, gv = p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()
+        # bounds from the fp32 arithmetic: a few roundings (2^-24 relative
+        # each) of every term's magnitude
+        pp = p_prev if t > 1 else p0.astype(np.float64)
+        mp = m_prev if t > 1 else np.zeros(n)
+        vp = v_prev if t > 1 else np.zeros(n)
+        b1, b2, lr = hp32["beta1"], hp32["beta2"], hp32["lr"]
+        u = 2.0 ** -24
+        step_mag = lr * np.abs(rm / (1 - b1 ** t)) / (np.sqrt(rv / (1 - b2 ** t)) + hp32["eps"])
+        assert np.all(np.abs(gm - rm) <= 4 * u * (b1 * np.abs(mp) + (1 - b1) * np.abs(g)))
+        assert np.all(np.abs(gv - rv) <= 4 * u * (b2 * vp + (1 - b2) * g.astype(np.float64) ** 2))
+        assert np.all(np.abs(gp - rp) <= 4 * u * np.abs(pp) + 16 * u * step_mag)
+        np.testing.assert_array_equal(pb.view(torch.int16).cpu().numpy().view(np.uint16), O.rne_bf16_bits(gp))
+        p_prev, m_prev, v_prev = gp.astype(np.float64), gm.astype(np.float64), gv.astype(np.float64)
 
 
 def test_70b_workload_full_size_sampled(F):

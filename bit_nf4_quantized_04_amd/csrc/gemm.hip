@@ -397,7 +397,7 @@ inline int ext_cols(int r) { return int(nf4::cdiv(2 * r, 64) * 64); }
 
 struct FwdPlan {
     int Zu;  // split-K of the down-projection
-    size_t off_u, off_ext, off_part, off_sc, total;
+    size_t off_u, off_ext, off_part, off_sc, off_tail, total;
 };
 
 // Workspace of the GEMM-path down-projection: u, its bf16 hi/lo extension,
@@ -424,9 +424,11 @@ FwdPlan plan_forward(int64_t rows, int64_t cols, int64_t M, int r) {
         return p;
     }
     FwdPlan p = plan_down(rows, cols, M, r);
-    if (nf4::use_rd_grid(M, rows) || nf4::use_big_gemm(M, rows)) {  // fp32 block scales of the register-dequant GEMM
-        p.off_sc = p.total;
-        p.total += nf4::rd_scales_bytes(rows, cols);
+    if (nf4::use_rd_grid(M, rows) || nf4::use_big_gemm(M, rows)) {  // register-dequant GEMM: fp32 block
+        p.off_sc = p.total;                                           // scales, tail-split partials
+        p.total = nf4::align256(p.total + nf4::rd_scales_bytes(rows, cols));
+        p.off_tail = p.total;
+        p.total += nf4::fwd_tail_bytes(M, rows, cols);
     }
     return p;
 }
@@ -544,7 +546,8 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     LdNF4Rows lw{q};
     if (r == 0) {
         if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0))
-            return forward_rd(q, x, M, nullptr, 0, nullptr, 0, h, reinterpret_cast<float*>(w + fp.off_sc), st);
+            return forward_rd(q, x, M, nullptr, 0, nullptr, 0, h, reinterpret_cast<float*>(w + fp.off_sc),
+                              reinterpret_cast<float*>(w + fp.off_tail), st);
         if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, nullptr, 0, nullptr, 0, h, st);
         return gemm(st, M, q.rows, lx, lw, q.cols, LdNone{}, LdNone{}, 0, OutBF16{h, q.rows}, 1, true);
     }
@@ -553,7 +556,8 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext);
     if (rc) return rc;
     if (use_rd_grid(M, q.rows) && use_rd(q, M, r, ext_cols(r)))
-        return forward_rd(q, x, M, ext, ext_cols(r), B, r, h, reinterpret_cast<float*>(w + fp.off_sc), st);
+        return forward_rd(q, x, M, ext, ext_cols(r), B, r, h, reinterpret_cast<float*>(w + fp.off_sc),
+                          reinterpret_cast<float*>(w + fp.off_tail), st);
     if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};

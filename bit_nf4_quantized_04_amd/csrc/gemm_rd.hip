@@ -137,6 +137,11 @@ struct FwdArgs {
     // taking weight steps [z*spl, z*spl + spl) (and the rank-r steps if last)
     float* part;
     int spl;
+    // tail split (gridDim.y == 1, ztail > 1): the first tfull tiles take the
+    // whole reduction; each later tile is split ztail ways (spl_tail steps
+    // each) into tile-local fp32 partials [ztail][tile - tfull][RM][RN] at part
+    int64_t tfull;
+    int ztail, spl_tail;
 };
 
 // The gathered rank-r term of one output of the multi-adapter forward, fp32
@@ -315,6 +320,21 @@ __device__ __forceinline__ void nf4_step(const FwdCtx& c, int t, const uint4* cu
     interleave();
 }
 
+// XCD-aware tile order (workgroups are dealt round-robin to the 8 XCDs): a
+// run of consecutive `lin` goes to one XCD, and consecutive `lin` walk 4
+// token tiles at a time across the output tiles, so neighbouring tiles on
+// one XCD share x rows or weight rows in its L2.
+__device__ __forceinline__ int64_t xcd_lin(int64_t bid, int64_t T) {
+    return (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+}
+__device__ __forceinline__ void tile_of(int64_t lin, int64_t nMt, int64_t nNt, int64_t& tm, int64_t& tn) {
+    const int64_t G = 4, gsz = G * nNt;
+    const int64_t grp = lin / gsz, first = grp * G;
+    const int64_t gm = (nMt - first < G) ? (nMt - first) : G;
+    tm = first + (lin % gsz) % gm;
+    tn = (lin % gsz) / gm;
+}
+
 template <bool MULTI>
 __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     // the ring of x tiles and the two weight slots: separate arrays, so that
@@ -325,16 +345,30 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t N = a.N, K = a.K, M = a.M;
 
-    // XCD-aware tile order (workgroups are dealt round-robin to the 8 XCDs):
-    // each XCD walks a contiguous run of tiles, 4 token tiles at a time, so
-    // neighbouring tiles on one XCD share x rows or weight rows in its L2.
+    // the workgroup's tile and its share of the reduction
     const int64_t nMt = (M + RM - 1) / RM, nNt = (N + RN - 1) / RN, T = nMt * nNt;
     const int64_t bid = blockIdx.x;
-    const int64_t lin = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
-    const int64_t G = 4, gsz = G * nNt;
-    const int64_t grp = lin / gsz, first = grp * G;
-    const int64_t gm = (nMt - first < G) ? (nMt - first) : G;
-    const int64_t tm = first + (lin % gsz) % gm, tn = (lin % gsz) / gm;
+    int64_t lin, tt = 0;
+    int z, nz, spl;
+    if (gridDim.y > 1) {  // every tile split
+        lin = xcd_lin(bid, T);
+        z = int(blockIdx.y);
+        nz = int(gridDim.y);
+        spl = a.spl;
+    } else if (a.ztail <= 1 || bid < a.tfull) {  // whole reduction
+        lin = xcd_lin(bid, a.ztail <= 1 ? T : a.tfull);
+        z = 0;
+        nz = 1;
+        spl = int(K / RKS);
+    } else {  // a tail tile, split
+        tt = (bid - a.tfull) / a.ztail;
+        lin = a.tfull + tt;
+        z = int((bid - a.tfull) % a.ztail);
+        nz = a.ztail;
+        spl = a.spl_tail;
+    }
+    int64_t tm, tn;
+    tile_of(lin, nMt, nNt, tm, tn);
     const int64_t m0 = tm * RM, n0 = tn * RN;
 
     FwdCtx c{a};
@@ -374,10 +408,9 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int S1 = c.S1, S = c.S;
-    const int z = int(blockIdx.y);
-    const bool last = z == int(gridDim.y) - 1;
-    const int sb = z * a.spl;
-    const int se = (sb + a.spl < S1) ? sb + a.spl : S1;
+    const bool last = z == nz - 1;
+    const int sb = z * spl;
+    const int se = (sb + spl < S1) ? sb + spl : S1;
     // ---- prologue, in the issue order of the steady state: x tile s, then
     // weights s, for s = sb, sb+1, sb+2 (weights sb+2 go into slot 0 once
     // weights sb are in registers)
@@ -431,7 +464,17 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 
     // D layout of the 32x32 MFMA: lane holds column lane%32 and rows
     // 8*(v/4) + 4*(lane/32) + v%4, v = 0..15.
-    if (gridDim.y > 1) {  // one split of the reduction: fp32 partials
+    if (nz > 1 && gridDim.y == 1) {  // a split tail tile: tile-local fp32 partials
+        float* pz = a.part + (int64_t(z) * (T - a.tfull) + tt) * (RM * RN);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ln = 64 * w + 32 * j + c.nl;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) pz[(32 * i + 8 * (v >> 2) + 4 * c.hh + (v & 3)) * RN + ln] = acc[i][j][v];
+        }
+    } else if (gridDim.y > 1) {  // one split of the reduction: fp32 partials
         float* pz = a.part + int64_t(z) * M * N;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -808,6 +851,33 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
     }
 }
 
+// h of the split tail tiles: the tile-local partials summed in split order.
+// One workgroup per 4 rows of a tail tile, four consecutive columns per
+// thread (16-byte partial reads).
+__global__ __launch_bounds__(256) void k_tail_sum(FwdArgs a) {
+    const int64_t M = a.M, N = a.N;
+    const int64_t nMt = (M + RM - 1) / RM, nNt = (N + RN - 1) / RN, T = nMt * nNt;
+    const int64_t trem = T - a.tfull;
+    const int64_t tt = blockIdx.x / (RM / 4);
+    const int lr = int(blockIdx.x % (RM / 4)) * 4 + (threadIdx.x >> 6), lc = 4 * (threadIdx.x & 63);
+    int64_t tm, tn;
+    tile_of(a.tfull + tt, nMt, nNt, tm, tn);
+    const int64_t m = tm * RM + lr, col = tn * RN + lc;
+    if (m >= M || col >= N) return;
+    const float* p = a.part + tt * (RM * RN) + lr * RN + lc;
+    float4 v = *reinterpret_cast<const float4*>(p);
+    for (int zz = 1; zz < a.ztail; ++zz) {
+        const float4 b = *reinterpret_cast<const float4*>(p + int64_t(zz) * trem * (RM * RN));
+        v.x += b.x;
+        v.y += b.y;
+        v.z += b.z;
+        v.w += b.w;
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    for (int e = 0; e < 4; ++e)
+        if (col + e < N) a.h[m * N + col + e] = to_bf16(vv[e]);
+}
+
 // The multi-adapter forward after a split reduction: h[m][n] = bf16( the
 // partials summed in split order + the gathered rank-r term ).  A wave takes
 // 64 consecutive columns of one row, so the token's id and su row are
@@ -906,8 +976,36 @@ int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, 
     return NF4_OK;
 }
 
+struct TailPlan {
+    int64_t T, tfull, grid;
+    int z, spl;
+};
+
+static TailPlan tail_plan(int64_t M, int64_t rows, int64_t cols) {
+    constexpr int64_t kCUs = 256;  // one workgroup per CU (the LDS of this kernel)
+    TailPlan p{};
+    p.T = cdiv(M, RM) * cdiv(rows, RN);
+    p.tfull = p.T / kCUs * kCUs;
+    const int64_t trem = p.T - p.tfull;
+    const int64_t S1 = cols / RKS;
+    p.z = 1;
+    p.spl = int(S1);
+    if (trem > 0) {
+        const int64_t z = std::min<int64_t>(4, std::max<int64_t>(1, kCUs / trem));
+        const int64_t spl = cdiv(cdiv(S1, z), 4) * 4;
+        p.z = int(cdiv(S1, spl));
+        p.spl = int(spl);
+    }
+    if (p.z <= 1) {
+        p.z = 1;
+        p.tfull = p.T;
+    }
+    p.grid = p.tfull + (p.T - p.tfull) * p.z;
+    return p;
+}
+
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
-               const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st) {
+               const uint16_t* B, int r, uint16_t* h, float* scale_ws, float* tail_ws, hipStream_t st) {
     const float* scales = q.absmax;
     const int64_t nb = q.rows * q.cols / 64;
     if (q.dq) {
@@ -919,11 +1017,24 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
         if (hipPeekAtLastError() != hipSuccess) return launch_status();
         scales = scale_ws;
     }
+    const TailPlan tp = tail_plan(M, q.rows, q.cols);
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, r > 0 ? ext : nullptr, B, h,
-              M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0, nullptr, int(q.cols / RKS)};
-    const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
-    launch_dominant(k_fwd_rd<false>, dim3(unsigned(T)), dim3(RT), 0, st, a);
-    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+              M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0, tail_ws, int(q.cols / RKS),
+              tp.tfull, tp.z, tp.spl};
+    launch_dominant(k_fwd_rd<false>, dim3(unsigned(tp.grid)), dim3(RT), 0, st, a);
+    if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    if (tp.z > 1) {
+        hipLaunchKernelGGL(k_tail_sum, dim3(unsigned((tp.T - tp.tfull) * (RM / 4))), dim3(256), 0, st, a);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+    }
+    return NF4_OK;
+}
+
+// One full pass of the GPU (kCUs workgroups) over the first tiles, then the
+// remaining tiles split so that their pass is shorter.
+size_t fwd_tail_bytes(int64_t M, int64_t rows, int64_t cols) {
+    const TailPlan tp = tail_plan(M, rows, cols);
+    return tp.z > 1 ? align256(size_t(tp.z) * size_t(tp.T - tp.tfull) * RM * RN * 4) : 0;
 }
 
 // Splits of the forward reduction for the multi-adapter pass: enough
@@ -951,7 +1062,7 @@ int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* 
     const int S1 = int(q.cols / RKS);
     const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, nullptr, nullptr, h,
-              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl};
+              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl, 0, 1, spl};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
     launch_dominant(k_fwd_rd<true>, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();

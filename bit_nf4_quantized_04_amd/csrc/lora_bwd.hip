@@ -247,13 +247,36 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict_
 // out[j][i] = scale * sum_z part[z][i][j]  (i < n, j < r): the transposed reduce of dA
 __global__ __launch_bounds__(256) void k_reduce_t(const float* __restrict__ part, int Z, int64_t n, int r,
                                                   float scale, float* __restrict__ out) {
-    const int64_t tot = n * r;
-    for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < tot; t += int64_t(gridDim.x) * 256) {
-        const int64_t j = t / n, i = t % n;
+    // out[j][i] = scale * sum_z part[z][i][j]; a workgroup takes 16 i x 64 j:
+    // partial rows are read along j (contiguous), summed in split order,
+    // transposed through LDS and written along i
+    __shared__ float tile[16][65];
+    const int64_t i0 = int64_t(blockIdx.x) * 16;
+    const int j0 = int(blockIdx.y) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
+    const int j = j0 + tx;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int ii = ty + 4 * k;
+        const int64_t i = i0 + ii;
         float a = 0.0f;
-        for (int z = 0; z < Z; ++z) a += part[(int64_t(z) * n + i) * r + j];
-        out[t] = a * scale;
+        if (i < n && j < r) {
+            const float* p = part + i * r + j;
+#pragma unroll 8
+            for (int z = 0; z < Z; ++z) a += p[int64_t(z) * n * r];
+        }
+        tile[ii][tx] = a;
     }
+    __syncthreads();
+    // 64 j x 16 i outputs: thread (jj, iq) writes i0 + 4iq .. +3 of row j0 + jj
+    const int jj = threadIdx.x >> 2, iq = threadIdx.x & 3;
+    const int jo = j0 + jj;
+    if (jo < r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = i0 + 4 * iq + e;
+            if (i < n) out[int64_t(jo) * n + i] = tile[4 * iq + e][jj] * scale;
+        }
 }
 
 unsigned ew(int64_t n) { return unsigned(std::max<int64_t>(1, std::min<int64_t>(8192, (n + 255) / 256))); }
@@ -306,7 +329,8 @@ int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* b
 }
 
 int reduce_t(hipStream_t st, const float* part, int Z, int64_t n, int r, float scale, float* out) {
-    hipLaunchKernelGGL(k_reduce_t, dim3(ew(n * r)), dim3(256), 0, st, part, Z, n, r, scale, out);
+    hipLaunchKernelGGL(k_reduce_t, dim3(unsigned(cdiv(n, 16)), unsigned(cdiv(r, 64))), dim3(256), 0, st, part, Z, n,
+                       r, scale, out);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

@@ -69,8 +69,11 @@ int forward_big(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ex
 // block scales.
 size_t rd_scales_bytes(int64_t rows, int64_t cols);
 bool use_rd(const QView& q, int64_t M, int r, int KL);
+// When the tiles leave a partial last pass over the CUs, that pass's tiles
+// split their reduction (fwd_tail_bytes() of workspace for the partials).
+size_t fwd_tail_bytes(int64_t M, int64_t rows, int64_t cols);
 int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
-               const uint16_t* B, int r, uint16_t* h, float* scale_ws, hipStream_t st);
+               const uint16_t* B, int r, uint16_t* h, float* scale_ws, float* tail_ws, hipStream_t st);
 // One AdamW step on adapter parameters (adamw.hip).
 int adamw_step(float* p, const float* g, float* m, float* v, uint16_t* pb, int64_t n, int step, float lr,
                float beta1, float beta2, float eps, float weight_decay, hipStream_t st);

@@ -320,6 +320,28 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
     }
 }
 
+// u = the sum of the Z down-projection partials (in order), and ext [M][KL]
+// = (bf16 hi of scale*u | bf16 lo | 0 pad), from one pass.
+__global__ __launch_bounds__(256) void k_fin_u(const float* __restrict__ part, int Z, int64_t M, int r, int KL,
+                                               float scale, float* __restrict__ u, uint16_t* __restrict__ ext) {
+    const int64_t n = M * KL;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+        const int64_t m = i / KL;
+        const int c = int(i - m * KL);
+        if (c < r) {
+            float a = 0.0f;
+            for (int z = 0; z < Z; ++z) a += part[(int64_t(z) * M + m) * r + c];
+            u[m * r + c] = a;
+            uint16_t h, l;
+            split_bf16(__fmul_rn(scale, a), h, l);
+            ext[i] = h;
+            ext[i + r] = l;
+        } else if (c >= 2 * r) {
+            ext[i] = 0;
+        }
+    }
+}
+
 // From v [M][r] fp32: ext [M][KL] = (bf16 hi of scale*v | bf16 lo | 0 pad),
 // and optionally hi/lo [M][r] of v itself.
 __global__ __launch_bounds__(256) void k_splits(const float* __restrict__ v, int64_t M, int r, int KL,
@@ -506,9 +528,8 @@ int down_projection(hipStream_t st, const nf4::QView& q, const uint16_t* x, int6
         rc = gemm(st, M, r, lx, la, q.cols, LdNone{}, LdNone{}, 0, OutPartial{part, M, r}, fp.Zu);
     }
     if (rc) return rc;
-    hipLaunchKernelGGL(k_reduce, dim3(ew_grid(M * r)), dim3(256), 0, st, part, fp.Zu, M * r, 1.0f, u);
-    hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * ext_cols(r))), dim3(256), 0, st, u, M, r,
-                       ext_cols(r), scale, ext, (uint16_t*)nullptr, (uint16_t*)nullptr);
+    hipLaunchKernelGGL(k_fin_u, dim3(ew_grid(M * ext_cols(r))), dim3(256), 0, st, part, fp.Zu, M, r,
+                       ext_cols(r), scale, u, ext);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : nf4::launch_status();
 }
 
@@ -599,13 +620,8 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
         // dU = s dH B (B^T made contiguous along out first)
         if ((rc = transpose16(st, B, out, r, bt))) return rc;
         if ((rc = nt_product(st, dH, M, out, bt, r, bp.Zdu, part))) return rc;
-        hipLaunchKernelGGL(k_reduce, dim3(ew_grid(M * r)), dim3(256), 0, st, part, bp.Zdu, M * r, scale, du);
-        hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * KL)), dim3(256), 0, st, du, M, r, KL, 1.0f, duext,
-                           (uint16_t*)nullptr, (uint16_t*)nullptr);
-        if (hipPeekAtLastError() != hipSuccess) return launch_status();
+        if ((rc = fin_du(st, part, bp.Zdu, M, r, KL, scale, u, duext, duq, uq))) return rc;
         // dB = s dH^T u, dA = dU^T x: reductions over the tokens
-        if ((rc = split128(st, u, M, r, uq))) return rc;
-        if ((rc = split128(st, du, M, r, duq))) return rc;
         if ((rc = tn_product(st, dH, M, out, uq, r, bp.Zdb, part))) return rc;
         hipLaunchKernelGGL(k_reduce, dim3(ew_grid(out * r)), dim3(256), 0, st, part, bp.Zdb, out * r, scale, dB);
         if (hipPeekAtLastError() != hipSuccess) return launch_status();

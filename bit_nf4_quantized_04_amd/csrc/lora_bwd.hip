@@ -42,59 +42,105 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f
 
 // ------------------------------------------------------------------ k_nt
 // part[z][m][j] = sum over k in chunk z of P[m][k] * Q[j][k]; P [M][K],
-// Q [J][K] bf16, J <= 32 * NF.  Wave w of block bx owns rows
-// 128 bx + 32 w .. +31; lane (row, hh) loads 8 consecutive k of its row.
-template <int NF>
+// Q [J][K] bf16, J <= 16 * NJ, K % 16 == 0, chunks of NT_SLAB multiples.
+// A workgroup owns 32 rows and one chunk, walked in slabs of 512 k; wave w
+// takes the 128 k at 128 w of each slab, so a workgroup streams 1 KB of
+// every row per slab.  v_mfma_f32_16x16x32_bf16: lane (i, g) = (lane % 16,
+// lane / 16) holds k 8g .. 8g + 7 of a 32-k slice of row (or Q row) i, so
+// the four lanes of a row read 64 contiguous bytes and each load
+// instruction touches 16 rows.  The four waves' sums meet in LDS at the
+// end, and only one fp32 partial per workgroup goes to memory: short rows
+// of tokens with long chunks keep the partials small next to the streamed
+// operand.  Every workgroup reads its chunk of Q; when the splits are a
+// multiple of 8 the workgroups that share an XCD (consecutive ids go round
+// the eight XCDs) share chunks, so each XCD's L2 holds an eighth of Q while
+// P streams past.
+constexpr int NT_ROWS = 32, NT_SLAB = 512;
+
+template <int NJ>
 __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int64_t M, int64_t K,
-                                            const uint16_t* __restrict__ Q, int J, int64_t kchunk,
+                                            const uint16_t* __restrict__ Q, int J, int64_t kchunk, int Z,
                                             float* __restrict__ part) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int rl = lane & 31, hh = lane >> 5;
-    const int64_t m = int64_t(blockIdx.x) * 128 + 32 * w + rl;
-    const int64_t mc = m < M ? m : M - 1;
-    const int z = blockIdx.y;
+    constexpr int RS = 16 * NJ + 4;  // LDS row stride (floats): the four row groups of a fragment 16 banks apart
+    __shared__ float red[4][NT_ROWS][RS];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int li = lane & 15, g = lane >> 4;
+    const int64_t lin = blockIdx.x;
+    int64_t tile;
+    int z;
+    if ((Z & 7) == 0) {  // XCD lin % 8 takes splits lin % 8 + 8 i
+        const int64_t rest = lin >> 3, q = Z >> 3;
+        z = int(lin & 7) + 8 * int(rest % q);
+        tile = rest / q;
+    } else {
+        z = int(lin % Z);
+        tile = lin / Z;
+    }
+    const int64_t m0 = tile * NT_ROWS;
     const int64_t k0 = int64_t(z) * kchunk, k1 = std::min<int64_t>(K, k0 + kchunk);
-    const uint16_t* pr = P + mc * K + 8 * hh;
-    const uint16_t* qr[NF];
+    const uint16_t* pr[2];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const int j = 32 * f + rl;
-        qr[f] = Q + int64_t(j < J ? j : J - 1) * K + 8 * hh;
+    for (int rb = 0; rb < 2; ++rb) {
+        const int64_t m = m0 + 16 * rb + li;
+        pr[rb] = P + (m < M ? m : M - 1) * K + 8 * g;
     }
-    f32x16_t acc[NF];
+    const uint16_t* qr[NJ];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int jb = 0; jb < NJ; ++jb) {
+        const int j = 16 * jb + li;
+        qr[jb] = Q + int64_t(j < J ? j : J - 1) * K + 8 * g;
+    }
+    f32x4_t acc[2][NJ];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[f][v] = 0.0f;
-    int64_t k = k0;
-    for (; k + 128 <= k1; k += 128) {  // eight slices of 16, all loads first
-        u32x4_t a[8], b[8][NF];
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            a[s] = *reinterpret_cast<const u32x4_t*>(pr + k + 16 * s);
+        for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int64_t kb = k0 + 128 * w; kb < k1; kb += NT_SLAB) {
+        if (kb + 128 <= k1) {  // four slices of 32, all loads first
+            u32x4_t a[4][2], b[4][NJ];
 #pragma unroll
-            for (int f = 0; f < NF; ++f) b[s][f] = *reinterpret_cast<const u32x4_t*>(qr[f] + k + 16 * s);
+            for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) a[sl][rb] = *reinterpret_cast<const u32x4_t*>(pr[rb] + kb + 32 * sl);
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb) b[sl][jb] = *reinterpret_cast<const u32x4_t*>(qr[jb] + kb + 32 * sl);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a[sl][rb], b[sl][jb], acc[rb][jb]);
+        } else {
+            for (int64_t k = kb; k < k1; k += 32) {
+                // K % 16 == 0: a last slice of 16 leaves the lanes of g >= 2 past K
+                const bool ok = k + 8 * g < k1;
+                const u32x4_t zero = {0u, 0u, 0u, 0u};
+                u32x4_t a[2], b[NJ];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) a[rb] = ok ? *reinterpret_cast<const u32x4_t*>(pr[rb] + k) : zero;
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb) b[jb] = ok ? *reinterpret_cast<const u32x4_t*>(qr[jb] + k) : zero;
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a[rb], b[jb], acc[rb][jb]);
+            }
         }
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int f = 0; f < NF; ++f) acc[f] = mfma32(a[s], b[s][f], acc[f]);
     }
-    for (; k < k1; k += 16) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(pr + k);
+    // D layout of the 16x16 MFMA: lane holds column li and rows 4g + e
 #pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] = mfma32(a, *reinterpret_cast<const u32x4_t*>(qr[f] + k), acc[f]);
-    }
-    // D layout: lane holds column rl and rows 8(v/4) + 4hh + v%4 of the frag
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const int j = 32 * f + rl;
-        if (j >= J) continue;
+        for (int jb = 0; jb < NJ; ++jb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t mm = int64_t(blockIdx.x) * 128 + 32 * w + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (mm < M) part[(int64_t(z) * M + mm) * J + j] = acc[f][v];
-        }
+            for (int e = 0; e < 4; ++e) red[w][16 * rb + 4 * g + e][16 * jb + li] = acc[rb][jb][e];
+    __syncthreads();
+    const int rows = int(std::min<int64_t>(NT_ROWS, M - m0));
+    for (int idx = tid; idx < rows * J; idx += 256) {
+        const int row = idx / J, j = idx - row * J;
+        const float a = (red[0][row][j] + red[1][row][j]) + (red[2][row][j] + red[3][row][j]);
+        part[(int64_t(z) * M + m0 + row) * J + j] = a;
     }
 }
 
@@ -217,24 +263,35 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
     }
 }
 
-// q2 [M][128]: bf16 hi of v[m][j] at column j, lo at 64 + j (j < r <= 64), zero elsewhere.
-__global__ __launch_bounds__(256) void k_split128(const float* __restrict__ v, int64_t M, int r,
-                                                  uint16_t* __restrict__ q2) {
-    const int64_t n = M * 128;
+// The end of dU: du = scale * (sum of the Z partials, in order), and the
+// bf16 forms the later products read, all from one pass (r <= 64):
+// duext [M][KL] = [hi | lo of du | 0 pad] for the dX rank-r steps, and
+// duq / uq [M][128] = hi at column j, lo at 64 + j (zero past r) of du and u.
+__global__ __launch_bounds__(256) void k_fin_du(const float* __restrict__ part, int Z, int64_t M, int r,
+                                                int KL, float scale, const float* __restrict__ u,
+                                                uint16_t* __restrict__ duext, uint16_t* __restrict__ duq,
+                                                uint16_t* __restrict__ uq) {
+    const int64_t n = M * 64;
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
-        const int64_t m = i >> 7;
-        const int c = int(i & 127), j = c & 63;
-        uint16_t val = 0;
+        const int64_t m = i >> 6;
+        const int j = int(i & 63);
+        uint16_t dh = 0, dl = 0, uh = 0, ul = 0;
         if (j < r) {
-            uint16_t h, l;
-            split_bf16(v[m * r + j], h, l);
-            val = c < 64 ? h : l;
+            float a = 0.0f;
+            for (int z = 0; z < Z; ++z) a += part[(int64_t(z) * M + m) * r + j];
+            split_bf16(a * scale, dh, dl);
+            split_bf16(u[m * r + j], uh, ul);
+            duext[m * KL + j] = dh;
+            duext[m * KL + r + j] = dl;
         }
-        q2[i] = val;
+        if (2 * r + j < KL) duext[m * KL + 2 * r + j] = 0;
+        duq[m * 128 + j] = dh;
+        duq[m * 128 + 64 + j] = dl;
+        uq[m * 128 + j] = uh;
+        uq[m * 128 + 64 + j] = ul;
     }
 }
 
-// bt [r][n] = b [n][r] (bf16)
 __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ b, int64_t n, int r,
                                                      uint16_t* __restrict__ bt) {
     const int64_t tot = n * r;
@@ -286,12 +343,16 @@ unsigned ew(int64_t n) { return unsigned(std::max<int64_t>(1, std::min<int64_t>(
 namespace nf4 {
 
 // Splits of the reduction so that the grid holds about 1024 workgroups.
+// Splits of the reduction: one per slab when there are fewer than eight
+// slabs, else a multiple of 8 (at least 512 workgroups when the rows allow);
+// chunks are whole slabs, and a trailing chunk past K adds zero.
 int nt_splits(int64_t M, int64_t K) {
-    const int64_t tiles = cdiv(M, 128);
-    int64_t z = cdiv(1024, tiles);
-    z = std::min<int64_t>(z, std::max<int64_t>(1, K / 128));
-    return int(std::max<int64_t>(1, std::min<int64_t>(z, 64)));
+    const int64_t slabs = cdiv(K, NT_SLAB);
+    if (slabs < 8) return int(slabs);
+    const int64_t tiles = cdiv(M, NT_ROWS);
+    return int(8 * std::max<int64_t>(1, std::min<int64_t>(cdiv(512, 8 * tiles), slabs / 8)));
 }
+int64_t nt_chunk(int64_t K, int Z) { return cdiv(cdiv(K, Z), NT_SLAB) * NT_SLAB; }
 int tn_splits(int64_t RR, int64_t M) {
     const int64_t tiles = cdiv(RR, 256);
     int64_t z = cdiv(768, tiles);
@@ -301,12 +362,17 @@ int tn_splits(int64_t RR, int64_t M) {
 
 int nt_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t K, const uint16_t* Q, int J, int Z,
                float* part) {
-    const int64_t kchunk = cdiv(cdiv(K, Z), 16) * 16;
-    const dim3 grid(unsigned(cdiv(M, 128)), unsigned(Z));
-    if (J <= 32)
-        hipLaunchKernelGGL(k_nt<1>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, part);
+    if (Z != nt_splits(M, K)) return NF4_EINVAL;
+    const int64_t kchunk = nt_chunk(K, Z);
+    const int64_t nwg = cdiv(M, NT_ROWS) * Z;
+    if (nwg >= (int64_t(1) << 31)) return NF4_ESHAPE;
+    const dim3 grid = dim3(unsigned(nwg));
+    if (J <= 16)
+        hipLaunchKernelGGL(k_nt<1>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, Z, part);
+    else if (J <= 32)
+        hipLaunchKernelGGL(k_nt<2>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, Z, part);
     else
-        hipLaunchKernelGGL(k_nt<2>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, part);
+        hipLaunchKernelGGL(k_nt<4>, grid, dim3(256), 0, st, P, M, K, Q, J, kchunk, Z, part);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
@@ -318,8 +384,9 @@ int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const u
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
-int split128(hipStream_t st, const float* v, int64_t M, int r, uint16_t* q2) {
-    hipLaunchKernelGGL(k_split128, dim3(ew(M * 128)), dim3(256), 0, st, v, M, r, q2);
+int fin_du(hipStream_t st, const float* part, int Z, int64_t M, int r, int KL, float scale, const float* u,
+           uint16_t* duext, uint16_t* duq, uint16_t* uq) {
+    hipLaunchKernelGGL(k_fin_du, dim3(ew(M * 64)), dim3(256), 0, st, part, Z, M, r, KL, scale, u, duext, duq, uq);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

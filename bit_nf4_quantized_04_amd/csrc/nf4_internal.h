@@ -117,7 +117,10 @@ int nt_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t K, const ui
                float* part);
 int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const uint16_t* Q2, int J, int Z,
                float* part);
-int split128(hipStream_t st, const float* v, int64_t M, int r, uint16_t* q2);
+// The dU partials summed and scaled, written as the dX extension (hi | lo |
+// pad, [M][KL]) and as hi/lo [M][128] for the dA product, with u's hi/lo too.
+int fin_du(hipStream_t st, const float* part, int Z, int64_t M, int r, int KL, float scale, const float* u,
+           uint16_t* duext, uint16_t* duq, uint16_t* uq);
 int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt);
 int reduce_t(hipStream_t st, const float* part, int Z, int64_t n, int r, float scale, float* out);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)

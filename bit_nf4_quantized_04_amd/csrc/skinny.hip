@@ -239,6 +239,17 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
     }
 }
 
+// v as held by another lane of the same quad (DPP quad_perm: 0x55 reads quad
+// position 1, 0xAA position 2, 0xFF position 3), and one lane's v for the
+// whole wave
+template <int CTRL>
+__device__ __forceinline__ float quad_from(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_val(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 // ---------------------------------------------------------------------------
 // M = 1: the "diagonal" dequant-GEMV.
 //
@@ -269,16 +280,16 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
 // of resident workgroups (at most), and workgroup b takes chunks b, b + G,
 // b + 2G, ... of the G-strided sequence: neighbouring workgroups stream
 // neighbouring rows, and no counter or atomic is involved.
-constexpr int G1_NC = 2;  // rows per wave per chunk (the ping-pong pair)
+constexpr int G1_NC = 3;  // rows per wave per chunk (and fetch ring slots)
 
 template <bool DQ, bool GSH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_gemv1(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv1(
     nf4::QView q, const uint16_t* __restrict__ x, const float* __restrict__ upart, int r,
     const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
     float* __restrict__ u_out, int R, int nchunks) {
     __shared__ __attribute__((aligned(16))) uint32_t tbl[4][16][64];  // [wave][entry][lane]
     __shared__ float q127[128];
-    __shared__ float dlds[2][4][G1_NC][16];  // diagonal D[i][i] per (parity, wave, row, i)
+    __shared__ float dlds[2][4][G1_NC];  // the wave's region sum per (parity, wave, row)
     __shared__ float us[64];
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -351,8 +362,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
         // count on every path, the value unused)
         f.bv = *reinterpret_cast<const uint16_t*>(lora ? bbase + (crow * uint32_t(r) + lane_rc) * 2u : codes);
     };
-    // the diagonal element held by this lane: D[4(l/16)+e][l%16] with e = l%16 - 4(l/16)
-    const int de = (l & 15) - 4 * (l >> 4);
     __syncthreads();  // q127, us ready
     // A fragment of the rank-r step: {hi, lo} of s*u[l] in the first dword
     uint32_t ua0 = 0u;
@@ -412,45 +421,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
             acc = mfma16(xa[st], we, acc);
             acc = mfma16(xa[st], wo, acc);
         }
-        float d = 0.0f;
-        d = (de == 0) ? acc[0] : d;
-        d = (de == 1) ? acc[1] : d;
-        d = (de == 2) ? acc[2] : d;
-        d = (de == 3) ? acc[3] : d;
-        if (de >= 0 && de < 4) dlds[par][w][i][l & 15] = d;  // the 16 diagonal holders
+        // the region sum is the trace of D: lane 20g + e holds D[4g+e][4g+e]
+        // in acc[e], so the quad at lane 20g gathers its four diagonal
+        // entries and the four quads (lanes 0, 20, 40, 60) add up
+        const float qd = (acc[0] + quad_from<0x55>(acc[1])) + (quad_from<0xAA>(acc[2]) + quad_from<0xFF>(acc[3]));
+        const float t = (lane_val(qd, 0) + lane_val(qd, 20)) + (lane_val(qd, 40) + lane_val(qd, 60));
+        if (l == 0) dlds[par][w][i] = t;
     };
 
-    // chunk c: rows c*rows_chunk + sub*G1_NC + {0, 1}; row 0 of the next chunk
-    // is fetched while row 1 of this one is processed (unconditionally: past
-    // the end the fetch reads the clamped last row, which keeps the load
-    // counts of every path equal).  The scheduling barriers keep each row's
-    // loads issued a whole row ahead of their use.
+    // The wave's rows in order: chunk c contributes rows c*rows_chunk +
+    // sub*G1_NC + {0 .. G1_NC-1}, and the chunks are blockIdx.x, +G, +2G, ...
+    // A ring of G1_NC fetch slots keeps the next G1_NC - 1 rows in flight
+    // while one row is processed (past the end the fetches read the clamped
+    // last row, which keeps the load counts of every path equal).  The
+    // scheduling barriers keep each row's loads issued that far ahead.
     const int G = int(gridDim.x);
     int c = blockIdx.x;
-    Fetch fa, fb;
-    fetch(int64_t(c) * rows_chunk + sub * G1_NC, fa);
+    auto seq_row = [&](int cc, int j) {  // row j of the ring, counted from chunk cc
+        return int64_t(cc + (j / G1_NC) * G) * rows_chunk + sub * G1_NC + (j % G1_NC);
+    };
+    Fetch ring[G1_NC];
+#pragma unroll
+    for (int j = 0; j < G1_NC - 1; ++j) fetch(seq_row(c, j), ring[j]);
     for (int k = 0; c < nchunks; ++k, c += G) {
-        const int64_t rbase = int64_t(c) * rows_chunk + sub * G1_NC;
-        fetch(rbase + 1, fb);
-        __builtin_amdgcn_sched_barrier(0);
-        process(fa, k & 1, 0);
-        fetch(rbase + int64_t(G) * rows_chunk, fa);
-        __builtin_amdgcn_sched_barrier(0);
-        process(fb, k & 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < G1_NC; ++i) {
+            fetch(seq_row(c, i + G1_NC - 1), ring[(i + G1_NC - 1) % G1_NC]);
+            __builtin_amdgcn_sched_barrier(0);
+            process(ring[i], k & 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __syncthreads();
         // finish the chunk's rows: regions summed, in order
         if (tid < rows_chunk) {
             const int sb = tid / G1_NC, i = tid % G1_NC;
             const int64_t o = int64_t(c) * rows_chunk + tid;
             float v = 0.0f;
-            for (int rr = 0; rr < R; ++rr) {
-                const float* dd = dlds[k & 1][sb * R + rr][i];
-                float t = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) t += dd[e];
-                v += t;
-            }
+            for (int rr = 0; rr < R; ++rr) v += dlds[k & 1][sb * R + rr][i];
             if (o < N) h[o] = to_bf16(v);
         }
     }

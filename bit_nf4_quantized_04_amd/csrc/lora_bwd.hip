@@ -147,8 +147,11 @@ __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int6
 // ------------------------------------------------------------------ k_tn
 // part[z][R][j] = sum over tokens m in chunk z of P[m][R] * (Qh[m][j] + Ql[m][j])
 // with Q2 = [M][128] (hi at j, lo at 64 + j), j < J <= 64.  Block bx owns
-// columns R0 = 256 bx .. +255 of P; wave w the 64 of them at 64 w.
-constexpr int TN_PS = 256 + 32;  // LDS row stride of the P tile (elements): 576 bytes
+// columns R0 = 128 bx .. +127 of P; wave w the 32 of them at 32 w.  Narrow
+// column stripes leave room for few token chunks, so the fp32 partials stay
+// well below the streamed operand.
+constexpr int TN_COLS = 128;
+constexpr int TN_PS = TN_COLS + 32;  // LDS row stride of the P tile (elements): 320 bytes
 constexpr int TN_QS = 128 + 32;  // of the Q tile: 320 bytes
 
 // Four consecutive k (rows kb + 8(q>>1) + 4h .. +3) of column cb + (lane % 32),
@@ -171,20 +174,20 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
     __shared__ __attribute__((aligned(16))) uint16_t pt[64 * TN_PS];
     __shared__ __attribute__((aligned(16))) uint16_t qt[64 * TN_QS];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t R0 = int64_t(blockIdx.x) * 256;
+    const int64_t R0 = int64_t(blockIdx.x) * TN_COLS;
     const int z = blockIdx.y;
     const int64_t m0 = int64_t(z) * mchunk, m1 = std::min<int64_t>(M, m0 + mchunk);
     const bool pvec = RR % 8 == 0;
 
-    // tile loads into registers: P chunk c = tid + 256 i (row c/32, 16-byte
-    // chunk c%32), Q chunk c = tid + 256 i (row c/16, chunk c%16); rows past
+    // tile loads into registers: P chunk c = tid + 256 i (row c/16, 16-byte
+    // chunk c%16), Q chunk c = tid + 256 i (row c/16, chunk c%16); rows past
     // the chunk are zero (they would otherwise count twice)
-    uint4 pv[8], qv[4];
+    uint4 pv[4], qv[4];
     auto load = [&](int64_t mb) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i;
-            const int64_t mm = mb + (c >> 5), rr = R0 + 8 * (c & 31);
+            const int64_t mm = mb + (c >> 4), rr = R0 + 8 * (c & 15);
             uint4 v = make_uint4(0, 0, 0, 0);
             if (mm < m1) {
                 const uint16_t* src = P + mm * RR + rr;
@@ -209,9 +212,9 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
     };
     auto store = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i;
-            *reinterpret_cast<uint4*>(&pt[(c >> 5) * TN_PS + 8 * (c & 31)]) = pv[i];
+            *reinterpret_cast<uint4*>(&pt[(c >> 4) * TN_PS + 8 * (c & 15)]) = pv[i];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -220,13 +223,11 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
         }
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) acc[f][v] = 0.0f;
 
     if (m0 < m1) load(m0);
     for (int64_t mb = m0; mb < m1; mb += 64) {
@@ -236,15 +237,12 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
         if (mb + 64 < m1) load(mb + 64);
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-            u32x4_t a[2], b[4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = tr_frag(pt, TN_PS, 16 * sl, 64 * w + 32 * i, lane);
+            u32x4_t b[4];
+            const u32x4_t a = tr_frag(pt, TN_PS, 16 * sl, 32 * w, lane);
 #pragma unroll
             for (int f = 0; f < 4; ++f) b[f] = tr_frag(qt, TN_QS, 16 * sl, 32 * f, lane);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int f = 0; f < 4; ++f) acc[i][f] = mfma32(a[i], b[f], acc[i][f]);
+            for (int f = 0; f < 4; ++f) acc[f] = mfma32(a, b[f], acc[f]);
         }
     }
     // C[R][j] = hi part (frags 0, 1) + lo part (frags 2, 3)
@@ -254,12 +252,10 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
         const int j = 32 * f + rl;
         if (j >= J) continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t R = R0 + 64 * w + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
-                if (R < RR) part[(int64_t(z) * RR + R) * J + j] = acc[i][f][v] + acc[i][f + 2][v];
-            }
+        for (int v = 0; v < 16; ++v) {
+            const int64_t R = R0 + 32 * w + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (R < RR) part[(int64_t(z) * RR + R) * J + j] = acc[f][v] + acc[f + 2][v];
+        }
     }
 }
 
@@ -353,12 +349,14 @@ int nt_splits(int64_t M, int64_t K) {
     return int(8 * std::max<int64_t>(1, std::min<int64_t>(cdiv(512, 8 * tiles), slabs / 8)));
 }
 int64_t nt_chunk(int64_t K, int Z) { return cdiv(cdiv(K, Z), NT_SLAB) * NT_SLAB; }
-int tn_splits(int64_t RR, int64_t M) {
-    const int64_t tiles = cdiv(RR, 256);
-    int64_t z = cdiv(768, tiles);
-    z = std::min<int64_t>(z, std::max<int64_t>(1, M / 64));
-    return int(std::max<int64_t>(1, std::min<int64_t>(z, 64)));
+// Token chunks of the column-stripe products: about 512 workgroups, chunks
+// of whole 64-token steps, and no empty chunk.
+int64_t tn_chunk(int64_t RR, int64_t M) {
+    const int64_t tiles = cdiv(RR, TN_COLS);
+    const int64_t z = std::max<int64_t>(1, std::min<int64_t>(cdiv(512, tiles), cdiv(M, 64)));
+    return cdiv(cdiv(M, z), 64) * 64;
 }
+int tn_splits(int64_t RR, int64_t M) { return int(cdiv(M, tn_chunk(RR, M))); }
 
 int nt_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t K, const uint16_t* Q, int J, int Z,
                float* part) {
@@ -378,8 +376,9 @@ int nt_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t K, const ui
 
 int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const uint16_t* Q2, int J, int Z,
                float* part) {
-    const int64_t mchunk = cdiv(cdiv(M, Z), 64) * 64;
-    hipLaunchKernelGGL(k_tn, dim3(unsigned(cdiv(RR, 256)), unsigned(Z)), dim3(256), 0, st, P, M, RR, Q2, J,
+    if (Z != tn_splits(RR, M)) return NF4_EINVAL;
+    const int64_t mchunk = tn_chunk(RR, M);
+    hipLaunchKernelGGL(k_tn, dim3(unsigned(cdiv(RR, TN_COLS)), unsigned(Z)), dim3(256), 0, st, P, M, RR, Q2, J,
                        mchunk, part);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }

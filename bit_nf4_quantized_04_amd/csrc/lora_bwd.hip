@@ -45,13 +45,16 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f
 // Q [J][K] bf16, J <= 16 * NJ, K % 16 == 0, chunks of NT_SLAB multiples.
 // A workgroup owns 32 rows and one chunk, walked in slabs of 512 k; wave w
 // takes the 128 k at 128 w of each slab, so a workgroup streams 1 KB of
-// every row per slab.  v_mfma_f32_16x16x32_bf16: lane (i, g) = (lane % 16,
-// lane / 16) holds k 8g .. 8g + 7 of a 32-k slice of row (or Q row) i, so
-// the four lanes of a row read 64 contiguous bytes and each load
-// instruction touches 16 rows.  The four waves' sums meet in LDS at the
-// end, and only one fp32 partial per workgroup goes to memory: short rows
-// of tokens with long chunks keep the partials small next to the streamed
-// operand.  Every workgroup reads its chunk of Q; when the splits are a
+// every row per slab.  Each wave stages its 32 x 128 piece of P in its own
+// LDS tile, loading four rows of 256 contiguous bytes per instruction
+// (16-byte chunk c of row i stored at chunk c ^ (i % 16), so that both the
+// stores and the fragment reads are free of bank conflicts).
+// v_mfma_f32_16x16x32_bf16: lane (i, g) = (lane % 16, lane / 16) holds k
+// 8g .. 8g + 7 of a 32-k slice of row (or Q row) i; the Q fragments, which
+// every workgroup rereads from L2, load straight from global memory.  The
+// four waves' sums meet in LDS at the end, and only one fp32 partial per
+// workgroup goes to memory: short rows of tokens with long chunks keep the
+// partials small next to the streamed operand.  Every workgroup reads its chunk of Q; when the splits are a
 // multiple of 8 the workgroups that share an XCD (consecutive ids go round
 // the eight XCDs) share chunks, so each XCD's L2 holds an eighth of Q while
 // P streams past.
@@ -62,7 +65,12 @@ __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int6
                                             const uint16_t* __restrict__ Q, int J, int64_t kchunk, int Z,
                                             float* __restrict__ part) {
     constexpr int RS = 16 * NJ + 4;  // LDS row stride (floats): the four row groups of a fragment 16 banks apart
-    __shared__ float red[4][NT_ROWS][RS];
+    // the per-wave P tiles (32 rows x 128 k each) and, after the K loop, the
+    // four waves' sums share one buffer
+    constexpr int RED_F = 4 * NT_ROWS * RS, PT_F = 4 * NT_ROWS * 16 * 4;
+    __shared__ __attribute__((aligned(16))) float lbuf[RED_F > PT_F ? RED_F : PT_F];
+    uint4(*pt)[NT_ROWS][16] = reinterpret_cast<uint4(*)[NT_ROWS][16]>(lbuf);
+    float(*red)[NT_ROWS][RS] = reinterpret_cast<float(*)[NT_ROWS][RS]>(lbuf);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const int64_t lin = blockIdx.x;
@@ -78,11 +86,14 @@ __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int6
     }
     const int64_t m0 = tile * NT_ROWS;
     const int64_t k0 = int64_t(z) * kchunk, k1 = std::min<int64_t>(K, k0 + kchunk);
-    const uint16_t* pr[2];
+    // staging loads: instruction t, lane l -> row 4t + l/16, 16-byte chunk l
+    // % 16 (rows past M read row M - 1; their sums are dropped)
+    const uint16_t* pr = P + 8 * li;
+    int64_t roff[8];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int64_t m = m0 + 16 * rb + li;
-        pr[rb] = P + (m < M ? m : M - 1) * K + 8 * g;
+    for (int t = 0; t < 8; ++t) {
+        const int64_t m = m0 + 4 * t + (lane >> 4);
+        roff[t] = (m < M ? m : M - 1) * K;
     }
     const uint16_t* qr[NJ];
 #pragma unroll
@@ -96,38 +107,41 @@ __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int6
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int64_t kb = k0 + 128 * w; kb < k1; kb += NT_SLAB) {
-        if (kb + 128 <= k1) {  // four slices of 32, all loads first
-            u32x4_t a[4][2], b[4][NJ];
+        // the wave's 32 x 128 piece of P into LDS (zero past K: K % 16 == 0
+        // keeps every 16-byte chunk either whole or wholly past the end)
+        const bool full = kb + 128 <= k1;
+        uint4 v[8];
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl) {
+        for (int t = 0; t < 8; ++t)
+            v[t] = (full || kb + 8 * li < k1) ? *reinterpret_cast<const uint4*>(pr + roff[t] + kb) : make_uint4(0u, 0u, 0u, 0u);
+        u32x4_t b[4][NJ];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) a[sl][rb] = *reinterpret_cast<const u32x4_t*>(pr[rb] + kb + 32 * sl);
+        for (int sl = 0; sl < 4; ++sl) {
+            const bool ok = full || kb + 32 * sl + 8 * g < k1;
 #pragma unroll
-                for (int jb = 0; jb < NJ; ++jb) b[sl][jb] = *reinterpret_cast<const u32x4_t*>(qr[jb] + kb + 32 * sl);
-            }
-#pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a[sl][rb], b[sl][jb], acc[rb][jb]);
-        } else {
-            for (int64_t k = kb; k < k1; k += 32) {
-                // K % 16 == 0: a last slice of 16 leaves the lanes of g >= 2 past K
-                const bool ok = k + 8 * g < k1;
-                const u32x4_t zero = {0u, 0u, 0u, 0u};
-                u32x4_t a[2], b[NJ];
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) a[rb] = ok ? *reinterpret_cast<const u32x4_t*>(pr[rb] + k) : zero;
-#pragma unroll
-                for (int jb = 0; jb < NJ; ++jb) b[jb] = ok ? *reinterpret_cast<const u32x4_t*>(qr[jb] + k) : zero;
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a[rb], b[jb], acc[rb][jb]);
-            }
+            for (int jb = 0; jb < NJ; ++jb)
+                b[sl][jb] = ok ? *reinterpret_cast<const u32x4_t*>(qr[jb] + kb + 32 * sl) : u32x4_t{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = 4 * t + (lane >> 4);
+            pt[w][row][li ^ (row & 15)] = v[t];
+        }
+        // one wave writes and reads its own tile, and LDS keeps a wave's
+        // accesses in order; the barrier keeps the compiler from moving them
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int row = 16 * rb + li;
+                const u32x4_t a = __builtin_bit_cast(u32x4_t, pt[w][row][(4 * sl + g) ^ (row & 15)]);
+#pragma unroll
+                for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a, b[sl][jb], acc[rb][jb]);
+            }
+        __builtin_amdgcn_wave_barrier();
     }
+    __syncthreads();  // every wave is done with its tile
     // D layout of the 16x16 MFMA: lane holds column li and rows 4g + e
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)

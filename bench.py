@@ -296,24 +296,7 @@ def main():
         kern = [hev.elapsed_ms(a, b) for a, b in pairs]
         for e in [t0, t1] + [e for p in pairs for e in p]:
             hev.destroy(e)
-        if hook_events:
-            # a pair of events around one dispatch also spans the queue time
-            # of one event marker; measured here as two events recorded back
-            # to back on the same stream, and taken off every dispatch
-            kern = [k - marker_ms for k in kern]
         return total, kern
-
-    def marker_cost(K):
-        pairs = [(hev.create(), hev.create()) for _ in range(K)]
-        torch.cuda.synchronize()
-        for a, b in pairs:
-            hev.record(a)
-            hev.record(b)
-        torch.cuda.synchronize()
-        v = float(np.mean([hev.elapsed_ms(a, b) for a, b in pairs]))
-        for e in [e for p in pairs for e in p]:
-            hev.destroy(e)
-        return v
 
     # whole-step timing (no hook), then the dominant kernel with the hook
     K, W = args.steps, args.warmup
@@ -322,7 +305,6 @@ def main():
         t, _ = timed(step, K, W)
         print("%s pass: %.4f ms/step over %d steps" % (args.only, t, K), flush=True)
         return
-    marker_ms = marker_cost(max(K, 20))
     t_dec, _ = timed(decode_step, K, W)
     _, k_dec = timed(decode_step, K, 1, hook_events=True)
     t_dbw, _ = timed(decode_bwd_step, K, W)
@@ -394,7 +376,7 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_gemv1"),
             "kernel": "fused dequant product, M=1", "kernel_ms": round(k_ms, 5),
-            "algorithmic_bytes_per_launch": kb, "event_marker_ms_removed": round(marker_ms, 5),
+            "algorithmic_bytes_per_launch": kb,
         },
         "train_7b": {
             "workload": "7B MLP %d->%d NF4 + double quant, r=%d, M=%d, forward + backward" % (

@@ -36,9 +36,10 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6
 WORKLOADS = {"decode": 2, "7b": 3, "70b": 4}
 
 
-def decode_bytes(out, inp, M, r, ngroups, with_A=True):
-    """Algorithmic HBM bytes of one decode forward (double quant)."""
-    b = out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * M * inp + 2 * M * out
+def decode_bytes(out, inp, M, r, ngroups, with_A=True, block=64):
+    """Algorithmic HBM bytes of one decode forward (double quant, blocks of
+    `block` elements: one int8 scale code per block)."""
+    b = out * inp // 2 + out * inp // block + 4 * ngroups + 2 * M * inp + 2 * M * out
     b += 2 * r * out + (2 * r * inp if with_A else 0)
     return b
 
@@ -315,6 +316,37 @@ def main():
     t_mg, _ = timed(merge_step, K, W)
     t_ad, _ = timed(adamw_step, K, W)
     ad_bytes = 30 * n_ad  # p, m, v read and written, g read, the bf16 copy written
+    # the decode step and the 7B training pass on weights quantized in blocks
+    # of 128 (the layer calls expand the scales per 64-element half first)
+    wt = torch.from_numpy(w).to(dev)
+    q128 = [F.nf4_quantize(wt, double_quant=True, block_size=128)]
+    del wt
+    for _ in range(2):
+        q0 = q128[0]
+        q128.append(F.NF4Weight(q0.codes.clone(), q0.absmax.clone(), q0.scale_codes.clone(),
+                                q0.group_absmax.clone(), out, inp, True, 256, 128))
+    ws_d128 = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128, out, inp, 1, r),
+                              256), dtype=torch.uint8, device=dev)
+
+    def decode128_step(i):
+        F.qlora_linear_forward(q128[i % len(q128)], x1, A, B, scale, ws=ws_d128, out=h1)
+
+    t_d128, _ = timed(decode128_step, K, W)
+    del q128
+    q7b = F.nf4_quantize(torch.from_numpy(wl.weight(c7)).to(dev), double_quant=True, block_size=128)
+    wsf7b = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128, sh7["out"], sh7["inp"],
+                                                    M7, sh7["r"]), 256), dtype=torch.uint8, device=dev)
+    wsb7b = torch.empty(max(F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD | F.QLORA_OP_BLOCK128, sh7["out"], sh7["inp"],
+                                                    M7, sh7["r"]), 256), dtype=torch.uint8, device=dev)
+
+    def train7_128_step(i):
+        _, u = F.qlora_linear_forward(q7b, x7, A7, B7, s7, want_u=True, ws=wsf7b, out=h7)
+        F.qlora_linear_backward(q7b, x7, dH7, A7, B7, s7, u=u, ws=wsb7b)
+
+    t_7b128, _ = timed(train7_128_step, K, W)
+    del q7b, wsf7b, wsb7b
+    ng128 = (out * inp // 128 + 255) // 256
+    d128_bytes = decode_bytes(out, inp, 1, r, ng128, block=128)
     mg_bytes = out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * r * (inp + out) + 2 * out * inp
     f7 = sum(train_flops(sh7["out"], sh7["inp"], M7, sh7["r"]))
     mu_flops = 2 * Mm * shm["out"] * shm["inp"] + 2 * Mm * shm["r"] * (shm["inp"] + shm["out"])
@@ -393,6 +425,16 @@ def main():
             "workload": "AdamW on the layer's adapters, %d fp32 parameters" % n_ad,
             "ms": round(t_ad, 4), "GBps": round(ad_bytes / (t_ad * 1e-3) / 1e9, 2),
             "frac_hbm_peak": round(ad_bytes / (t_ad * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "block128": {
+            "workload": "weights quantized in blocks of 128 (double quant, groups of 256 blocks): "
+                        "the 70B decode step and the 7B training pass",
+            "decode_ms": round(t_d128, 5),
+            "decode_GBps": round(d128_bytes / (t_d128 * 1e-3) / 1e9, 2),
+            "decode_frac_hbm_peak": round(d128_bytes / (t_d128 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "train_7b_ms": round(t_7b128, 4),
+            "train_7b_TFLOPs": round(f7 / (t_7b128 * 1e-3) / 1e12, 2),
+            "train_7b_frac_mfma_peak": round(f7 / (t_7b128 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "multi_adapter": {
             "workload": "%d adapters r=%d on %d->%d NF4 base, %d tokens" % (

@@ -13,16 +13,16 @@ hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Validates an nf4_tensor for a linear call (cols % 64 == 0) or for
-// dequantization (rows*cols % 64 == 0).
+// Validates an nf4_tensor for a linear call (cols % 64 == 0, rows*cols a
+// whole number of blocks) or for dequantization (a whole number of blocks).
 int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
     if (!t) return NF4_EINVAL;
-    if (t->cfg.block_size != 64) return NF4_EUNSUPPORTED;
+    if (t->cfg.block_size != 64 && t->cfg.block_size != 128) return NF4_EUNSUPPORTED;
     if (t->rows < 0 || t->cols < 0) return NF4_EINVAL;
     if (t->cfg.double_quant != 0 && t->cfg.double_quant != 1) return NF4_EINVAL;
     if (t->cfg.double_quant && t->cfg.dq_group < 1) return NF4_EUNSUPPORTED;
     const int64_t n = t->rows * t->cols;
-    if (linear ? (t->cols % 64 != 0) : (n % 64 != 0)) return NF4_ESHAPE;
+    if ((linear && t->cols % 64 != 0) || n % t->cfg.block_size != 0) return NF4_ESHAPE;
     if (n / 64 >= (int64_t(1) << 31)) return NF4_EINVAL;  // block indices are 32-bit
     if (n > 0) {
         if (!t->codes || !al16(t->codes)) return NF4_EINVAL;
@@ -43,6 +43,39 @@ int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
     v->gshift = -1;
     for (int sh = 0; sh < 31; ++sh)
         if ((1 << sh) == v->group) v->gshift = sh;
+    v->bshift = t->cfg.block_size == 128 ? 7 : 6;
+    return NF4_OK;
+}
+
+// Bytes at the front of a layer call's workspace that hold the per-half-block
+// scales of a 128-element-block weight.
+inline size_t expand_bytes(int64_t rows, int64_t cols) {
+    return (size_t(rows * cols / 64) * 4 + 255) / 256 * 256;
+}
+
+// A layer call on a 128-element-block weight runs the 64-block kernels on
+// the expanded scales or scale codes (the same dequantized values); the
+// expansion takes the front of the workspace, the call gets the rest.
+int layer_view(nf4::QView* v, void** ws, size_t* ws_bytes, hipStream_t st) {
+    if (v->bshift == 6) return NF4_OK;
+    const size_t eb = expand_bytes(v->rows, v->cols);
+    if (!*ws || *ws_bytes < eb || !al16(*ws)) return NF4_EWORKSPACE;
+    const int rc = nf4::expand_scales(*v, *ws, st);
+    if (rc) return rc;
+    if (v->dq) {  // int8 codes per half-block; a group of G blocks is 2G halves
+        v->qcodes = static_cast<const int8_t*>(*ws);
+        // (G >= 2^30 blocks of 128 covers any accepted tensor, which has
+        // fewer than 2^30 of them: one group, any size past the end will do)
+        v->group = v->group >= (1 << 30) ? 0x7fffffff : 2 * v->group;
+        v->gshift = -1;
+        for (int sh = 0; sh < 31; ++sh)
+            if ((1 << sh) == v->group) v->gshift = sh;
+    } else {
+        v->absmax = static_cast<const float*>(*ws);
+    }
+    v->bshift = 6;
+    *ws = static_cast<char*>(*ws) + eb;
+    *ws_bytes -= eb;
     return NF4_OK;
 }
 
@@ -82,7 +115,7 @@ const char* nf4_strerror(int code) {
         case NF4_OK: return "ok";
         case NF4_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad rank or scale)";
         case NF4_ESHAPE: return "shape not a multiple of the 64-element block (linear calls: cols % 64 != 0)";
-        case NF4_EUNSUPPORTED: return "unsupported configuration (block_size must be 64, dq_group >= 1)";
+        case NF4_EUNSUPPORTED: return "unsupported configuration (block_size must be 64 or 128, dq_group >= 1)";
         case NF4_EWORKSPACE: return "workspace missing or smaller than qlora_workspace_bytes()";
         case NF4_ELAUNCH: return "HIP kernel launch failed (see nf4_last_hip_error)";
         default: return "unknown error code";
@@ -118,17 +151,17 @@ int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg, size_t*
 int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* cfg, uint8_t* codes,
                  float* absmax, int8_t* scale_codes, float* group_absmax, void* stream) {
     if (!cfg) return NF4_EINVAL;
-    if (cfg->block_size != 64) return NF4_EUNSUPPORTED;
+    if (cfg->block_size != 64 && cfg->block_size != 128) return NF4_EUNSUPPORTED;
     if (cfg->double_quant != 0 && cfg->double_quant != 1) return NF4_EINVAL;
     if (cfg->double_quant && cfg->dq_group < 1) return NF4_EUNSUPPORTED;
     if (rows < 0 || cols < 0) return NF4_EINVAL;
     const int64_t n = rows * cols;
-    if (n % 64 != 0) return NF4_ESHAPE;
+    if (n % cfg->block_size != 0) return NF4_ESHAPE;
     if (n == 0) return NF4_OK;
     if (bad_ptr(W) || bad_ptr(codes) || bad_ptr(absmax)) return NF4_EINVAL;
     if (cfg->double_quant && (bad_ptr(scale_codes) || bad_ptr(group_absmax))) return NF4_EINVAL;
-    return nf4::launch_quantize(W, n, cfg->double_quant, cfg->dq_group, codes, absmax, scale_codes,
-                                group_absmax, static_cast<hipStream_t>(stream));
+    return nf4::launch_quantize(W, n, cfg->block_size, cfg->double_quant, cfg->dq_group, codes, absmax,
+                                scale_codes, group_absmax, static_cast<hipStream_t>(stream));
 }
 
 int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream) {
@@ -152,7 +185,8 @@ int nf4_dequantize_bf16(const nf4_tensor* W, uint16_t* W_out, void* stream) {
 size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
                              int32_t n_adapters) {
     if (rows < 0 || cols < 0 || M < 0 || r < 0 || r > 256) return 0;
-    return nf4::workspace_bytes(op, rows, cols, M, r, n_adapters);
+    const size_t base = nf4::workspace_bytes(op & ~QLORA_OP_BLOCK128, rows, cols, M, r, n_adapters);
+    return (op & QLORA_OP_BLOCK128) ? expand_bytes(rows, cols) + base : base;
 }
 
 int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -168,6 +202,7 @@ int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M, cons
     if (r > 0 && (bad_ptr(A) || bad_ptr(B))) return NF4_EINVAL;
     if (u_out && !al16(u_out)) return NF4_EINVAL;
     if (v.cols == 0) return NF4_EINVAL;
+    if ((rc = layer_view(&v, &ws, &ws_bytes, static_cast<hipStream_t>(stream)))) return rc;
     return nf4::forward_impl(v, x, M, A, B, r, scale, h, r > 0 ? u_out : nullptr, ws, ws_bytes,
                              static_cast<hipStream_t>(stream));
 }
@@ -185,6 +220,7 @@ int qlora_linear_forward_multi(const nf4_tensor* W, const uint16_t* x, int64_t M
     if (bad_ptr(x) || bad_ptr(h) || bad_ptr(A_bank) || bad_ptr(B_bank) || bad_ptr(scales) ||
         bad_ptr(ids))
         return NF4_EINVAL;
+    if ((rc = layer_view(&v, &ws, &ws_bytes, static_cast<hipStream_t>(stream)))) return rc;
     return nf4::forward_multi_impl(v, x, M, A_bank, B_bank, n_adapters, r, scales, ids, h, ws,
                                    ws_bytes, static_cast<hipStream_t>(stream));
 }
@@ -209,6 +245,7 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
         if (rc) return rc;
         return nf4::zero_f32(dB, v.rows * int64_t(r), st);
     }
+    if ((rc = layer_view(&v, &ws, &ws_bytes, static_cast<hipStream_t>(stream)))) return rc;
     return nf4::backward_impl(v, x, dH, M, A, B, r, scale, u, dX, dA, dB, ws, ws_bytes,
                               static_cast<hipStream_t>(stream));
 }

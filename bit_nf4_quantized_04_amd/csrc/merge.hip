@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __r
                 if (o >= N || col >= K) continue;
                 const int64_t el = o * K + col;
                 const uint32_t cd = *reinterpret_cast<const uint32_t*>(codes + el / 2);
-                const int64_t b = el >> 6;
+                const int64_t b = el >> q.bshift;
                 float s;
                 if (DQ) {
                     const int64_t g = GSH ? (b >> q.gshift) : (b / q.group);

@@ -22,10 +22,16 @@ struct QView {  // a validated nf4_tensor
     int dq;        // 0/1
     int group;     // dq_group
     int gshift;    // log2(group) when group is a power of two, else -1
+    int bshift;    // log2(block size): 6 (64 elements) or 7 (128)
 };
 
-int launch_quantize(const float* W, int64_t n, int dq, int group, uint8_t* codes, float* absmax,
+int launch_quantize(const float* W, int64_t n, int block, int dq, int group, uint8_t* codes, float* absmax,
                     int8_t* qcodes, float* gabs, hipStream_t s);
+// Every 64-element half of a 128-element block takes its block's fp32 scale,
+// or with double quant its int8 scale code (the group of dq_group blocks is
+// then 2 dq_group halves), into s64[rows*cols/64]: the layer kernels see a
+// 64-block weight that dequantizes to the same values.
+int expand_scales(const QView& q, void* s64, hipStream_t s);
 int launch_dequant_f32(const QView& q, float* out, hipStream_t s);
 int launch_dequant_bf16(const QView& q, uint16_t* out, hipStream_t s);
 

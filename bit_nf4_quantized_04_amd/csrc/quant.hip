@@ -31,19 +31,22 @@ __device__ __forceinline__ uint32_t nearest_code(float w) {
     return c;
 }
 
-// One thread = 4 consecutive elements; 16 lanes = one 64-element block.  The
-// absmax is a 16-lane butterfly max; codes of 4 elements pack into 2 bytes.
+// One thread = 4 consecutive elements; L lanes = one block of 4L elements
+// (16 lanes for 64, 32 for 128).  The absmax is an L-lane butterfly max;
+// codes of 4 elements pack into 2 bytes.
+template <int L>
 __global__ __launch_bounds__(256) void k_quant_blocks(const float4* __restrict__ W, int64_t n4,
                                                       uint16_t* __restrict__ codes,
                                                       float* __restrict__ absmax) {
+    constexpr int LSH = L == 16 ? 4 : 5;
     const int64_t stride = int64_t(gridDim.x) * 256;
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) {
-        // n4 is a multiple of 16 and so is `stride`: the 16 lanes of a block
+        // n4 is a multiple of L and so is `stride`: the L lanes of a block
         // enter and leave the loop together.
         const float4 v = W[i];
         float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+        for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
         uint32_t packed;
         if (m == 0.0f) {
             packed = 0x7777u;  // an all-zero block: every element is level 7 (0.0)
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(const float4* __restrict__
             packed = ((c0 << 4) | c1) | (((c2 << 4) | c3) << 8);
         }
         codes[i] = uint16_t(packed);
-        if ((threadIdx.x & 15) == 0) absmax[i >> 4] = m;
+        if ((threadIdx.x & (L - 1)) == 0) absmax[i >> LSH] = m;
     }
 }
 
@@ -81,19 +84,20 @@ __global__ __launch_bounds__(256) void k_dq_scales(const float* __restrict__ abs
     }
 }
 
-// One thread = one dword of codes = 8 elements of one block.
+// One thread = one dword of codes = 8 elements of one block (dword i is in
+// block i >> dsh: 8 dwords per 64-element block, 16 per 128).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ codes,
                                                  const float* __restrict__ absmax,
                                                  const int8_t* __restrict__ qcodes,
-                                                 const float* __restrict__ gabs, int G, int64_t n8,
+                                                 const float* __restrict__ gabs, int G, int dsh, int64_t n8,
                                                  void* __restrict__ out) {
     __shared__ float lv[16];
     if (threadIdx.x < 16) lv[threadIdx.x] = bits_f(level_bits(threadIdx.x));
     __syncthreads();
     const int64_t stride = int64_t(gridDim.x) * 256;
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride) {
-        const int64_t b = i >> 3;
+        const int64_t b = i >> dsh;
         float s;
         if (qcodes) {
             s = __fmul_rn(q_over_127(qcodes[b]), gabs[b / G]);
@@ -122,6 +126,27 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
     }
 }
 
+// Half-block j of a 128-element-block weight takes the scale (or the int8
+// scale code) of block j / 2.  A thread writes 16 bytes of dst (16 codes or
+// 4 scales) from the 8 or 2 source entries they repeat; dst is 16-byte
+// aligned, src is read entry by entry (it need not be).
+template <typename T>
+__global__ __launch_bounds__(256) void k_expand_scales(const T* __restrict__ src, int64_t n64,
+                                                       T* __restrict__ dst) {
+    constexpr int E = 16 / int(sizeof(T));  // entries of dst per thread
+    const int64_t nv = n64 / E;
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < nv; i += stride) {
+        T v[E];
+#pragma unroll
+        for (int k = 0; k < E / 2; ++k) v[2 * k] = v[2 * k + 1] = src[i * (E / 2) + k];
+        *reinterpret_cast<uint4*>(dst + i * E) = __builtin_bit_cast(uint4, v);
+    }
+    // the last n64 % E entries
+    const int64_t j = nv * E + int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (blockIdx.x == 0 && j < n64) dst[j] = src[j >> 1];
+}
+
 inline unsigned grid_for(int64_t items, int64_t per_block) {
     int64_t g = (items + per_block - 1) / per_block;
     const int64_t cap = 256 * 64;  // enough to fill the chip; the kernels grid-stride
@@ -134,15 +159,16 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
 
 namespace nf4 {
 
-int launch_quantize(const float* W, int64_t n, int dq, int group, uint8_t* codes, float* absmax,
+int launch_quantize(const float* W, int64_t n, int block, int dq, int group, uint8_t* codes, float* absmax,
                     int8_t* qcodes, float* gabs, hipStream_t s) {
     const int64_t n4 = n / 4;
-    hipLaunchKernelGGL(k_quant_blocks, dim3(grid_for(n4, 256)), dim3(256), 0, s,
+    auto kern = block == 128 ? k_quant_blocks<32> : k_quant_blocks<16>;
+    hipLaunchKernelGGL(kern, dim3(grid_for(n4, 256)), dim3(256), 0, s,
                        reinterpret_cast<const float4*>(W), n4, reinterpret_cast<uint16_t*>(codes),
                        absmax);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (dq) {
-        const int64_t nb = n / 64;
+        const int64_t nb = n / block;
         const int64_t ng = (nb + group - 1) / group;
         hipLaunchKernelGGL(k_dq_scales, dim3(unsigned((ng + 3) / 4)), dim3(256), 0, s, absmax, nb,
                            group, qcodes, gabs);
@@ -154,14 +180,25 @@ int launch_quantize(const float* W, int64_t n, int dq, int group, uint8_t* codes
 int launch_dequant_f32(const QView& q, float* out, hipStream_t s) {
     const int64_t n8 = q.rows * q.cols / 8;
     hipLaunchKernelGGL(k_dequant<false>, dim3(grid_for(n8, 256)), dim3(256), 0, s, q.codes,
-                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, n8, (void*)out);
+                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, q.bshift - 3, n8, (void*)out);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
 int launch_dequant_bf16(const QView& q, uint16_t* out, hipStream_t s) {
     const int64_t n8 = q.rows * q.cols / 8;
     hipLaunchKernelGGL(k_dequant<true>, dim3(grid_for(n8, 256)), dim3(256), 0, s, q.codes,
-                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, n8, (void*)out);
+                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, q.bshift - 3, n8, (void*)out);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int expand_scales(const QView& q, void* s64, hipStream_t s) {
+    const int64_t n64 = q.rows * q.cols / 64;
+    if (q.dq)
+        hipLaunchKernelGGL(k_expand_scales<int8_t>, dim3(grid_for(n64 / 16 + 1, 256)), dim3(256), 0, s, q.qcodes,
+                           n64, static_cast<int8_t*>(s64));
+    else
+        hipLaunchKernelGGL(k_expand_scales<float>, dim3(grid_for(n64 / 4 + 1, 256)), dim3(256), 0, s, q.absmax,
+                           n64, static_cast<float*>(s64));
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

@@ -26,6 +26,7 @@ _lib = C.CDLL(LIB_PATH)
 
 NF4_OK, NF4_EINVAL, NF4_ESHAPE, NF4_EUNSUPPORTED, NF4_EWORKSPACE, NF4_ELAUNCH = range(6)
 QLORA_OP_FORWARD, QLORA_OP_BACKWARD, QLORA_OP_FORWARD_MULTI = 1, 2, 3
+QLORA_OP_BLOCK128 = 0x100  # OR'ed into a workspace query for a weight with 128-element blocks
 
 
 class nf4_config(C.Structure):
@@ -185,35 +186,41 @@ class NF4Weight:
     cols: int
     double_quant: bool
     dq_group: int = 256
+    block_size: int = 64
+
+    @property
+    def op_flags(self) -> int:
+        """Flag for the workspace queries of the layer calls on this weight."""
+        return QLORA_OP_BLOCK128 if self.block_size == 128 else 0
 
     def c_struct(self) -> nf4_tensor:
         return nf4_tensor(
             _ptr(self.codes) or None, _ptr(self.absmax) or None,
             _ptr(self.scale_codes) if self.double_quant else None,
             _ptr(self.group_absmax) if self.double_quant else None,
-            self.rows, self.cols, nf4_config(64, int(self.double_quant), self.dq_group))
+            self.rows, self.cols, nf4_config(self.block_size, int(self.double_quant), self.dq_group))
 
 
-def nf4_quantize(W, double_quant: bool, dq_group: int = 256, stream=None) -> NF4Weight:
-    """Quantize a contiguous fp32 CUDA tensor [rows, cols]."""
+def nf4_quantize(W, double_quant: bool, dq_group: int = 256, block_size: int = 64, stream=None) -> NF4Weight:
+    """Quantize a contiguous fp32 CUDA tensor [rows, cols] in blocks of 64 or 128."""
     import torch
 
     rows, cols = W.shape
     n = rows * cols
     dev = W.device
-    nb = n // 64
+    nb = n // block_size
     codes = torch.empty(max(n // 2, 16), dtype=torch.uint8, device=dev)
     absmax = torch.empty(max(nb, 4), dtype=torch.float32, device=dev)
     sc = gab = None
     if double_quant:
         sc = torch.empty(max(nb, 16), dtype=torch.int8, device=dev)
         gab = torch.empty(max((nb + dq_group - 1) // dq_group, 4), dtype=torch.float32, device=dev)
-    cfg = nf4_config(64, int(double_quant), dq_group)
+    cfg = nf4_config(block_size, int(double_quant), dq_group)
     _check(_lib.nf4_quantize(_ptr(W), rows, cols, C.byref(cfg), _ptr(codes), _ptr(absmax),
                              _ptr(sc), _ptr(gab), _stream(stream)), "nf4_quantize")
     return NF4Weight(codes[: n // 2], absmax[:nb], None if sc is None else sc[:nb],
                      None if gab is None else gab[: (nb + dq_group - 1) // dq_group],
-                     rows, cols, double_quant, dq_group)
+                     rows, cols, double_quant, dq_group, block_size)
 
 
 def nf4_dequantize(w: NF4Weight, stream=None):
@@ -249,7 +256,7 @@ def qlora_linear_forward(w: NF4Weight, x, A, B, scale: float, want_u: bool = Fal
     r = 0 if A is None else A.shape[0]
     h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
     u = torch.empty((M, r), dtype=torch.float32, device=x.device) if (want_u and r) else None
-    need = qlora_workspace_bytes(QLORA_OP_FORWARD, w.rows, w.cols, M, r)
+    need = qlora_workspace_bytes(QLORA_OP_FORWARD | w.op_flags, w.rows, w.cols, M, r)
     if ws is None:
         ws = _workspace(need, x.device)
     t = w.c_struct()
@@ -267,7 +274,7 @@ def qlora_linear_forward_multi(w: NF4Weight, x, A_bank, B_bank, scales, ids, ws=
     M = x.shape[0]
     n, r = A_bank.shape[0], A_bank.shape[1]
     h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
-    need = qlora_workspace_bytes(QLORA_OP_FORWARD_MULTI, w.rows, w.cols, M, r, n)
+    need = qlora_workspace_bytes(QLORA_OP_FORWARD_MULTI | w.op_flags, w.rows, w.cols, M, r, n)
     if ws is None:
         ws = _workspace(need, x.device)
     t = w.c_struct()
@@ -288,7 +295,7 @@ def qlora_linear_backward(w: NF4Weight, x, dH, A, B, scale: float, u=None, want_
     dX = torch.empty((M, w.cols), dtype=torch.bfloat16, device=dev) if want_dx else None
     dA = torch.empty((r, w.cols), dtype=torch.float32, device=dev)
     dB = torch.empty((w.rows, r), dtype=torch.float32, device=dev)
-    need = qlora_workspace_bytes(QLORA_OP_BACKWARD, w.rows, w.cols, M, r)
+    need = qlora_workspace_bytes(QLORA_OP_BACKWARD | w.op_flags, w.rows, w.cols, M, r)
     if ws is None:
         ws = _workspace(need, dev)
     t = w.c_struct()

@@ -6,8 +6,9 @@
  *     h = Wb x + (alpha/r) B (A x),        Wb = bf16( s~_b * NF4[code] )
  *
  * whose frozen base weight is stored as 4-bit NormalFloat codes in blocks of
- * 64 elements, each block with an absmax scale that may itself be quantized
- * to int8 ("double quantization").  Sources, by page title and section:
+ * 64 (or 128) elements, each block with an absmax scale that may itself be
+ * quantized to int8 ("double quantization").  Sources, by page title and
+ * section:
  *
  *  [P1] "QLoRA Finetuner", sections "1. Low-Rank Adaptation (LoRA)" (forward
  *       h = W0 x + (alpha/r) B(A x)) and "2. Block-by-Block NormalFloat4 (NF4)
@@ -20,6 +21,7 @@
  *       quantization" (scales divided by their absmax, times 127, rounded to
  *       int8), "The LoRA adapter path" (layout x W^T, (x A^T) B^T * scale; the
  *       dequantized weight is cast to bfloat16 and receives no gradient),
+ *       "The quantization backbone" (blocks of 64 or 128 weights),
  *       "Common misconceptions" (the 16 NF4 levels), "Paged optimizers" (the
  *       Adam moments of the adapters paged to host memory), "Merging and deploying"
  *       (the adapter fused into a standalone 16-bit model).
@@ -27,7 +29,8 @@
  *       adapters into the base weights (W_new = W + (alpha/r) B A).
  *  [P5] "Parameter-Efficient Fine-Tuning: From LoRA to QLoRA", "Pillar 1"
  *       (level table, worked example, two codes per byte, first element in
- *       the high nibble), "Pillar 2" (8-bit scales in groups of 256), "The
+ *       the high nibble), "Block-Wise (Chunking) Quantization" (block size
+ *       64 or 128), "Pillar 2" (8-bit scales in groups of 256), "The
  *       Real-World Bottleneck" (one resident base, adapter chosen per request).
  *
  * Conventions shared by every call:
@@ -61,7 +64,7 @@ enum {
     NF4_OK = 0,
     NF4_EINVAL = 1,        /* null pointer, negative size, r outside [0, 256], bad scale */
     NF4_ESHAPE = 2,        /* rows*cols not a multiple of the block; linear calls: cols % 64 != 0 */
-    NF4_EUNSUPPORTED = 3,  /* block_size != 64, dq_group < 1 */
+    NF4_EUNSUPPORTED = 3,  /* block_size not 64 or 128, dq_group < 1 */
     NF4_EWORKSPACE = 4,    /* workspace pointer NULL or smaller than qlora_workspace_bytes() */
     NF4_ELAUNCH = 5        /* a HIP launch failed; see nf4_last_hip_error() */
 };
@@ -69,7 +72,8 @@ enum {
 /* Quantization settings [P2 "Hyperparameters"].  The quant type is NF4 and
  * the compute dtype bf16; both are fixed. */
 typedef struct nf4_config {
-    int32_t block_size;    /* elements per block; must be 64 [P1 section 2] */
+    int32_t block_size;    /* elements per block: 64 [P1 section 2] or 128 [P3 "The quantization
+                              backbone"; P5 "Block-Wise (Chunking) Quantization"] */
     int32_t double_quant;  /* 0: fp32 block scales; 1: int8 scale codes + fp32 group constants */
     int32_t dq_group;      /* blocks per second-level group, >= 1 (256 [P5 Pillar 2]);
                               dq_group >= number of blocks gives one global constant [P3] */
@@ -79,8 +83,8 @@ typedef struct nf4_config {
  *  codes:        rows*cols/2 bytes; element e of the row-major flattening is
  *                the high nibble of byte e/2 when e is even, the low nibble
  *                when e is odd [P5 "Pillar 1", byte packing].
- *  absmax:       rows*cols/64 fp32 block scales (read when double_quant == 0).
- *  scale_codes:  rows*cols/64 int8 codes q_b in [0, 127] (double_quant == 1).
+ *  absmax:       rows*cols/block_size fp32 block scales (read when double_quant == 0).
+ *  scale_codes:  rows*cols/block_size int8 codes q_b in [0, 127] (double_quant == 1).
  *  group_absmax: ceil(nblocks/dq_group) fp32 group constants c_g (double_quant == 1).
  * The scale used for block b is s_b, or fl32(fl32(q_b/127) * c_g) with
  * g = b / dq_group (the operation-by-operation inverse of the quantizer). */
@@ -112,7 +116,8 @@ int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg,
                       size_t* code_bytes, size_t* scale_bytes, size_t* group_bytes);
 
 /* Quantize W (fp32 [rows, cols], device) [P1 section 2; P5 "Pillar 1"]:
- * per contiguous 64-element block of the row-major flattening,
+ * per contiguous block of block_size (64 or 128) elements of the row-major
+ * flattening,
  *   s_b = max |w|, w' = fl32(w / s_b), code = nearest NF4 level to w'
  *   (an exact tie goes to the lower level; an all-zero block gets code 7).
  * Writes `codes` and `absmax` (always).  With double quant [P3 "Double
@@ -120,7 +125,8 @@ int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg,
  *   c_g = max s_b,  q_b = round_half_even(fl32(fl32(s_b / c_g) * 127))
  * (q_b = 0 when c_g = 0) into scale_codes and group_absmax, which must then be
  * non-NULL.  Errors: NF4_EINVAL (NULL pointer, negative size), NF4_ESHAPE
- * (rows*cols % 64 != 0), NF4_EUNSUPPORTED (block_size != 64, dq_group < 1). */
+ * (rows*cols % block_size != 0), NF4_EUNSUPPORTED (block_size not 64 or 128,
+ * dq_group < 1). */
 int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* cfg,
                  uint8_t* codes, float* absmax, int8_t* scale_codes, float* group_absmax,
                  void* stream);
@@ -132,8 +138,13 @@ int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream);
  * LoRA adapter path" casts the dequantized weight to bfloat16]. */
 int nf4_dequantize_bf16(const nf4_tensor* W, uint16_t* W_out, void* stream);
 
-/* Workspace sizes for the layer calls (bytes; 0 means none is needed). */
-enum { QLORA_OP_FORWARD = 1, QLORA_OP_BACKWARD = 2, QLORA_OP_FORWARD_MULTI = 3 };
+/* Workspace sizes for the layer calls (bytes; 0 means none is needed).  For
+ * a weight with 128-element blocks OR QLORA_OP_BLOCK128 into `op`: the call
+ * then also keeps one fp32 scale per 64-element half-block (rows*cols/16
+ * bytes, rounded up to 256) at the front of the workspace, and the kernels
+ * of the 64-element layout run on it (every weight is dequantized to the
+ * same value). */
+enum { QLORA_OP_FORWARD = 1, QLORA_OP_BACKWARD = 2, QLORA_OP_FORWARD_MULTI = 3, QLORA_OP_BLOCK128 = 0x100 };
 size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
                              int32_t n_adapters);
 

@@ -76,8 +76,10 @@ def test_quantize_argument_errors(F):
     assert q(FAKE, 64, 64, None, FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
     assert q(FAKE, -1, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
     assert q(FAKE, 3, 5, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_ESHAPE
-    bad = _cfg(F, bs=128)
+    bad = _cfg(F, bs=96)
     assert q(FAKE, 64, 64, C.byref(bad), FAKE, FAKE, FAKE, FAKE) == F.NF4_EUNSUPPORTED
+    b128 = _cfg(F, bs=128)
+    assert q(FAKE, 3, 64, C.byref(b128), FAKE, FAKE, FAKE, FAKE) == F.NF4_ESHAPE  # 192 elements: a partial block
     bad = _cfg(F, g=0)
     assert q(FAKE, 64, 64, C.byref(bad), FAKE, FAKE, FAKE, FAKE) == F.NF4_EUNSUPPORTED
     assert q(FAKE, 64, 64, C.byref(cfg), FAKE, FAKE, None, FAKE) == F.NF4_EINVAL  # DQ needs its outputs
@@ -130,6 +132,28 @@ def test_dequantize_argument_errors(F):
     assert lib.nf4_dequantize(C.byref(t), None, None) == F.NF4_EINVAL
     t = F.nf4_tensor(FAKE, None, None, None, 2, 64, F.nf4_config(64, 0, 256))
     assert lib.nf4_dequantize_bf16(C.byref(t), FAKE, None) == F.NF4_EINVAL  # no-DQ needs absmax
+
+
+def test_block128_layer_calls(F):
+    """A 128-element-block weight: the layer calls keep one fp32 scale per
+    64-element half-block at the front of the workspace, so the workspace
+    query with the flag is larger by exactly that (rounded to 256 bytes), and
+    a call given only the 64-block size is refused."""
+    lib = F._lib
+    for op in (F.QLORA_OP_FORWARD, F.QLORA_OP_BACKWARD):
+        base = F.qlora_workspace_bytes(op, 128, 256, 600, 8)
+        flagged = F.qlora_workspace_bytes(op | F.QLORA_OP_BLOCK128, 128, 256, 600, 8)
+        assert flagged == base + (128 * 256 // 16 + 255) // 256 * 256
+    base = F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 128, 256, 1, 0)
+    assert F.qlora_workspace_bytes(F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128, 128, 256, 1, 0) == base + 2048
+    t = _tensor(F, bs=128)
+    fwd = lambda ws, wsb: lib.qlora_linear_forward(C.byref(t), FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, None, ws, wsb, None)
+    assert fwd(FAKE, 1024) == F.NF4_EWORKSPACE  # the expansion alone needs 2048 bytes
+    assert fwd(None, 1 << 20) == F.NF4_EWORKSPACE
+    # a linear call on 128-blocks that straddle rows is fine (cols % 64 == 0),
+    # a tensor that is not a whole number of blocks is not
+    t2 = _tensor(F, rows=3, cols=64, bs=128)
+    assert lib.qlora_linear_forward(C.byref(t2), FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, None, FAKE, 1 << 20, None) == F.NF4_ESHAPE
 
 
 def test_workspace_sizes_are_monotone(F):

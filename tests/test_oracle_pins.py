@@ -268,6 +268,61 @@ def test_double_quant_rounds_half_to_even():
     assert q.tolist() == [0, 2, 4, 6, 127]
 
 
+# -------------------------------------------- blocks of 128 (the pages allow 64 or 128)
+def test_block128_codes_by_exact_argmin():
+    """Blocks of 128 contiguous elements of the row-major flattening ("QLoRA
+    explained", "The quantization backbone"; "From LoRA to QLoRA",
+    "Block-Wise (Chunking) Quantization"): each block's absmax divides its
+    own 128 elements, checked against exact rational arithmetic."""
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((3, 128)) * 0.03).astype(np.float32)
+    codes, sc = O.quantize_first_level(w, 128)
+    assert codes.shape == (384,) and sc.shape == (3,)
+    codes = codes.reshape(3, 128)
+    for b in range(3):
+        blk = w[b]
+        m = np.float32(np.max(np.abs(blk)))
+        assert sc[b] == m
+        for j in range(128):
+            wn = _f32_from_fraction(Fraction(float(blk[j])) / Fraction(float(m)))
+            assert codes[b, j] == _exact_code(wn)
+
+
+def test_block128_equals_block64_when_halves_share_the_absmax():
+    """If both 64-element halves of every 128-block hold the block's absmax,
+    quantizing in blocks of 128 or of 64 gives the same codes, scales that
+    repeat pairwise, and (with second-level groups covering the same
+    elements) the same scale codes and group constants."""
+    rng = np.random.default_rng(22)
+    w = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    blocks = w.reshape(-1, 128)
+    m = np.max(np.abs(blocks), axis=1)
+    blocks[:, 5] = m
+    blocks[:, 64 + 9] = -m
+    w = blocks.reshape(w.shape)
+    a = O.quantize(w, double_quant=False, block_size=128)
+    b = O.quantize(w, double_quant=False, block_size=64)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(np.repeat(a["absmax"], 2), b["absmax"])
+    a = O.quantize(w, double_quant=True, block_size=128, dq_group=8)
+    b = O.quantize(w, double_quant=True, block_size=64, dq_group=16)
+    np.testing.assert_array_equal(np.repeat(a["scale_codes"], 2), b["scale_codes"])
+    np.testing.assert_array_equal(a["group_absmax"], b["group_absmax"])
+    np.testing.assert_array_equal(O.dequantize(a, w.shape, block_size=128, dq_group=8),
+                                  O.dequantize(b, w.shape, block_size=64, dq_group=16))
+
+
+def test_block128_storage_closed_form():
+    """4 bits per code plus one fp32 scale per 128 weights (0.25 bit), or one
+    int8 scale per 128 weights and one fp32 constant per 256 blocks."""
+    n = 128 * 256 * 10
+    cb, sb, gb = O.storage_bytes(n, double_quant=False, block_size=128)
+    assert (cb, sb, gb) == (n // 2, 4 * n // 128, 0)
+    cb, sb, gb = O.storage_bytes(n, double_quant=True, block_size=128)
+    assert (cb, sb, gb) == (n // 2, n // 128, 4 * 10)
+    assert 8 * (sb + gb) / n == 8 / 128 + 32 / (128 * 256)
+
+
 def test_storage_accounting_matches_the_pages():
     g = _load("accounting.json")["double_quant"]
     n = 64 * 256 * 100

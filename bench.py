@@ -155,7 +155,7 @@ def main():
     ap.add_argument("--workload", default="70b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "decode_bwd", "train", "copy"], default=None,
+    ap.add_argument("--only", choices=["decode", "decode_bwd", "train", "multi", "copy"], default=None,
                     help="profile one pass only (no JSON line); 'copy' runs a plain 512 MiB "
                          "device-to-device copy, the calibration for HBM byte counters")
     args = ap.parse_args()
@@ -302,7 +302,8 @@ def main():
     # whole-step timing (no hook), then the dominant kernel with the hook
     K, W = args.steps, args.warmup
     if args.only:
-        step = {"decode": decode_step, "decode_bwd": decode_bwd_step, "train": train_step}[args.only]
+        step = {"decode": decode_step, "decode_bwd": decode_bwd_step, "train": train_step,
+                "multi": multi_step}[args.only]
         t, _ = timed(step, K, W)
         print("%s pass: %.4f ms/step over %d steps" % (args.only, t, K), flush=True)
         return

@@ -543,15 +543,32 @@ int zero_f32(float* p, int64_t n, hipStream_t st) {
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
+// Workspace of the multi-adapter forward: su [M][r] fp32, the token buckets
+// (when used), then the fp32 block scales and split partials of the
+// register-dequant kernel (when used).
+struct MultiWs {
+    size_t sort, sc, part, total;
+};
+MultiWs multi_ws_offsets(int64_t rows, int64_t cols, int64_t M, int r, int n) {
+    MultiWs w{};
+    size_t o = align256(size_t(M) * (r > 0 ? r : 0) * 4);
+    w.sort = o;
+    if (nf4::use_multi_sort(M, n, r)) o += nf4::multi_sort_bytes(M, n > 0 ? n : 0);
+    w.sc = o;
+    if (nf4::use_rd_grid(M, rows)) {
+        o += align256(nf4::rd_scales_bytes(rows, cols));
+        w.part = o;
+        o += nf4::fwd_multi_part_bytes(M, rows, cols);
+    }
+    w.total = o;
+    return w;
+}
+
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters) {
     if (op == QLORA_OP_FORWARD) return plan_forward(rows, cols, M, r).total;
     if (op == QLORA_OP_BACKWARD) return plan_backward(rows, cols, M, r).total;
-    if (op == QLORA_OP_FORWARD_MULTI)  // su, then the fp32 block scales of the register-dequant kernel
-        return align256(size_t(M) * (r > 0 ? r : 0) * 4) +
-               (nf4::use_rd_grid(M, rows)
-                    ? align256(nf4::rd_scales_bytes(rows, cols)) + nf4::fwd_multi_part_bytes(M, rows, cols)
-                    : 0);
-    (void)n_adapters;
+    if (op == QLORA_OP_FORWARD_MULTI)  // su, the token buckets, the fp32 block scales and partials of the
+        return multi_ws_offsets(rows, cols, M, r, n_adapters).total;  // register-dequant kernel
     return 0;
 }
 
@@ -674,18 +691,24 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
 int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* Ab,
                        const uint16_t* Bb, int n, int r, const float* scales, const int32_t* ids,
                        uint16_t* h, void* ws, size_t ws_bytes, hipStream_t st) {
-    const size_t need = workspace_bytes(QLORA_OP_FORWARD_MULTI, q.rows, q.cols, M, r, n);
-    if (ws_bytes < need || !ws) return NF4_EWORKSPACE;
-    float* su = static_cast<float*>(ws);
-    hipLaunchKernelGGL(k_multi_down, dim3(unsigned(M)), dim3(256), 0, st, x, q.cols, Ab, n, r,
-                       scales, ids, su);
-    if (hipPeekAtLastError() != hipSuccess) return launch_status();
-    if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0) && al16(Bb) && al16(ws))
-    {
-        char* sc = static_cast<char*>(ws) + align256(size_t(M) * r * 4);
-        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h, reinterpret_cast<float*>(sc),
-                                reinterpret_cast<float*>(sc + align256(rd_scales_bytes(q.rows, q.cols))), st);
+    const MultiWs lay = multi_ws_offsets(q.rows, q.cols, M, r, n);
+    if (ws_bytes < lay.total || !ws) return NF4_EWORKSPACE;
+    char* w = static_cast<char*>(ws);
+    float* su = reinterpret_cast<float*>(w);
+    MultiSort ms{};
+    const bool sorted = use_multi_sort(M, n, r) && al16(ws);
+    int rc;
+    if (sorted) {  // tokens bucketed by adapter: each adapter's A read once per 16 tokens
+        if ((rc = multi_sort(ids, M, n, w + lay.sort, &ms, st))) return rc;
+        if ((rc = multi_down_seg(ms, x, q.cols, Ab, r, scales, su, st))) return rc;
+    } else {
+        hipLaunchKernelGGL(k_multi_down, dim3(unsigned(M)), dim3(256), 0, st, x, q.cols, Ab, n, r,
+                           scales, ids, su);
+        if (hipPeekAtLastError() != hipSuccess) return launch_status();
     }
+    if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0) && al16(Bb) && al16(ws))
+        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h, reinterpret_cast<float*>(w + lay.sc),
+                                reinterpret_cast<float*>(w + lay.part), sorted ? &ms : nullptr, st);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     return gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
                 OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1, true);

@@ -1054,7 +1054,7 @@ size_t fwd_multi_part_bytes(int64_t M, int64_t rows, int64_t cols) {
 
 int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
                      const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, float* part_ws,
-                     hipStream_t st) {
+                     const MultiSort* ms, hipStream_t st) {
     const float* scales;
     int rc = block_scales(q, scale_ws, &scales, st);
     if (rc) return rc;
@@ -1067,6 +1067,7 @@ int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* 
     launch_dominant(k_fwd_rd<true>, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (Z > 1) {
+        if (ms) return multi_fin_seg(*ms, part_ws, Z, M, q.rows, su, r, Bb, h, st);
         hipLaunchKernelGGL(k_multi_fin, dim3(unsigned(std::min<int64_t>(cdiv(M * q.rows, 256), 8192))), dim3(256), 0,
                            st, a, Z);
         if (hipPeekAtLastError() != hipSuccess) return launch_status();

@@ -108,7 +108,26 @@ bool use_rd_grid(int64_t M, int64_t N);
 size_t fwd_multi_part_bytes(int64_t M, int64_t rows, int64_t cols);
 int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
                      const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, float* part_ws,
-                     hipStream_t st);
+                     const struct MultiSort* ms, hipStream_t st);
+// Multi-adapter tokens bucketed by adapter id (multi.hip): bucket order,
+// bucket and segment offsets (segments of up to 16 tokens of one bucket).
+constexpr int kMultiSortMaxAdapters = 4096;
+struct MultiSort {
+    int32_t* perm;  // [M] token indices in bucket order
+    int32_t* off;   // [n_ad + 2] first position of each bucket (bucket n_ad: invalid ids)
+    int32_t* seg;   // [n_ad + 2] first segment of each bucket
+    int n_ad;
+    int bound;      // an upper bound on the number of segments (the launch grid)
+};
+bool use_multi_sort(int64_t M, int n_ad, int r);
+size_t multi_sort_bytes(int64_t M, int n_ad);
+int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms, hipStream_t st);
+// su[t] = s_id x_t A_id^T for every token of a valid id (r <= 64, K % 32 == 0)
+int multi_down_seg(const MultiSort& ms, const uint16_t* x, int64_t K, const uint16_t* Ab, int r,
+                   const float* scales, float* su, hipStream_t st);
+// h = bf16(the Z partials [Z][M][N] summed in order + the gathered term)
+int multi_fin_seg(const MultiSort& ms, const float* part, int Z, int64_t M, int64_t N, const float* su, int r,
+                  const uint16_t* Bb, uint16_t* h, hipStream_t st);
 bool use_dx_rd(const QView& q, int64_t M, int r, int KL);
 size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols);
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,

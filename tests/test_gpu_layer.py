@@ -241,6 +241,30 @@ def test_multi_adapter_large_tiles(F, M, out, inp, r, n):
     U.assert_close("h", U.bf16_to_f64(h), href)
 
 
+@pytest.mark.parametrize("n,r", [(5000, 2), (3, 80)])
+def test_multi_adapter_unbucketed(F, n, r):
+    """More adapters than the token bucketing takes (4096), or r > 64: the
+    per-token down-projection and gather."""
+    import torch
+
+    rng = np.random.default_rng(n + r)
+    out, inp, M = 320, 256, 600
+    w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
+    x = _bits(rng, (M, inp), 1.0)
+    ab = _bits(rng, (n, r, inp), 0.05)
+    bb = _bits(rng, (n, out, r), 0.05)
+    scales = (2.0 ** rng.integers(-2, 3, size=n)).astype(np.float32)
+    ids = rng.integers(-1, n + 1, size=M).astype(np.int32)
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    h = F.qlora_linear_forward_multi(q, U.bf(x), U.bf(ab), U.bf(bb),
+                                     torch.from_numpy(scales).to(U.dev()),
+                                     torch.from_numpy(ids).to(U.dev()))
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    href = O.forward_multi(wb, x, ab, bb, scales.astype(np.float64), ids)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+
+
 def test_multi_adapter_workload(F):
     """64 adapters, r = 16, 2048 tokens with uniform ids on the 4096 x 4096 base."""
     import torch

@@ -342,6 +342,39 @@ __global__ __launch_bounds__(256) void k_fin_u(const float* __restrict__ part, i
     }
 }
 
+// k_fin_u (the first gu workgroups) and, in the same launch, the fp32 block
+// scales fl32(fl32(q_b/127) * c_g) of a double-quantized weight for the
+// register-dequant GEMM: two independent passes, one launch.
+template <bool GSH>
+__global__ __launch_bounds__(256) void k_fin_u_bs(const float* __restrict__ part, int Z, int64_t M, int r, int KL,
+                                                  float scale, float* __restrict__ u, uint16_t* __restrict__ ext,
+                                                  int gu, nf4::QView q, int64_t nbk, float* __restrict__ sc) {
+    if (int(blockIdx.x) < gu) {
+        const int64_t n = M * KL;
+        for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gu) * 256) {
+            const int64_t m = i / KL;
+            const int c = int(i - m * KL);
+            if (c < r) {
+                float a = 0.0f;
+                for (int z = 0; z < Z; ++z) a += part[(int64_t(z) * M + m) * r + c];
+                u[m * r + c] = a;
+                uint16_t h, l;
+                split_bf16(__fmul_rn(scale, a), h, l);
+                ext[i] = h;
+                ext[i + r] = l;
+            } else if (c >= 2 * r) {
+                ext[i] = 0;
+            }
+        }
+        return;
+    }
+    const int64_t stride = int64_t(gridDim.x - gu) * 256;
+    for (int64_t k = int64_t(blockIdx.x - gu) * 256 + threadIdx.x; k < nbk; k += stride) {
+        const int64_t g = GSH ? (k >> q.gshift) : (k / q.group);
+        sc[k] = __fmul_rn(q_over_127(q.qcodes[k]), q.gabs[g]);
+    }
+}
+
 // From v [M][r] fp32: ext [M][KL] = (bf16 hi of scale*v | bf16 lo | 0 pad),
 // and optionally hi/lo [M][r] of v itself.
 __global__ __launch_bounds__(256) void k_splits(const float* __restrict__ v, int64_t M, int r, int KL,
@@ -459,8 +492,8 @@ struct BwdPlan {
     FwdPlan f;       // recompute of u when it is not supplied
     int Zdu, Zdb, Zda;
     bool skinny;     // r <= 64: the lora_bwd.hip products
-    size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, off_sc,
-        off_dxv, off_dxp, total;
+    size_t off_uh, off_ul, off_du, off_duext, off_duh, off_dul, off_bt, off_uq, off_duq, off_part, off_part_a,
+        off_sc, off_dxv, off_dxp, total;
 };
 
 BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
@@ -488,8 +521,12 @@ BwdPlan plan_backward(int64_t rows, int64_t cols, int64_t M, int r) {
     }
     size_t part = size_t(p.Zdu) * M * r;
     if (size_t(p.Zdb) * rows * r > part) part = size_t(p.Zdb) * rows * r;
-    if (size_t(p.Zda) * r * cols > part) part = size_t(p.Zda) * r * cols;
+    if (!p.skinny && size_t(p.Zda) * r * cols > part) part = size_t(p.Zda) * r * cols;
     p.off_part = o; o = nf4::align256(o + part * 4);
+    if (p.skinny) {  // dA partials apart, so that one launch reduces dB and dA
+        p.off_part_a = o;
+        o = nf4::align256(o + size_t(p.Zda) * r * cols * 4);
+    }
     if (!nf4::use_bwd_small(rows, cols, M) &&
         nf4::cdiv(M, 256) * nf4::cdiv(cols, 256) >= 16) {  // register-dequant dX: fp32 block scales,
         p.off_sc = o;                                       // split partials
@@ -515,9 +552,11 @@ unsigned ew_grid(int64_t n) {
 
 // u = x A^T (fp32 [M][r]) into u (split-K through `part`), then the bf16
 // hi/lo extension of scale*u into ext.
+// u = x A^T and its extension; with `bs` non-null also the fp32 block
+// scales of the double-quantized q into bs, in the same launch as u's end.
 int down_projection(hipStream_t st, const nf4::QView& q, const uint16_t* x, int64_t M,
                     const uint16_t* A, int r, float scale, const FwdPlan& fp, char* ws, float* u,
-                    uint16_t* ext) {
+                    uint16_t* ext, float* bs = nullptr) {
     float* part = reinterpret_cast<float*>(ws + fp.off_part);
     int rc;
     if (r <= 64) {
@@ -528,8 +567,20 @@ int down_projection(hipStream_t st, const nf4::QView& q, const uint16_t* x, int6
         rc = gemm(st, M, r, lx, la, q.cols, LdNone{}, LdNone{}, 0, OutPartial{part, M, r}, fp.Zu);
     }
     if (rc) return rc;
-    hipLaunchKernelGGL(k_fin_u, dim3(ew_grid(M * ext_cols(r))), dim3(256), 0, st, part, fp.Zu, M, r,
-                       ext_cols(r), scale, u, ext);
+    if (bs && q.dq) {
+        const int gu = int(ew_grid(M * ext_cols(r)));
+        const int64_t nbk = q.rows * q.cols / 64;
+        const dim3 grid = dim3(unsigned(gu + std::min<int64_t>(nf4::cdiv(nbk, 256), 4096)));
+        if (q.gshift >= 0)
+            hipLaunchKernelGGL(k_fin_u_bs<true>, grid, dim3(256), 0, st, part, fp.Zu, M, r, ext_cols(r), scale, u,
+                               ext, gu, q, nbk, bs);
+        else
+            hipLaunchKernelGGL(k_fin_u_bs<false>, grid, dim3(256), 0, st, part, fp.Zu, M, r, ext_cols(r), scale, u,
+                               ext, gu, q, nbk, bs);
+    } else {
+        hipLaunchKernelGGL(k_fin_u, dim3(ew_grid(M * ext_cols(r))), dim3(256), 0, st, part, fp.Zu, M, r,
+                           ext_cols(r), scale, u, ext);
+    }
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : nf4::launch_status();
 }
 
@@ -591,11 +642,18 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     }
     float* u = u_out ? u_out : reinterpret_cast<float*>(w + fp.off_u);
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
-    int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext);
+    const bool rd = use_rd_grid(M, q.rows) && use_rd(q, M, r, ext_cols(r));
+    float* scw = rd ? reinterpret_cast<float*>(w + fp.off_sc) : nullptr;
+    int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext, scw);
     if (rc) return rc;
-    if (use_rd_grid(M, q.rows) && use_rd(q, M, r, ext_cols(r)))
-        return forward_rd(q, x, M, ext, ext_cols(r), B, r, h, reinterpret_cast<float*>(w + fp.off_sc),
-                          reinterpret_cast<float*>(w + fp.off_tail), st);
+    if (rd) {  // the block scales are decoded: the GEMM sees plain fp32 scales
+        QView qv = q;
+        if (q.dq) {
+            qv.dq = 0;
+            qv.absmax = scw;
+        }
+        return forward_rd(qv, x, M, ext, ext_cols(r), B, r, h, scw, reinterpret_cast<float*>(w + fp.off_tail), st);
+    }
     if (use_big_gemm(M, q.rows)) return forward_big(q, x, M, ext, ext_cols(r), B, r, h, st);
     LdRowMajor le{ext, M, ext_cols(r), ext_cols(r), true};
     LdDupRows lb{B, q.rows, r};
@@ -629,21 +687,27 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     float* part = reinterpret_cast<float*>(w + bp.off_part);
     if (use_bwd_small(out, in, M))
         return backward_small(q, x, dH, M, A, r, B, scale, u, dX, dA, dB, w + bp.off_dxv, st);
+    float* dx_rd_scales = (bp.skinny && dX && q.dq && use_dx_rd(q, M, r, KL))
+                              ? reinterpret_cast<float*>(w + bp.off_sc) : nullptr;
     const bool dh_vec = al16(dH) && (out % 8 == 0);
     if (bp.skinny) {
         uint16_t* bt = reinterpret_cast<uint16_t*>(w + bp.off_bt);
         uint16_t* uq = reinterpret_cast<uint16_t*>(w + bp.off_uq);
         uint16_t* duq = reinterpret_cast<uint16_t*>(w + bp.off_duq);
-        // dU = s dH B (B^T made contiguous along out first)
-        if ((rc = transpose16(st, B, out, r, bt))) return rc;
+        // dU = s dH B (B^T made contiguous along out first; the block scales of
+        // the register-dequant dX product decoded in the same launch)
+        if (dx_rd_scales) {
+            if ((rc = transpose_bs(st, B, out, r, bt, q, dx_rd_scales))) return rc;
+        } else if ((rc = transpose16(st, B, out, r, bt))) {
+            return rc;
+        }
         if ((rc = nt_product(st, dH, M, out, bt, r, bp.Zdu, part))) return rc;
         if ((rc = fin_du(st, part, bp.Zdu, M, r, KL, scale, u, duext, duq, uq))) return rc;
         // dB = s dH^T u, dA = dU^T x: reductions over the tokens
+        float* part_a = reinterpret_cast<float*>(w + bp.off_part_a);
         if ((rc = tn_product(st, dH, M, out, uq, r, bp.Zdb, part))) return rc;
-        hipLaunchKernelGGL(k_reduce, dim3(ew_grid(out * r)), dim3(256), 0, st, part, bp.Zdb, out * r, scale, dB);
-        if (hipPeekAtLastError() != hipSuccess) return launch_status();
-        if ((rc = tn_product(st, x, M, in, duq, r, bp.Zda, part))) return rc;
-        if ((rc = reduce_t(st, part, bp.Zda, in, r, 1.0f, dA))) return rc;
+        if ((rc = tn_product(st, x, M, in, duq, r, bp.Zda, part_a))) return rc;
+        if ((rc = reduce_pair(st, part, bp.Zdb, out * r, scale, dB, part_a, bp.Zda, in, r, 1.0f, dA))) return rc;
     } else {
     hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * r)), dim3(256), 0, st, u, M, r, r, 1.0f,
                        (uint16_t*)nullptr, uh, ul);
@@ -674,9 +738,15 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     }
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
-        if (use_dx_rd(q, M, r, KL))
-            rc = dx_rd(q, dH, M, duext, KL, A, r, dX, reinterpret_cast<float*>(w + bp.off_sc),
+        if (use_dx_rd(q, M, r, KL)) {
+            QView qv = q;
+            if (dx_rd_scales) {  // decoded already: plain fp32 scales
+                qv.dq = 0;
+                qv.absmax = dx_rd_scales;
+            }
+            rc = dx_rd(qv, dH, M, duext, KL, A, r, dX, reinterpret_cast<float*>(w + bp.off_sc),
                        reinterpret_cast<float*>(w + bp.off_dxp), st);
+        }
         else if (use_big_gemm(M, in))
             rc = dx_big(q, dH, M, duext, KL, A, r, dX, st);
         else

@@ -302,24 +302,59 @@ __global__ __launch_bounds__(256) void k_fin_du(const float* __restrict__ part, 
     }
 }
 
+// A workgroup takes 64 rows of b (one contiguous slab of 64 r elements),
+// transposes them through LDS and writes 64 consecutive elements of each of
+// the r rows of bt.  r <= 64.
+__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ b, int64_t n, int r,
+                                               uint16_t* __restrict__ bt, int64_t bx) {
+    __shared__ uint16_t tile[64][66];
+    const int tid = threadIdx.x;
+    const int64_t o0 = bx * 64;
+    const int rows = int(n - o0 < 64 ? n - o0 : 64);
+    const uint16_t* src = b + o0 * r;
+    for (int e = tid; e < rows * r; e += 256) {
+        const int o = e / r;
+        tile[o][e - o * r] = src[e];
+    }
+    __syncthreads();
+    for (int e = tid; e < r * 64; e += 256) {
+        const int j = e >> 6, o = e & 63;
+        if (o < rows) bt[int64_t(j) * n + o0 + o] = tile[o][j];
+    }
+}
+
 __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ b, int64_t n, int r,
                                                      uint16_t* __restrict__ bt) {
-    const int64_t tot = n * r;
-    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < tot; i += int64_t(gridDim.x) * 256) {
-        const int64_t j = i / n, o = i % n;
-        bt[i] = b[o * r + j];
+    transpose_tile(b, n, r, bt, blockIdx.x);
+}
+
+// The transpose (the first gt workgroups) and, in the same launch, the fp32
+// block scales fl32(fl32(q_b/127) * c_g) of a double-quantized weight for
+// the register-dequant dX product: two independent passes, one launch.
+template <bool GSH>
+__global__ __launch_bounds__(256) void k_tr_bs(const uint16_t* __restrict__ b, int64_t n, int r,
+                                               uint16_t* __restrict__ bt, int gt, nf4::QView q, int64_t nbk,
+                                               float* __restrict__ sc) {
+    if (int(blockIdx.x) < gt) {
+        transpose_tile(b, n, r, bt, blockIdx.x);
+        return;
+    }
+    const int64_t stride = int64_t(gridDim.x - gt) * 256;
+    for (int64_t k = int64_t(blockIdx.x - gt) * 256 + threadIdx.x; k < nbk; k += stride) {
+        const int64_t g = GSH ? (k >> q.gshift) : (k / q.group);
+        sc[k] = __fmul_rn(q_over_127(q.qcodes[k]), q.gabs[g]);
     }
 }
 
 // out[j][i] = scale * sum_z part[z][i][j]  (i < n, j < r): the transposed reduce of dA
-__global__ __launch_bounds__(256) void k_reduce_t(const float* __restrict__ part, int Z, int64_t n, int r,
-                                                  float scale, float* __restrict__ out) {
+__device__ __forceinline__ void reduce_t_tile(const float* __restrict__ part, int Z, int64_t n, int r,
+                                              float scale, float* __restrict__ out, int64_t bx, int by) {
     // out[j][i] = scale * sum_z part[z][i][j]; a workgroup takes 16 i x 64 j:
     // partial rows are read along j (contiguous), summed in split order,
     // transposed through LDS and written along i
     __shared__ float tile[16][65];
-    const int64_t i0 = int64_t(blockIdx.x) * 16;
-    const int j0 = int(blockIdx.y) * 64;
+    const int64_t i0 = bx * 16;
+    const int j0 = by * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
     const int j = j0 + tx;
 #pragma unroll
@@ -344,6 +379,29 @@ __global__ __launch_bounds__(256) void k_reduce_t(const float* __restrict__ part
             const int64_t i = i0 + 4 * iq + e;
             if (i < n) out[int64_t(jo) * n + i] = tile[4 * iq + e][jj] * scale;
         }
+}
+
+__global__ __launch_bounds__(256) void k_reduce_t(const float* __restrict__ part, int Z, int64_t n, int r,
+                                                  float scale, float* __restrict__ out) {
+    reduce_t_tile(part, Z, n, r, scale, out, blockIdx.x, int(blockIdx.y));
+}
+
+// dB = sb * (the Zb partials [Zb][nb] summed in split order), in the first
+// gb workgroups, and the transposed reduce of dA in the rest: one launch.
+__global__ __launch_bounds__(256) void k_reduce_pair(const float* __restrict__ pb, int Zb, int64_t nb, float sb,
+                                                     float* __restrict__ outb, int gb,
+                                                     const float* __restrict__ pa, int Za, int64_t na, int r,
+                                                     float sa, float* __restrict__ outa) {
+    if (int(blockIdx.x) < gb) {
+        for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < nb; i += int64_t(gb) * 256) {
+            float a = 0.0f;
+            for (int z = 0; z < Zb; ++z) a += pb[int64_t(z) * nb + i];
+            outb[i] = a * sb;
+        }
+        return;
+    }
+    const int64_t t = int64_t(blockIdx.x) - gb, ti = (na + 15) / 16;
+    reduce_t_tile(pa, Za, na, r, sa, outa, t % ti, int(t / ti));
 }
 
 unsigned ew(int64_t n) { return unsigned(std::max<int64_t>(1, std::min<int64_t>(8192, (n + 255) / 256))); }
@@ -404,7 +462,30 @@ int fin_du(hipStream_t st, const float* part, int Z, int64_t M, int r, int KL, f
 }
 
 int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt) {
-    hipLaunchKernelGGL(k_transpose16, dim3(ew(n * r)), dim3(256), 0, st, b, n, r, bt);
+    if (r > 64) return NF4_EINVAL;
+    hipLaunchKernelGGL(k_transpose16, dim3(unsigned(cdiv(n, 64))), dim3(256), 0, st, b, n, r, bt);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int transpose_bs(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt, const QView& q, float* sc) {
+    if (r > 64 || !q.dq) return NF4_EINVAL;
+    const int gt = int(cdiv(n, 64));
+    const int64_t nbk = q.rows * q.cols / 64;
+    const int64_t gs = std::min<int64_t>(cdiv(nbk, 256), 4096);
+    const dim3 grid = dim3(unsigned(gt + gs));
+    if (q.gshift >= 0)
+        hipLaunchKernelGGL(k_tr_bs<true>, grid, dim3(256), 0, st, b, n, r, bt, gt, q, nbk, sc);
+    else
+        hipLaunchKernelGGL(k_tr_bs<false>, grid, dim3(256), 0, st, b, n, r, bt, gt, q, nbk, sc);
+    return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
+}
+
+int reduce_pair(hipStream_t st, const float* pb, int Zb, int64_t nb, float sb, float* outb, const float* pa, int Za,
+                int64_t na, int r, float sa, float* outa) {
+    const int gb = int(ew(nb));
+    const int64_t ga = cdiv(na, 16) * cdiv(r, 64);
+    hipLaunchKernelGGL(k_reduce_pair, dim3(unsigned(gb + ga)), dim3(256), 0, st, pb, Zb, nb, sb, outb, gb, pa, Za, na,
+                       r, sa, outa);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

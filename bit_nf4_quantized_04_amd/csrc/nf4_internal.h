@@ -147,6 +147,12 @@ int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const u
 int fin_du(hipStream_t st, const float* part, int Z, int64_t M, int r, int KL, float scale, const float* u,
            uint16_t* duext, uint16_t* duq, uint16_t* uq);
 int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt);
+// transpose16 and the fp32 block scales of a double-quantized q into sc, one launch
+int transpose_bs(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt, const QView& q, float* sc);
+// dB = sb * sum of Zb partials [Zb][nb], and dA = the transposed reduce of
+// Za partials [Za][na][r] scaled by sa, one launch
+int reduce_pair(hipStream_t st, const float* pb, int Zb, int64_t nb, float sb, float* outb, const float* pa, int Za,
+                int64_t na, int r, float sa, float* outa);
 int reduce_t(hipStream_t st, const float* part, int Z, int64_t n, int r, float scale, float* out);
 int zero_f32(float* p, int64_t n, hipStream_t s);  // fill kernel (graph-capture safe)
 size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int n_adapters);

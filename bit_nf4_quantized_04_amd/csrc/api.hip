@@ -84,10 +84,14 @@ inline bool bad_ptr(const void* p) { return !p || !al16(p); }
 }  // namespace
 
 namespace nf4 {
+namespace {
+thread_local bool g_prof_start_taken = false;
+}
 void prof_events(hipEvent_t* start, hipEvent_t* stop) {
     *start = g_prof_start;
     *stop = g_prof_stop;
 }
+bool& prof_start_taken() { return g_prof_start_taken; }
 int launch_status() {
     const hipError_t e = hipGetLastError();
     g_last_hip_error = int(e);
@@ -130,6 +134,7 @@ int nf4_profile_events(void* start, void* stop) {
     if ((start == nullptr) != (stop == nullptr)) return NF4_EINVAL;
     g_prof_start = static_cast<hipEvent_t>(start);
     g_prof_stop = static_cast<hipEvent_t>(stop);
+    nf4::prof_start_taken() = false;
     return NF4_OK;
 }
 

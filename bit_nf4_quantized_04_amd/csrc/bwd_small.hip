@@ -431,8 +431,8 @@ int backward_small(const QView& q, const uint16_t* x, const uint16_t* dH, int64_
     float* part = reinterpret_cast<float*>(ws);
     float* du = reinterpret_cast<float*>(ws + align256(size_t(M) * size_t(p.nchunk) * size_t(ps) * 4));
     // dB = s dH^T u
-    hipLaunchKernelGGL(k_bs_db, dim3(unsigned(std::min<int64_t>(cdiv(out * cdiv(r, 4), 256), 4096))), dim3(256), 0,
-                       st, dH, int(M), out, u, r, scale, dB);
+    launch_before_dominant(k_bs_db, dim3(unsigned(std::min<int64_t>(cdiv(out * cdiv(r, 4), 256), 4096))), dim3(256),
+                           0, st, dH, int(M), out, u, r, scale, dB);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     // one pass over the weight rows: dX partials (dH Wb) and dU partials (dH
     // B); without dX only the rank-r slabs run

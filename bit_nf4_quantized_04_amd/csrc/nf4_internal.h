@@ -46,18 +46,41 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
                   const uint16_t* A, const uint16_t* B, int r, float scale, const float* u,
                   uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t s);
 // Profiling hook: the caller's events (or null) that bracket the dominant
-// kernel of a call; launch_dominant attaches them to the dispatch itself.
+// kernel of a call, attached to kernel dispatches (hipExtLaunchKernelGGL).
+// The kernel launched just before the dominant one, when launched with
+// launch_before_dominant, records the start event at its end: the pair then
+// spans the dominant kernel alone, with no marker packet of its own in the
+// queue.  Otherwise both events attach to the dominant kernel's dispatch.
 void prof_events(hipEvent_t* start, hipEvent_t* stop);
+bool& prof_start_taken();  // per thread: the start event was attached to the previous kernel
+
+template <typename Kernel, typename... Args>
+void launch_before_dominant(Kernel kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                            Args... args) {
+    hipEvent_t a, b;
+    prof_events(&a, &b);
+    if (a && b) {
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, nullptr, a, 0, args...);
+        prof_start_taken() = true;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+    }
+}
 
 template <typename Kernel, typename... Args>
 void launch_dominant(Kernel kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st,
                      Args... args) {
     hipEvent_t a, b;
     prof_events(&a, &b);
-    if (a && b)
-        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, b, 0, args...);
-    else
+    if (a && b) {
+        if (prof_start_taken())
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, nullptr, b, 0, args...);
+        else
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, a, b, 0, args...);
+        prof_start_taken() = false;
+    } else {
         hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+    }
 }
 // Decode path (M <= kSkinnyMaxM, r <= kSkinnyMaxR): partial down-projection
 // kernel + fused dequant-GEMV kernel.

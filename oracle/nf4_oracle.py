@@ -26,6 +26,13 @@ Sources (cited by page title and section):
 * "How Fine-Tuning LLMs with LoRA and QLoRA Works" (instagit), FAQ on merging
   adapters into the base weights (W + (alpha/r) B A), and "QLoRA explained",
   section "Merging and deploying" (a standalone 16-bit model): ``merge``.
+* "QLoRA Finetuner", section "1. Low-Rank Adaptation (LoRA)", and the
+  adapter-branch diagram of the same page: dropout on the input of the
+  adapter branch only, h = W0 x + (alpha/r) B(A(dropout(x))); "QLoRA
+  explained" sets lora_dropout = 0.05.  The pages give no random number
+  generator: ``philox4x32_10`` is the published counter-based generator of
+  Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+  3" (SC 2011), and ``dropout_keep`` the reading stated there.
 * "QLoRA Specification for EMEP Fine-Tuning" ("GPU Orchestration": adapters
   and optimizer state in full precision), "QLoRA explained" ("Paged
   optimizers": the Adam moments of the LoRA parameters paged to host memory):
@@ -45,6 +52,8 @@ pages; it is pinned by the round-trip identities only.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -334,6 +343,85 @@ def backward64(wb, x, dh, a, b, scale: float):
 def backward(wb, x_bits, dh_bits, a_bits, b_bits, scale: float):
     """The layer backward on bf16 inputs (bit patterns); float64 results."""
     return backward64(wb, _bf(x_bits), _bf(dh_bits), _bf(a_bits), _bf(b_bits), scale)
+
+
+# ---------------------------------------------------------------------------
+# LoRA dropout on the adapter input ("QLoRA Finetuner", section 1 and its
+# adapter-branch diagram).  READING (the pages name dropout and its rate
+# only): inverted dropout, an element kept with probability 1 - p and the kept
+# ones scaled by 1/(1 - p); the keep decision of element (m, k) of x [M, in]
+# comes from Philox-4x32-10 with counter (lo, hi of m*in + k, 0, 0) and key
+# (lo, hi of the 64-bit seed): keep iff its first output word >= ceil(p 2^32).
+# ---------------------------------------------------------------------------
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers (Salmon et al. 2011)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key schedule increments (golden ratio, sqrt 3 - 1)
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox-4x32 with 10 rounds on arrays of counters [n, 4] and keys [n, 2]
+    (uint32): each round multiplies words 0 and 2 by the two multipliers into
+    64-bit products, and the new words are (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),
+    hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key advances by the two increments
+    between rounds."""
+    c = np.array(ctr, dtype=np.uint64).reshape(-1, 4)
+    k = np.array(key, dtype=np.uint64).reshape(-1, 2)
+    mask = np.uint64(0xFFFFFFFF)
+    for rnd in range(10):
+        if rnd:
+            k = (k + np.array(_PHILOX_W, dtype=np.uint64)) & mask
+        p0 = c[:, 0] * np.uint64(_PHILOX_M[0])
+        p1 = c[:, 2] * np.uint64(_PHILOX_M[1])
+        c = np.stack([(p1 >> np.uint64(32)) ^ c[:, 1] ^ k[:, 0], p1 & mask,
+                      (p0 >> np.uint64(32)) ^ c[:, 3] ^ k[:, 1], p0 & mask], axis=1)
+    return c.astype(np.uint32)
+
+
+def dropout_threshold(p: float) -> int:
+    """ceil(p 2^32) for p in [0, 1): the smallest first word that is dropped."""
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout rate must lie in [0, 1)")
+    return int(math.ceil(float(p) * 4294967296.0))
+
+
+def dropout_keep(M: int, inp: int, p: float, seed: int) -> np.ndarray:
+    """Boolean keep mask [M, inp] of the adapter-input dropout."""
+    idx = np.arange(M * inp, dtype=np.uint64)
+    ctr = np.zeros((idx.size, 4), dtype=np.uint64)
+    ctr[:, 0] = idx & np.uint64(0xFFFFFFFF)
+    ctr[:, 1] = idx >> np.uint64(32)
+    key = np.empty((idx.size, 2), dtype=np.uint64)
+    key[:, 0] = seed & 0xFFFFFFFF
+    key[:, 1] = (seed >> 32) & 0xFFFFFFFF
+    first = philox4x32_10(ctr, key)[:, 0].astype(np.uint64)
+    return (first >= np.uint64(dropout_threshold(p))).reshape(M, inp)
+
+
+def forward_dropout64(wb, x, a, b, scale: float, keep, p: float):
+    """h = x Wb^T + s (dropout(x) A^T) B^T with dropout(x) = keep * x / (1 - p)
+    (float64).  Returns (h, u) with u = dropout(x) A^T."""
+    x = np.asarray(x, dtype=np.float64)
+    xd = np.where(keep, x, 0.0) / (1.0 - p)
+    u = xd @ np.asarray(a, dtype=np.float64).T
+    h = x @ np.asarray(wb, dtype=np.float64).T + float(scale) * (u @ np.asarray(b, dtype=np.float64).T)
+    return h, u
+
+
+def backward_dropout64(wb, x, dh, a, b, scale: float, keep, p: float):
+    """Gradients of the dropout forward for upstream dH (float64): with
+    xd = dropout(x) and u = xd A^T, dU = s dH B, dB = s dH^T u, dA = dU^T xd,
+    dX = dH Wb + keep * (dU A) / (1 - p)."""
+    x = np.asarray(x, dtype=np.float64)
+    dh = np.asarray(dh, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    s = float(scale)
+    xd = np.where(keep, x, 0.0) / (1.0 - p)
+    u = xd @ a.T
+    du = s * (dh @ b)
+    db = s * (dh.T @ u)
+    da = du.T @ xd
+    dx = dh @ np.asarray(wb, dtype=np.float64) + np.where(keep, du @ a, 0.0) / (1.0 - p)
+    return {"dX": dx, "dA": da, "dB": db, "dU": du}
 
 
 def merge(wb, a_bits, b_bits, scale: float) -> np.ndarray:

@@ -323,6 +323,72 @@ def test_block128_storage_closed_form():
     assert 8 * (sb + gb) / n == 8 / 128 + 32 / (128 * 256)
 
 
+# ------------------------------------------------- adapter-input dropout
+def test_philox_known_answers():
+    """The counter-based generator behind the dropout mask reproduces the
+    known-answer vectors published with it."""
+    g = _load("philox_kat.json")
+    for v in g["vectors"]:
+        ctr = [int(h, 16) for h in v["ctr"]]
+        key = [int(h, 16) for h in v["key"]]
+        got = O.philox4x32_10([ctr], [key])[0]
+        assert ["%08x" % int(w) for w in got] == v["out"]
+
+
+def test_dropout_threshold_and_keep_rate():
+    assert O.dropout_threshold(0.0) == 0 and O.dropout_threshold(0.5) == 2 ** 31
+    assert np.all(O.dropout_keep(3, 64, 0.0, 123))
+    for p in (0.05, 0.5):
+        keep = O.dropout_keep(512, 1024, p, 7)
+        n = keep.size
+        sigma = math.sqrt(p * (1 - p) / n)
+        assert abs(keep.mean() - (1 - p)) < 6 * sigma
+    a = O.dropout_keep(8, 128, 0.3, 1)
+    assert np.array_equal(a, O.dropout_keep(8, 128, 0.3, 1))        # deterministic in the seed
+    assert not np.array_equal(a, O.dropout_keep(8, 128, 0.3, 2))    # and depends on it
+    assert np.array_equal(a[:4], O.dropout_keep(4, 128, 0.3, 1))     # element (m, k) is counter m*in + k
+
+
+def test_dropout_p0_is_the_plain_layer():
+    rng = np.random.default_rng(31)
+    M, out, inp, r = 5, 24, 64, 4
+    wb = rng.standard_normal((out, inp))
+    x, dh = rng.standard_normal((M, inp)), rng.standard_normal((M, out))
+    a, b = rng.standard_normal((r, inp)), rng.standard_normal((out, r))
+    keep = O.dropout_keep(M, inp, 0.0, 5)
+    h0, u0 = O.forward64(wb, x, a, b, 2.0)
+    h1, u1 = O.forward_dropout64(wb, x, a, b, 2.0, keep, 0.0)
+    np.testing.assert_array_equal(h0, h1)
+    np.testing.assert_array_equal(u0, u1)
+    g0 = O.backward64(wb, x, dh, a, b, 2.0)
+    g1 = O.backward_dropout64(wb, x, dh, a, b, 2.0, keep, 0.0)
+    for k in ("dX", "dA", "dB", "dU"):
+        np.testing.assert_array_equal(g0[k], g1[k])
+
+
+def test_dropout_backward_matches_finite_differences():
+    """With the mask fixed the layer is linear in x, A and B, so central
+    differences are exact up to rounding."""
+    rng = np.random.default_rng(32)
+    M, out, inp, r, p, s = 3, 7, 64, 3, 0.3, 2.0
+    wb = rng.standard_normal((out, inp))
+    x, dh = rng.standard_normal((M, inp)), rng.standard_normal((M, out))
+    a, b = rng.standard_normal((r, inp)), rng.standard_normal((out, r))
+    keep = O.dropout_keep(M, inp, p, 11)
+    assert 0 < keep.sum() < keep.size
+    g = O.backward_dropout64(wb, x, dh, a, b, s, keep, p)
+    loss = lambda xx, aa, bb: float(np.sum(dh * O.forward_dropout64(wb, xx, aa, bb, s, keep, p)[0]))
+    eps = 1e-3
+    for name, arr, fn in (("dX", x, lambda v: loss(v, a, b)), ("dA", a, lambda v: loss(x, v, b)),
+                          ("dB", b, lambda v: loss(x, a, v))):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            e = np.zeros_like(arr)
+            e[idx] = eps
+            num[idx] = (fn(arr + e) - fn(arr - e)) / (2 * eps)
+        np.testing.assert_allclose(g[name], num, rtol=1e-7, atol=1e-7)
+
+
 def test_storage_accounting_matches_the_pages():
     g = _load("accounting.json")["double_quant"]
     n = 64 * 256 * 100

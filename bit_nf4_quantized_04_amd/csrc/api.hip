@@ -190,8 +190,15 @@ int nf4_dequantize_bf16(const nf4_tensor* W, uint16_t* W_out, void* stream) {
 size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
                              int32_t n_adapters) {
     if (rows < 0 || cols < 0 || M < 0 || r < 0 || r > 256) return 0;
-    const size_t base = nf4::workspace_bytes(op & ~QLORA_OP_BLOCK128, rows, cols, M, r, n_adapters);
-    return (op & QLORA_OP_BLOCK128) ? expand_bytes(rows, cols) + base : base;
+    const size_t base = nf4::workspace_bytes(op & ~(QLORA_OP_BLOCK128 | QLORA_OP_DROPOUT), rows, cols, M, r,
+                                             n_adapters);
+    // dropout: xd bf16 [M][in]; the backward also the fp32 dH Wb [M][in]
+    const int base_op = op & ~(QLORA_OP_BLOCK128 | QLORA_OP_DROPOUT);
+    const size_t xd = (op & QLORA_OP_DROPOUT)
+                          ? (size_t(M) * size_t(cols) * 2 + 255) / 256 * 256 +
+                                (base_op == QLORA_OP_BACKWARD ? (size_t(M) * size_t(cols) * 4 + 255) / 256 * 256 : 0)
+                          : 0;
+    return ((op & QLORA_OP_BLOCK128) ? expand_bytes(rows, cols) : 0) + xd + base;
 }
 
 int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -253,6 +260,83 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
     if ((rc = layer_view(&v, &ws, &ws_bytes, static_cast<hipStream_t>(stream)))) return rc;
     return nf4::backward_impl(v, x, dH, M, A, B, r, scale, u, dX, dA, dB, ws, ws_bytes,
                               static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// The dropout settings: the keep threshold and 1/(1 - p); p in [0, 1).
+bool dropout_ok(const qlora_dropout* d) { return d && isfinite(d->p) && d->p >= 0.0f && d->p < 1.0f; }
+
+// xd = keep * x at the front of the workspace (after a block-128 expansion).
+int dropout_input(const qlora_dropout* d, const uint16_t* x, int64_t M, int64_t cols, void** ws, size_t* ws_bytes,
+                  hipStream_t st, uint16_t** xd) {
+    const size_t xb = (size_t(M) * size_t(cols) * 2 + 255) / 256 * 256;
+    if (!*ws || *ws_bytes < xb || !al16(*ws)) return NF4_EWORKSPACE;
+    *xd = static_cast<uint16_t*>(*ws);
+    const int rc = nf4::dropout_x(x, M, cols, nf4::dropout_threshold(d->p), d->seed, *xd, st);
+    if (rc) return rc;
+    *ws = static_cast<char*>(*ws) + xb;
+    *ws_bytes -= xb;
+    return NF4_OK;
+}
+
+}  // namespace
+
+int qlora_linear_forward_dropout(const nf4_tensor* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float scale, const qlora_dropout* drop,
+                                 uint16_t* h, float* u_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!dropout_ok(drop)) return NF4_EINVAL;
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (M < 0 || r < 0 || r > 256 || !isfinite(scale)) return NF4_EINVAL;
+    if (!A || !B) r = 0;
+    if (M == 0 || v.rows == 0) return NF4_OK;
+    if (bad_ptr(x) || bad_ptr(h)) return NF4_EINVAL;
+    if (r > 0 && (bad_ptr(A) || bad_ptr(B))) return NF4_EINVAL;
+    if (u_out && !al16(u_out)) return NF4_EINVAL;
+    if (v.cols == 0) return NF4_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = layer_view(&v, &ws, &ws_bytes, st))) return rc;
+    if (r == 0) return nf4::forward_impl(v, x, M, A, B, 0, scale, h, nullptr, ws, ws_bytes, st);
+    uint16_t* xd;
+    if ((rc = dropout_input(drop, x, M, v.cols, &ws, &ws_bytes, st, &xd))) return rc;
+    const float ik = float(1.0 / (1.0 - double(drop->p)));
+    if ((rc = nf4::forward_impl(v, x, M, A, B, r, scale * ik, h, u_out, ws, ws_bytes, st, xd))) return rc;
+    return u_out ? nf4::scale_f32(u_out, M * r, ik, st) : NF4_OK;
+}
+
+int qlora_linear_backward_dropout(const nf4_tensor* W, const uint16_t* x, const uint16_t* dH, int64_t M,
+                                  const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                                  const qlora_dropout* drop, const float* u, uint16_t* dX, float* dA, float* dB,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    if (!dropout_ok(drop)) return NF4_EINVAL;
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (M < 0 || r < 1 || r > 256 || !isfinite(scale)) return NF4_EINVAL;
+    if (bad_ptr(A) || bad_ptr(B) || bad_ptr(dA) || bad_ptr(dB)) return NF4_EINVAL;
+    if (v.rows == 0 || v.cols == 0) return NF4_EINVAL;
+    if (M > 0 && (bad_ptr(x) || bad_ptr(dH))) return NF4_EINVAL;
+    if (u && !al16(u)) return NF4_EINVAL;
+    if (dX && !al16(dX)) return NF4_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (M == 0) {
+        rc = nf4::zero_f32(dA, int64_t(r) * v.cols, st);
+        if (rc) return rc;
+        return nf4::zero_f32(dB, v.rows * int64_t(r), st);
+    }
+    if ((rc = layer_view(&v, &ws, &ws_bytes, st))) return rc;
+    uint16_t* xd;
+    if ((rc = dropout_input(drop, x, M, v.cols, &ws, &ws_bytes, st, &xd))) return rc;
+    const size_t fb = (size_t(M) * size_t(v.cols) * 4 + 255) / 256 * 256;  // fp32 dH Wb
+    if (ws_bytes < fb) return NF4_EWORKSPACE;
+    float* dxf = static_cast<float*>(ws);
+    ws = static_cast<char*>(ws) + fb;
+    ws_bytes -= fb;
+    const nf4::BwdDropout bd{xd, dxf, float(1.0 / (1.0 - double(drop->p))), nf4::dropout_threshold(drop->p),
+                             drop->seed};
+    return nf4::backward_impl(v, x, dH, M, A, B, r, scale, u, dX, dA, dB, ws, ws_bytes, st, &bd);
 }
 
 int qlora_merge(const nf4_tensor* W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,

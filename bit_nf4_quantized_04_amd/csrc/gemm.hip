@@ -625,12 +625,13 @@ size_t workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int r, int
 
 int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                  int r, float scale, uint16_t* h, float* u_out, void* ws, size_t ws_bytes,
-                 hipStream_t st) {
+                 hipStream_t st, const uint16_t* xl) {
     const FwdPlan fp = plan_forward(q.rows, q.cols, M, r);
     if (ws_bytes < fp.total || (fp.total && !ws)) return NF4_EWORKSPACE;
     char* w = static_cast<char*>(ws);
+    if (!xl) xl = x;
     if (M <= kSkinnyMaxM && r <= kSkinnyMaxR)
-        return forward_skinny(q, x, M, A, B, r, scale, h, u_out, w, st);
+        return forward_skinny(q, x, M, A, B, r, scale, h, u_out, w, st, xl);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     LdNF4Rows lw{q};
     if (r == 0) {
@@ -644,7 +645,7 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
     uint16_t* ext = reinterpret_cast<uint16_t*>(w + fp.off_ext);
     const bool rd = use_rd_grid(M, q.rows) && use_rd(q, M, r, ext_cols(r));
     float* scw = rd ? reinterpret_cast<float*>(w + fp.off_sc) : nullptr;
-    int rc = down_projection(st, q, x, M, A, r, scale, fp, w, u, ext, scw);
+    int rc = down_projection(st, q, xl, M, A, r, scale, fp, w, u, ext, scw);
     if (rc) return rc;
     if (rd) {  // the block scales are decoded: the GEMM sees plain fp32 scales
         QView qv = q;
@@ -662,7 +663,7 @@ int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A
 
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M, const uint16_t* A,
                   const uint16_t* B, int r, float scale, const float* u_in, uint16_t* dX, float* dA,
-                  float* dB, void* ws, size_t ws_bytes, hipStream_t st) {
+                  float* dB, void* ws, size_t ws_bytes, hipStream_t st, const BwdDropout* drop) {
     const BwdPlan bp = plan_backward(q.rows, q.cols, M, r);
     if (ws_bytes < bp.total || !ws) return NF4_EWORKSPACE;
     char* w = static_cast<char*>(ws);
@@ -671,13 +672,17 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     int rc;
     // u (recomputed when not supplied)
     const float* u = u_in;
-    if (!u) {
+    if (!u) {  // with dropout u = (xd A^T) / (1 - p)
         float* uu = reinterpret_cast<float*>(w + bp.f.off_u);
-        rc = down_projection(st, q, x, M, A, r, scale, bp.f, w, uu,
+        rc = down_projection(st, q, drop ? drop->xd : x, M, A, r, scale, bp.f, w, uu,
                              reinterpret_cast<uint16_t*>(w + bp.f.off_ext));
         if (rc) return rc;
+        if (drop && (rc = scale_f32(uu, M * r, drop->inv_keep, st))) return rc;
         u = uu;
     }
+    const uint16_t* xa = drop ? drop->xd : x;             // the x of dA = dU^T x
+    const float sa = drop ? drop->inv_keep : 1.0f;        // and its scale
+    const bool small_plan = use_bwd_small(out, in, M);    // (no workspace for the large-tile dX then)
     uint16_t* uh = reinterpret_cast<uint16_t*>(w + bp.off_uh);
     uint16_t* ul = reinterpret_cast<uint16_t*>(w + bp.off_ul);
     float* du = reinterpret_cast<float*>(w + bp.off_du);
@@ -685,10 +690,13 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     uint16_t* duh = reinterpret_cast<uint16_t*>(w + bp.off_duh);
     uint16_t* dul = reinterpret_cast<uint16_t*>(w + bp.off_dul);
     float* part = reinterpret_cast<float*>(w + bp.off_part);
-    if (use_bwd_small(out, in, M))
+    if (small_plan && !drop)
         return backward_small(q, x, dH, M, A, r, B, scale, u, dX, dA, dB, w + bp.off_dxv, st);
-    float* dx_rd_scales = (bp.skinny && dX && q.dq && use_dx_rd(q, M, r, KL))
-                              ? reinterpret_cast<float*>(w + bp.off_sc) : nullptr;
+    // with dropout the dX product runs without the rank-r term, into fp32 (the
+    // tiled GEMM's partial output), and the masked term is added afterwards
+    const int rdx = drop ? 0 : r, KLdx = drop ? 0 : KL;
+    const bool dxrd = !drop && !small_plan && dX && use_dx_rd(q, M, rdx, KLdx);
+    float* dx_rd_scales = (bp.skinny && dxrd && q.dq) ? reinterpret_cast<float*>(w + bp.off_sc) : nullptr;
     const bool dh_vec = al16(dH) && (out % 8 == 0);
     if (bp.skinny) {
         uint16_t* bt = reinterpret_cast<uint16_t*>(w + bp.off_bt);
@@ -702,12 +710,12 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
             return rc;
         }
         if ((rc = nt_product(st, dH, M, out, bt, r, bp.Zdu, part))) return rc;
-        if ((rc = fin_du(st, part, bp.Zdu, M, r, KL, scale, u, duext, duq, uq))) return rc;
+        if ((rc = fin_du(st, part, bp.Zdu, M, r, KL, scale, u, duext, duq, uq, drop ? du : nullptr))) return rc;
         // dB = s dH^T u, dA = dU^T x: reductions over the tokens
         float* part_a = reinterpret_cast<float*>(w + bp.off_part_a);
         if ((rc = tn_product(st, dH, M, out, uq, r, bp.Zdb, part))) return rc;
-        if ((rc = tn_product(st, x, M, in, duq, r, bp.Zda, part_a))) return rc;
-        if ((rc = reduce_pair(st, part, bp.Zdb, out * r, scale, dB, part_a, bp.Zda, in, r, 1.0f, dA))) return rc;
+        if ((rc = tn_product(st, xa, M, in, duq, r, bp.Zda, part_a))) return rc;
+        if ((rc = reduce_pair(st, part, bp.Zdb, out * r, scale, dB, part_a, bp.Zda, in, r, sa, dA))) return rc;
     } else {
     hipLaunchKernelGGL(k_splits, dim3(ew_grid(M * r)), dim3(256), 0, st, u, M, r, r, 1.0f,
                        (uint16_t*)nullptr, uh, ul);
@@ -728,32 +736,38 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     hipLaunchKernelGGL(k_reduce, dim3(ew_grid(out * r)), dim3(256), 0, st, part, bp.Zdb, out * r, scale, dB);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     // dA = (dU_hi + dU_lo)^T x : [r][in], K = M.
-    const bool x_vec = al16(x);
-    rc = gemm(st, r, in, LdColMajor{duh, r, M, r, r % 8 == 0}, LdColMajor{x, in, M, in, x_vec}, M,
-              LdColMajor{dul, r, M, r, r % 8 == 0}, LdColMajor{x, in, M, in, x_vec}, M,
+    const bool x_vec = al16(xa);
+    rc = gemm(st, r, in, LdColMajor{duh, r, M, r, r % 8 == 0}, LdColMajor{xa, in, M, in, x_vec}, M,
+              LdColMajor{dul, r, M, r, r % 8 == 0}, LdColMajor{xa, in, M, in, x_vec}, M,
               OutPartial{part, r, in}, bp.Zda);
     if (rc) return rc;
-    hipLaunchKernelGGL(k_reduce, dim3(ew_grid(r * in)), dim3(256), 0, st, part, bp.Zda, r * in, 1.0f, dA);
+    hipLaunchKernelGGL(k_reduce, dim3(ew_grid(r * in)), dim3(256), 0, st, part, bp.Zda, r * in, sa, dA);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     }
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
-        if (use_dx_rd(q, M, r, KL)) {
+        const uint16_t* ex = drop ? nullptr : duext;
+        if (dxrd) {
             QView qv = q;
             if (dx_rd_scales) {  // decoded already: plain fp32 scales
                 qv.dq = 0;
                 qv.absmax = dx_rd_scales;
             }
-            rc = dx_rd(qv, dH, M, duext, KL, A, r, dX, reinterpret_cast<float*>(w + bp.off_sc),
+            rc = dx_rd(qv, dH, M, ex, KLdx, A, rdx, dX, reinterpret_cast<float*>(w + bp.off_sc),
                        reinterpret_cast<float*>(w + bp.off_dxp), st);
         }
+        else if (drop)
+            rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out, LdNone{}, LdNone{}, 0,
+                      OutPartial{drop->dxf, M, in}, 1, true);
         else if (use_big_gemm(M, in))
-            rc = dx_big(q, dH, M, duext, KL, A, r, dX, st);
+            rc = dx_big(q, dH, M, ex, KLdx, A, rdx, dX, st);
         else
             rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out,
                       LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1,
                       true);
         if (rc) return rc;
+        if (drop && (rc = dx_dropout_add(dX, drop->dxf, du, A, M, in, r, drop->thr, drop->seed, drop->inv_keep, st)))
+            return rc;
     }
     return NF4_OK;
 }

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void k_tn(const uint16_t* __restrict__ P, int6
 __global__ __launch_bounds__(256) void k_fin_du(const float* __restrict__ part, int Z, int64_t M, int r,
                                                 int KL, float scale, const float* __restrict__ u,
                                                 uint16_t* __restrict__ duext, uint16_t* __restrict__ duq,
-                                                uint16_t* __restrict__ uq) {
+                                                uint16_t* __restrict__ uq, float* __restrict__ du) {
     const int64_t n = M * 64;
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
         const int64_t m = i >> 6;
@@ -289,6 +289,7 @@ __global__ __launch_bounds__(256) void k_fin_du(const float* __restrict__ part, 
         if (j < r) {
             float a = 0.0f;
             for (int z = 0; z < Z; ++z) a += part[(int64_t(z) * M + m) * r + j];
+            if (du) du[m * r + j] = a * scale;
             split_bf16(a * scale, dh, dl);
             split_bf16(u[m * r + j], uh, ul);
             duext[m * KL + j] = dh;
@@ -456,8 +457,8 @@ int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const u
 }
 
 int fin_du(hipStream_t st, const float* part, int Z, int64_t M, int r, int KL, float scale, const float* u,
-           uint16_t* duext, uint16_t* duq, uint16_t* uq) {
-    hipLaunchKernelGGL(k_fin_du, dim3(ew(M * 64)), dim3(256), 0, st, part, Z, M, r, KL, scale, u, duext, duq, uq);
+           uint16_t* duext, uint16_t* duq, uint16_t* uq, float* du) {
+    hipLaunchKernelGGL(k_fin_du, dim3(ew(M * 64)), dim3(256), 0, st, part, Z, M, r, KL, scale, u, duext, duq, uq, du);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

@@ -35,16 +35,34 @@ int expand_scales(const QView& q, void* s64, hipStream_t s);
 int launch_dequant_f32(const QView& q, float* out, hipStream_t s);
 int launch_dequant_bf16(const QView& q, uint16_t* out, hipStream_t s);
 
-// Layer passes (defined in the GEMM / skinny / LoRA files).
+// Layer passes (defined in the GEMM / skinny / LoRA files).  `xl`, when
+// not null, is the input of the adapter branch (x with dropout applied);
+// the base product always reads x.
 int forward_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A,
                  const uint16_t* B, int r, float scale, uint16_t* h, float* u_out, void* ws,
-                 size_t ws_bytes, hipStream_t s);
+                 size_t ws_bytes, hipStream_t s, const uint16_t* xl = nullptr);
 int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint16_t* Ab,
                        const uint16_t* Bb, int n, int r, const float* scales, const int32_t* ids,
                        uint16_t* h, void* ws, size_t ws_bytes, hipStream_t s);
+// Adapter-input dropout in the backward (dropout.hip): xd = keep * x, the
+// rescale 1/(1 - p), and the mask of the dX term.
+struct BwdDropout {
+    const uint16_t* xd;
+    float* dxf;  // [M][in] fp32: dH Wb, before the masked term and the one rounding
+    float inv_keep;
+    uint32_t thr;
+    uint64_t seed;
+};
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M,
                   const uint16_t* A, const uint16_t* B, int r, float scale, const float* u,
-                  uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t s);
+                  uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, hipStream_t s,
+                  const BwdDropout* drop = nullptr);
+// dropout.hip
+uint32_t dropout_threshold(float p);  // ceil(p 2^32)
+int dropout_x(const uint16_t* x, int64_t M, int64_t K, uint32_t thr, uint64_t seed, uint16_t* xd, hipStream_t st);
+int scale_f32(float* v, int64_t n, float f, hipStream_t st);
+int dx_dropout_add(uint16_t* dx, const float* dxf, const float* du, const uint16_t* A, int64_t M, int64_t K, int r,
+                   uint32_t thr, uint64_t seed, float f, hipStream_t st);
 // Profiling hook: the caller's events (or null) that bracket the dominant
 // kernel of a call, attached to kernel dispatches (hipExtLaunchKernelGGL).
 // The kernel launched just before the dominant one, when launched with
@@ -88,7 +106,8 @@ constexpr int64_t kSkinnyMaxM = 16;
 constexpr int kSkinnyMaxR = 64;
 size_t skinny_ws_bytes(int64_t M, int r);
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-                   int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st);
+                   int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st,
+                   const uint16_t* xl = nullptr);
 // Large-M fused dequant-GEMMs (256 x 256 tiles).
 bool use_big_gemm(int64_t Mr, int64_t Nc);
 int forward_big(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext, int KL,
@@ -168,7 +187,7 @@ int tn_product(hipStream_t st, const uint16_t* P, int64_t M, int64_t RR, const u
 // The dU partials summed and scaled, written as the dX extension (hi | lo |
 // pad, [M][KL]) and as hi/lo [M][128] for the dA product, with u's hi/lo too.
 int fin_du(hipStream_t st, const float* part, int Z, int64_t M, int r, int KL, float scale, const float* u,
-           uint16_t* duext, uint16_t* duq, uint16_t* uq);
+           uint16_t* duext, uint16_t* duq, uint16_t* uq, float* du = nullptr);
 int transpose16(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt);
 // transpose16 and the fp32 block scales of a double-quantized q into sc, one launch
 int transpose_bs(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* bt, const QView& q, float* sc);

@@ -492,14 +492,14 @@ size_t skinny_ws_bytes(int64_t M, int r) {
 }
 
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-                   int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st) {
+                   int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st, const uint16_t* xl) {
     float* part = reinterpret_cast<float*>(ws);
     const int64_t nkb = q.cols / 64;
     const int R = nkb <= 64 ? 1 : nkb <= 128 ? 2 : nkb <= 256 ? 4 : 0;
     // (32-bit byte offsets inside the M = 1 kernel: codes under 4 GB)
     const bool gemv1 = M == 1 && R > 0 && r <= 64 && q.rows * q.cols / 2 < (int64_t(1) << 32);
     launch_before_dominant(k_down_small, dim3(unsigned(std::max<int64_t>(1, cdiv(r, 16))), DOWN_SPLIT),
-                           dim3(256), 0, st, x, int(M), q.cols, A, r, part);
+                           dim3(256), 0, st, xl ? xl : x, int(M), q.cols, A, r, part);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (gemv1) {
         auto kern = q.dq ? (q.gshift >= 0 ? k_gemv1<true, true> : k_gemv1<true, false>)

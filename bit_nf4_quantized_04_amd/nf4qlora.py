@@ -27,6 +27,7 @@ _lib = C.CDLL(LIB_PATH)
 NF4_OK, NF4_EINVAL, NF4_ESHAPE, NF4_EUNSUPPORTED, NF4_EWORKSPACE, NF4_ELAUNCH = range(6)
 QLORA_OP_FORWARD, QLORA_OP_BACKWARD, QLORA_OP_FORWARD_MULTI = 1, 2, 3
 QLORA_OP_BLOCK128 = 0x100  # OR'ed into a workspace query for a weight with 128-element blocks
+QLORA_OP_DROPOUT = 0x200   # OR'ed into a workspace query for the *_dropout calls
 
 
 class nf4_config(C.Structure):
@@ -43,6 +44,10 @@ class nf4_tensor(C.Structure):
         ("cols", C.c_int64),
         ("cfg", nf4_config),
     ]
+
+
+class qlora_dropout(C.Structure):
+    _fields_ = [("p", C.c_float), ("pad", C.c_uint32), ("seed", C.c_uint64)]
 
 
 _P = C.c_void_p
@@ -65,6 +70,11 @@ _SIGS = {
                                              C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "qlora_linear_backward": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, _I64, _P, _P, C.c_int32,
                                         C.c_float, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "qlora_linear_forward_dropout": (C.c_int, [C.POINTER(nf4_tensor), _P, _I64, _P, _P, C.c_int32, C.c_float,
+                                               C.POINTER(qlora_dropout), _P, _P, _P, C.c_size_t, _P]),
+    "qlora_linear_backward_dropout": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, _I64, _P, _P, C.c_int32,
+                                                C.c_float, C.POINTER(qlora_dropout), _P, _P, _P, _P, _P,
+                                                C.c_size_t, _P]),
     "qlora_merge": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, C.c_int32, C.c_float, _P, _P]),
     "qlora_adamw_step": (C.c_int, [_P, _P, _P, _P, _P, _I64, C.c_int32, C.c_float, C.c_float, C.c_float,
                                    C.c_float, C.c_float, _P]),
@@ -248,21 +258,30 @@ def _workspace(nbytes: int, device):
 
 
 def qlora_linear_forward(w: NF4Weight, x, A, B, scale: float, want_u: bool = False, ws=None,
-                         out=None, stream=None):
-    """h = x Wb^T + scale (x A^T) B^T; x, A, B bf16 CUDA tensors.  Returns h (and u)."""
+                         out=None, stream=None, dropout=None):
+    """h = x Wb^T + scale (dropout(x) A^T) B^T; x, A, B bf16 CUDA tensors.
+    dropout: None, or (p, seed) for dropout on the adapter input.  Returns h
+    (and u = dropout(x) A^T)."""
     import torch
 
     M = x.shape[0]
     r = 0 if A is None else A.shape[0]
     h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
     u = torch.empty((M, r), dtype=torch.float32, device=x.device) if (want_u and r) else None
-    need = qlora_workspace_bytes(QLORA_OP_FORWARD | w.op_flags, w.rows, w.cols, M, r)
+    flags = w.op_flags | (QLORA_OP_DROPOUT if dropout is not None else 0)
+    need = qlora_workspace_bytes(QLORA_OP_FORWARD | flags, w.rows, w.cols, M, r)
     if ws is None:
         ws = _workspace(need, x.device)
     t = w.c_struct()
-    _check(_lib.qlora_linear_forward(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale),
-                                     _ptr(h), _ptr(u), _ptr(ws), ws.numel(), _stream(stream)),
-           "qlora_linear_forward")
+    if dropout is None:
+        _check(_lib.qlora_linear_forward(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale),
+                                         _ptr(h), _ptr(u), _ptr(ws), ws.numel(), _stream(stream)),
+               "qlora_linear_forward")
+    else:
+        d = qlora_dropout(float(dropout[0]), 0, int(dropout[1]))
+        _check(_lib.qlora_linear_forward_dropout(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale),
+                                                 C.byref(d), _ptr(h), _ptr(u), _ptr(ws), ws.numel(),
+                                                 _stream(stream)), "qlora_linear_forward_dropout")
     return (h, u) if want_u else h
 
 
@@ -285,8 +304,9 @@ def qlora_linear_forward_multi(w: NF4Weight, x, A_bank, B_bank, scales, ids, ws=
 
 
 def qlora_linear_backward(w: NF4Weight, x, dH, A, B, scale: float, u=None, want_dx: bool = True,
-                          ws=None, stream=None):
-    """Returns (dX or None, dA fp32 [r, in], dB fp32 [out, r])."""
+                          ws=None, stream=None, dropout=None):
+    """Returns (dX or None, dA fp32 [r, in], dB fp32 [out, r]); dropout as in
+    qlora_linear_forward (the same (p, seed) regenerates the same mask)."""
     import torch
 
     M = x.shape[0]
@@ -295,13 +315,21 @@ def qlora_linear_backward(w: NF4Weight, x, dH, A, B, scale: float, u=None, want_
     dX = torch.empty((M, w.cols), dtype=torch.bfloat16, device=dev) if want_dx else None
     dA = torch.empty((r, w.cols), dtype=torch.float32, device=dev)
     dB = torch.empty((w.rows, r), dtype=torch.float32, device=dev)
-    need = qlora_workspace_bytes(QLORA_OP_BACKWARD | w.op_flags, w.rows, w.cols, M, r)
+    flags = w.op_flags | (QLORA_OP_DROPOUT if dropout is not None else 0)
+    need = qlora_workspace_bytes(QLORA_OP_BACKWARD | flags, w.rows, w.cols, M, r)
     if ws is None:
         ws = _workspace(need, dev)
     t = w.c_struct()
-    _check(_lib.qlora_linear_backward(C.byref(t), _ptr(x), _ptr(dH), M, _ptr(A), _ptr(B), r,
-                                      float(scale), _ptr(u), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
-                                      ws.numel(), _stream(stream)), "qlora_linear_backward")
+    if dropout is None:
+        _check(_lib.qlora_linear_backward(C.byref(t), _ptr(x), _ptr(dH), M, _ptr(A), _ptr(B), r,
+                                          float(scale), _ptr(u), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                          ws.numel(), _stream(stream)), "qlora_linear_backward")
+    else:
+        d = qlora_dropout(float(dropout[0]), 0, int(dropout[1]))
+        _check(_lib.qlora_linear_backward_dropout(C.byref(t), _ptr(x), _ptr(dH), M, _ptr(A), _ptr(B), r,
+                                                  float(scale), C.byref(d), _ptr(u), _ptr(dX), _ptr(dA), _ptr(dB),
+                                                  _ptr(ws), ws.numel(), _stream(stream)),
+               "qlora_linear_backward_dropout")
     return dX, dA, dB
 
 

@@ -144,7 +144,14 @@ int nf4_dequantize_bf16(const nf4_tensor* W, uint16_t* W_out, void* stream);
  * bytes, rounded up to 256) at the front of the workspace, and the kernels
  * of the 64-element layout run on it (every weight is dequantized to the
  * same value). */
-enum { QLORA_OP_FORWARD = 1, QLORA_OP_BACKWARD = 2, QLORA_OP_FORWARD_MULTI = 3, QLORA_OP_BLOCK128 = 0x100 };
+enum {
+    QLORA_OP_FORWARD = 1,
+    QLORA_OP_BACKWARD = 2,
+    QLORA_OP_FORWARD_MULTI = 3,
+    QLORA_OP_BLOCK128 = 0x100,  /* OR'ed in: the weight has 128-element blocks */
+    QLORA_OP_DROPOUT = 0x200    /* OR'ed in: the *_dropout calls (M*in*2 bytes more, the backward
+                                   M*in*6, each part rounded to 256) */
+};
 size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
                              int32_t n_adapters);
 
@@ -153,8 +160,8 @@ size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int3
  * W: rows = out, cols = in (cols % 64 == 0).  x bf16 [M, in]; A bf16 [r, in];
  * B bf16 [out, r]; h bf16 [M, out], overwritten.  u_out (fp32 [M, r]) may be
  * NULL; when given it receives u for the backward pass.  r == 0 or A/B NULL
- * gives the base product only.  Dropout on the adapter branch is not applied
- * (p = 0).  M == 0 is a successful no-op.  ws must hold
+ * gives the base product only.  No dropout on the adapter branch (p = 0; see
+ * qlora_linear_forward_dropout).  M == 0 is a successful no-op.  ws must hold
  * qlora_workspace_bytes(QLORA_OP_FORWARD, ...).  Products use bf16 operands
  * with fp32 accumulation; u stays fp32 (hi+lo bf16 pair inside the MFMA). */
 int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M,
@@ -183,6 +190,41 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
                           const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                           const float* u, uint16_t* dX, float* dA, float* dB,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* The layer with dropout on the adapter input [P1 section 1 and its
+ * adapter-branch diagram: h = W0 x + (alpha/r) B(A(dropout(x))); P3
+ * "Concrete example: Fine-tuning Llama-3-8B on a 24 GB GPU": lora_dropout =
+ * 0.05].  The pages give
+ * the rate only; this library's reading: inverted dropout, element (m, k)
+ * of x kept iff the first word of Philox-4x32-10 (Salmon, Moraes, Dror,
+ * Shaw, SC 2011) with counter (lo, hi of m*in + k, 0, 0) and key (lo, hi of
+ * seed) is >= ceil(p * 2^32), kept elements scaled by 1/(1 - p); the base
+ * product always reads x.  The same (p, seed) in the backward regenerates the
+ * same mask.  p must be finite and in [0, 1) (NF4_EINVAL otherwise). */
+typedef struct qlora_dropout {
+    float p;        /* dropout rate */
+    uint32_t pad;   /* unused */
+    uint64_t seed;  /* Philox key */
+} qlora_dropout;
+
+/* Forward with dropout: as qlora_linear_forward, with u_out = dropout(x) A^T
+ * fp32.  Workspace: qlora_workspace_bytes(QLORA_OP_FORWARD |
+ * QLORA_OP_DROPOUT [| QLORA_OP_BLOCK128], ...).  Arguments and errors as
+ * qlora_linear_forward, plus NF4_EINVAL for a bad `drop`. */
+int qlora_linear_forward_dropout(const nf4_tensor* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float scale, const qlora_dropout* drop,
+                                 uint16_t* h, float* u_out, void* ws, size_t ws_bytes, void* stream);
+/* Backward with dropout: dU = s dH B, dB = s dH^T u, dA = dU^T dropout(x),
+ * dX = dH Wb + keep * (dU A) / (1 - p) (dH Wb in fp32, the masked term added
+ * in fp32, one rounding to bf16).  u: dropout(x) A^T as the forward
+ * returned it, or NULL to recompute it.  Workspace:
+ * qlora_workspace_bytes(QLORA_OP_BACKWARD | QLORA_OP_DROPOUT [| ...], ...).
+ * Arguments and errors as qlora_linear_backward, plus NF4_EINVAL for a bad
+ * `drop`. */
+int qlora_linear_backward_dropout(const nf4_tensor* W, const uint16_t* x, const uint16_t* dH, int64_t M,
+                                  const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                                  const qlora_dropout* drop, const float* u, uint16_t* dX, float* dA, float* dB,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* Merge the adapter into the base weight for a standalone 16-bit model [P3
  * "Merging and deploying"; P4 FAQ on merging, W_new = W + (alpha/r) B A]:

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(F):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     lib = C.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -154,6 +154,28 @@ def test_block128_layer_calls(F):
     # a tensor that is not a whole number of blocks is not
     t2 = _tensor(F, rows=3, cols=64, bs=128)
     assert lib.qlora_linear_forward(C.byref(t2), FAKE, 4, FAKE, FAKE, 4, 2.0, FAKE, None, FAKE, 1 << 20, None) == F.NF4_ESHAPE
+
+
+def test_dropout_argument_errors(F):
+    """A dropout rate outside [0, 1) or no settings at all is refused before
+    anything is launched; the dropout workspace holds xd (M*in bf16) and, in
+    the backward, the fp32 dH Wb (M*in fp32)."""
+    lib = F._lib
+    t = _tensor(F)
+    fwd = lambda d: lib.qlora_linear_forward_dropout(C.byref(t), FAKE, 4, FAKE, FAKE, 4, 2.0, d, FAKE, None,
+                                                     FAKE, 1 << 30, None)
+    bwd = lambda d: lib.qlora_linear_backward_dropout(C.byref(t), FAKE, FAKE, 4, FAKE, FAKE, 4, 2.0, d, None,
+                                                      FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        d = F.qlora_dropout(p, 0, 1)
+        assert fwd(C.byref(d)) == F.NF4_EINVAL
+        assert bwd(C.byref(d)) == F.NF4_EINVAL
+    assert fwd(None) == F.NF4_EINVAL and bwd(None) == F.NF4_EINVAL
+    for op, per in ((F.QLORA_OP_FORWARD, 2), (F.QLORA_OP_BACKWARD, 6)):
+        base = F.qlora_workspace_bytes(op, 128, 256, 600, 8)
+        assert F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT, 128, 256, 600, 8) == base + 600 * 256 * per
+        both = F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT | F.QLORA_OP_BLOCK128, 128, 256, 600, 8)
+        assert both == base + 600 * 256 * per + 128 * 256 // 16
 
 
 def test_workspace_sizes_are_monotone(F):

@@ -346,6 +346,30 @@ def main():
 
     t_7b128, _ = timed(train7_128_step, K, W)
     del q7b, wsf7b, wsb7b
+    # the two training passes with dropout p = 0.05 on the adapter input
+    P_DROP = 0.05
+    wsf7d = torch.empty(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD | F.QLORA_OP_DROPOUT, sh7["out"], sh7["inp"],
+                                                M7, sh7["r"]), dtype=torch.uint8, device=dev)
+    wsb7d = torch.empty(F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD | F.QLORA_OP_DROPOUT, sh7["out"], sh7["inp"],
+                                                M7, sh7["r"]), dtype=torch.uint8, device=dev)
+
+    def train7_drop_step(i):
+        _, u = F.qlora_linear_forward(q7, x7, A7, B7, s7, want_u=True, ws=wsf7d, out=h7, dropout=(P_DROP, i))
+        F.qlora_linear_backward(q7, x7, dH7, A7, B7, s7, u=u, ws=wsb7d, dropout=(P_DROP, i))
+
+    t_7bd, _ = timed(train7_drop_step, K, W)
+    del wsf7d, wsb7d
+    ws_ftd = torch.empty(F.qlora_workspace_bytes(F.QLORA_OP_FORWARD | F.QLORA_OP_DROPOUT, out, inp, Mtrain, r),
+                         dtype=torch.uint8, device=dev)
+    ws_btd = torch.empty(F.qlora_workspace_bytes(F.QLORA_OP_BACKWARD | F.QLORA_OP_DROPOUT, out, inp, Mtrain, r),
+                         dtype=torch.uint8, device=dev)
+
+    def train_drop_step(i):
+        _, u = F.qlora_linear_forward(qs[0], xt, A, B, scale, want_u=True, ws=ws_ftd, out=ht, dropout=(P_DROP, i))
+        F.qlora_linear_backward(qs[0], xt, dH, A, B, scale, u=u, ws=ws_btd, dropout=(P_DROP, i))
+
+    t_trd, _ = timed(train_drop_step, max(K // 2, 3), max(W // 2, 1))
+    del ws_ftd, ws_btd
     ng128 = (out * inp // 128 + 255) // 256
     d128_bytes = decode_bytes(out, inp, 1, r, ng128, block=128)
     mg_bytes = out * inp // 2 + out * inp // 64 + 4 * ngroups + 2 * r * (inp + out) + 2 * out * inp
@@ -436,6 +460,16 @@ def main():
             "train_7b_ms": round(t_7b128, 4),
             "train_7b_TFLOPs": round(f7 / (t_7b128 * 1e-3) / 1e12, 2),
             "train_7b_frac_mfma_peak": round(f7 / (t_7b128 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+        "dropout": {
+            "workload": "training passes with dropout p=%g on the adapter input (keep decisions from "
+                        "Philox-4x32-10, a new seed every step)" % P_DROP,
+            "train_70b_ms": round(t_trd, 4),
+            "train_70b_TFLOPs": round((ffwd + fbwd) / (t_trd * 1e-3) / 1e12, 2),
+            "train_70b_vs_p0": round(t_trd / t_tr, 4),
+            "train_7b_ms": round(t_7bd, 4),
+            "train_7b_TFLOPs": round(f7 / (t_7bd * 1e-3) / 1e12, 2),
+            "train_7b_vs_p0": round(t_7bd / t_7b, 4),
         },
         "multi_adapter": {
             "workload": "%d adapters r=%d on %d->%d NF4 base, %d tokens" % (

@@ -8,8 +8,8 @@
 // adapter branch on xd = keep * x (exact in bf16) with 1/(1 - p) folded into
 // the scales.  The dX term keep * (dU A) / (1 - p) would need the mask per
 // output element inside the dX product, so that product runs without the
-// rank-r term into fp32 and a pass of its own adds the masked term and rounds
-// once.
+// rank-r term into fp32 (split partials) and a pass of its own adds the
+// partials and the masked term and rounds once.
 #include <algorithm>
 #include <cmath>
 
@@ -43,12 +43,12 @@ __global__ __launch_bounds__(256) void k_scale_f32(float* __restrict__ v, int64_
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) v[i] *= f;
 }
 
-// dX[m][i] = bf16( dxf[m][i] + f * keep(m, i) * sum_j dU[m][j] A[j][i] ),
-// dxf the fp32 dH Wb (one rounding for the whole sum): a workgroup takes 256
-// consecutive columns of one row (the dU row is the same for the whole
-// workgroup).
-__global__ __launch_bounds__(256) void k_dx_dropout_add(uint16_t* __restrict__ dx, const float* __restrict__ dxf,
-                                                        const float* __restrict__ du,
+// dX[m][i] = bf16( P[m][i] + f * keep(m, i) * sum_j dU[m][j] A[j][i] ), P
+// the fp32 dH Wb given as Z split partials [Z][M][K], added in split order
+// (one rounding for the whole sum): a workgroup takes 256 consecutive columns
+// of one row (the dU row is the same for the whole workgroup).
+__global__ __launch_bounds__(256) void k_dx_dropout_add(uint16_t* __restrict__ dx, const float* __restrict__ part,
+                                                        int Z, const float* __restrict__ du,
                                                         const uint16_t* __restrict__ A, int64_t M, int64_t K, int r,
                                                         uint32_t thr, uint64_t seed, float f) {
     const int64_t ntk = (K + 255) / 256, tiles = M * ntk;
@@ -60,7 +60,9 @@ __global__ __launch_bounds__(256) void k_dx_dropout_add(uint16_t* __restrict__ d
         for (int j = 0; j < r; ++j) acc = __builtin_fmaf(dr[j], bf16_f(A[int64_t(j) * K + i]), acc);
         const int64_t e = m * K + i;
         const float add = philox_w0(uint64_t(e), seed) >= thr ? f * acc : 0.0f;
-        dx[e] = to_bf16(dxf[e] + add);
+        float base = part[e];
+        for (int z = 1; z < Z; ++z) base += part[int64_t(z) * M * K + e];
+        dx[e] = to_bf16(base + add);
     }
 }
 
@@ -90,11 +92,11 @@ int scale_f32(float* v, int64_t n, float f, hipStream_t st) {
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
-int dx_dropout_add(uint16_t* dx, const float* dxf, const float* du, const uint16_t* A, int64_t M, int64_t K, int r,
-                   uint32_t thr, uint64_t seed, float f, hipStream_t st) {
+int dx_dropout_add(uint16_t* dx, const float* part, int Z, const float* du, const uint16_t* A, int64_t M, int64_t K,
+                   int r, uint32_t thr, uint64_t seed, float f, hipStream_t st) {
     const int64_t tiles = M * cdiv(K, 256);
-    hipLaunchKernelGGL(k_dx_dropout_add, dim3(unsigned(std::min<int64_t>(tiles, 65536))), dim3(256), 0, st, dx, dxf,
-                       du, A, M, K, r, thr, seed, f);
+    hipLaunchKernelGGL(k_dx_dropout_add, dim3(unsigned(std::min<int64_t>(tiles, 65536))), dim3(256), 0, st, dx, part,
+                       Z, du, A, M, K, r, thr, seed, f);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

@@ -692,10 +692,10 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     float* part = reinterpret_cast<float*>(w + bp.off_part);
     if (small_plan && !drop)
         return backward_small(q, x, dH, M, A, r, B, scale, u, dX, dA, dB, w + bp.off_dxv, st);
-    // with dropout the dX product runs without the rank-r term, into fp32 (the
-    // tiled GEMM's partial output), and the masked term is added afterwards
+    // with dropout the dX product runs without the rank-r term, into fp32
+    // partials, and the masked term is added afterwards
     const int rdx = drop ? 0 : r, KLdx = drop ? 0 : KL;
-    const bool dxrd = !drop && !small_plan && dX && use_dx_rd(q, M, rdx, KLdx);
+    const bool dxrd = !small_plan && dX && use_dx_rd(q, M, rdx, KLdx);
     float* dx_rd_scales = (bp.skinny && dxrd && q.dq) ? reinterpret_cast<float*>(w + bp.off_sc) : nullptr;
     const bool dh_vec = al16(dH) && (out % 8 == 0);
     if (bp.skinny) {
@@ -747,18 +747,24 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
     // dX = dH Wb + [dU_hi | dU_lo] [A; A] : [M][in], K = out (+ 2r).
     if (dX) {
         const uint16_t* ex = drop ? nullptr : duext;
+        // with dropout: the fp32 dH Wb as Zdx split partials at dxp
+        int Zdx = 1;
+        float* dxp = drop ? drop->dxf : nullptr;
         if (dxrd) {
             QView qv = q;
             if (dx_rd_scales) {  // decoded already: plain fp32 scales
                 qv.dq = 0;
                 qv.absmax = dx_rd_scales;
             }
-            rc = dx_rd(qv, dH, M, ex, KLdx, A, rdx, dX, reinterpret_cast<float*>(w + bp.off_sc),
-                       reinterpret_cast<float*>(w + bp.off_dxp), st);
+            float* part = reinterpret_cast<float*>(w + bp.off_dxp);
+            if (drop && (Zdx = dx_splits(M, q.rows, q.cols)) == 1) part = dxp;
+            if (drop) dxp = part;
+            rc = dx_rd(qv, dH, M, ex, KLdx, A, rdx, dX, reinterpret_cast<float*>(w + bp.off_sc), part, st,
+                       drop != nullptr);
         }
         else if (drop)
             rc = gemm(st, M, in, LdRowMajor{dH, M, out, out, dh_vec}, LdNF4Cols{q}, out, LdNone{}, LdNone{}, 0,
-                      OutPartial{drop->dxf, M, in}, 1, true);
+                      OutPartial{dxp, M, in}, 1, true);
         else if (use_big_gemm(M, in))
             rc = dx_big(q, dH, M, ex, KLdx, A, rdx, dX, st);
         else
@@ -766,7 +772,7 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
                       LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1,
                       true);
         if (rc) return rc;
-        if (drop && (rc = dx_dropout_add(dX, drop->dxf, du, A, M, in, r, drop->thr, drop->seed, drop->inv_keep, st)))
+        if (drop && (rc = dx_dropout_add(dX, dxp, Zdx, du, A, M, in, r, drop->thr, drop->seed, drop->inv_keep, st)))
             return rc;
     }
     return NF4_OK;

@@ -567,6 +567,7 @@ struct DxArgs {
     int64_t M, out, in;
     int KL, r;
     int spl;               // weight-row steps per split (a multiple of four)
+    int f32;               // nonzero: fp32 partials even for one split
 };
 
 // W tile layout: row-major with a 576-byte row stride, and the 16-byte chunk
@@ -815,7 +816,7 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
 
     // D layout: lane holds column lane%32 and rows 8(v/4) + 4(lane/32) + v%4
     float* pz = a.part + int64_t(z) * M * N;
-    const bool split = gridDim.y > 1;
+    const bool split = gridDim.y > 1 || a.f32;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int64_t n = i0 + 64 * w + 32 * j + (lane & 31);
@@ -955,7 +956,7 @@ size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols) {
 }
 
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
-          int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st) {
+          int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st, bool f32) {
     const float* scales;
     int rc = block_scales(q, scale_ws, &scales, st);
     if (rc) return rc;
@@ -963,11 +964,11 @@ int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, 
     const int S1 = int(q.rows / DK);
     const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);
     DxArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, dH, r > 0 ? duext : nullptr, A, dX, part_ws,
-             M, q.rows, q.cols, KL, r, spl};
+             M, q.rows, q.cols, KL, r, spl, f32 ? 1 : 0};
     const int64_t T = cdiv(M, RM) * cdiv(q.cols, RN);
     launch_dominant(k_dx_rd, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
-    if (Z > 1) {
+    if (Z > 1 && !f32) {
         const int64_t n = M * q.cols;  // a multiple of 256
         hipLaunchKernelGGL(k_split_sum, dim3(unsigned(std::min<int64_t>(cdiv(n, 1024), 8192))), dim3(256), 0, st,
                            part_ws, Z, n, dX);

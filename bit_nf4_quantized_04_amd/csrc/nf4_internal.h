@@ -61,8 +61,8 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
 uint32_t dropout_threshold(float p);  // ceil(p 2^32)
 int dropout_x(const uint16_t* x, int64_t M, int64_t K, uint32_t thr, uint64_t seed, uint16_t* xd, hipStream_t st);
 int scale_f32(float* v, int64_t n, float f, hipStream_t st);
-int dx_dropout_add(uint16_t* dx, const float* dxf, const float* du, const uint16_t* A, int64_t M, int64_t K, int r,
-                   uint32_t thr, uint64_t seed, float f, hipStream_t st);
+int dx_dropout_add(uint16_t* dx, const float* part, int Z, const float* du, const uint16_t* A, int64_t M, int64_t K,
+                   int r, uint32_t thr, uint64_t seed, float f, hipStream_t st);
 // Profiling hook: the caller's events (or null) that bracket the dominant
 // kernel of a call, attached to kernel dispatches (hipExtLaunchKernelGGL).
 // The kernel launched just before the dominant one, when launched with
@@ -172,8 +172,11 @@ int multi_fin_seg(const MultiSort& ms, const float* part, int Z, int64_t M, int6
                   const uint16_t* Bb, uint16_t* h, hipStream_t st);
 bool use_dx_rd(const QView& q, int64_t M, int r, int KL);
 size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols);
+int dx_splits(int64_t M, int64_t rows, int64_t cols);
+// f32: dX not written; the fp32 partials [dx_splits][M][in] go to part_ws
+// (also for one split), for the caller to finish.
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
-          int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st);
+          int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st, bool f32 = false);
 int dx_big(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL,
            const uint16_t* A, int r, uint16_t* dX, hipStream_t st);
 // Skinny rank-r products (lora_bwd.hip), r <= 64: fp32 partials over Z

@@ -37,7 +37,8 @@ CASES = [  # (M, out, in, r, p, seed, dq)
     (40, 320, 448, 24, 0.05, 3, False),       # tiled kernels
     (300, 160, 192, 80, 0.3, 4, True),        # r > 64
     (600, 4096, 1024, 64, 0.05, 5, True),     # register-dequant forward
-    (1000, 2048, 4096, 24, 0.1, 2**40 + 7, False),  # register-dequant forward and dX; a 64-bit seed
+    (1000, 2048, 4096, 24, 0.1, 2**40 + 7, False),  # register-dequant forward and dX (split); a 64-bit seed
+    (2048, 256, 6144, 16, 0.1, 6, True),      # register-dequant dX in one split
 ]
 
 

@@ -32,7 +32,8 @@ Sources (cited by page title and section):
   explained" sets lora_dropout = 0.05.  The pages give no random number
   generator: ``philox4x32_10`` is the published counter-based generator of
   Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
-  3" (SC 2011), and ``dropout_keep`` the reading stated there.
+  3" (SC 2011), and ``dropout_keep`` the reading stated there (each
+  counter's four output words serve four consecutive elements).
 * "QLoRA Specification for EMEP Fine-Tuning" ("GPU Orchestration": adapters
   and optimizer state in full precision), "QLoRA explained" ("Paged
   optimizers": the Adam moments of the LoRA parameters paged to host memory):
@@ -349,9 +350,10 @@ def backward(wb, x_bits, dh_bits, a_bits, b_bits, scale: float):
 # LoRA dropout on the adapter input ("QLoRA Finetuner", section 1 and its
 # adapter-branch diagram).  READING (the pages name dropout and its rate
 # only): inverted dropout, an element kept with probability 1 - p and the kept
-# ones scaled by 1/(1 - p); the keep decision of element (m, k) of x [M, in]
-# comes from Philox-4x32-10 with counter (lo, hi of m*in + k, 0, 0) and key
-# (lo, hi of the 64-bit seed): keep iff its first output word >= ceil(p 2^32).
+# ones scaled by 1/(1 - p); element e = m*in + k of x [M, in] takes output
+# word e mod 4 of Philox-4x32-10 at counter (lo, hi of floor(e/4), 0, 0) and
+# key (lo, hi of the 64-bit seed): kept iff that word >= ceil(p 2^32).  (All
+# four words of a counter are used, one per element.)
 # ---------------------------------------------------------------------------
 _PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers (Salmon et al. 2011)
 _PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key schedule increments (golden ratio, sqrt 3 - 1)
@@ -377,7 +379,7 @@ def philox4x32_10(ctr, key) -> np.ndarray:
 
 
 def dropout_threshold(p: float) -> int:
-    """ceil(p 2^32) for p in [0, 1): the smallest first word that is dropped."""
+    """ceil(p 2^32) for p in [0, 1): the smallest output word that is dropped."""
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout rate must lie in [0, 1)")
     return int(math.ceil(float(p) * 4294967296.0))
@@ -385,15 +387,16 @@ def dropout_threshold(p: float) -> int:
 
 def dropout_keep(M: int, inp: int, p: float, seed: int) -> np.ndarray:
     """Boolean keep mask [M, inp] of the adapter-input dropout."""
-    idx = np.arange(M * inp, dtype=np.uint64)
+    n = M * inp
+    idx = np.arange((n + 3) // 4, dtype=np.uint64)   # counters
     ctr = np.zeros((idx.size, 4), dtype=np.uint64)
     ctr[:, 0] = idx & np.uint64(0xFFFFFFFF)
     ctr[:, 1] = idx >> np.uint64(32)
     key = np.empty((idx.size, 2), dtype=np.uint64)
     key[:, 0] = seed & 0xFFFFFFFF
     key[:, 1] = (seed >> 32) & 0xFFFFFFFF
-    first = philox4x32_10(ctr, key)[:, 0].astype(np.uint64)
-    return (first >= np.uint64(dropout_threshold(p))).reshape(M, inp)
+    words = philox4x32_10(ctr, key).reshape(-1)[:n].astype(np.uint64)   # word e mod 4 of counter e // 4
+    return (words >= np.uint64(dropout_threshold(p))).reshape(M, inp)
 
 
 def forward_dropout64(wb, x, a, b, scale: float, keep, p: float):

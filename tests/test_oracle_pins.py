@@ -346,7 +346,20 @@ def test_dropout_threshold_and_keep_rate():
     a = O.dropout_keep(8, 128, 0.3, 1)
     assert np.array_equal(a, O.dropout_keep(8, 128, 0.3, 1))        # deterministic in the seed
     assert not np.array_equal(a, O.dropout_keep(8, 128, 0.3, 2))    # and depends on it
-    assert np.array_equal(a[:4], O.dropout_keep(4, 128, 0.3, 1))     # element (m, k) is counter m*in + k
+    assert np.array_equal(a[:4], O.dropout_keep(4, 128, 0.3, 1))     # element (m, k) depends on m*in + k only
+    assert np.array_equal(a.reshape(-1)[:10], O.dropout_keep(1, 10, 0.3, 1)[0])  # also for a ragged tail
+
+
+def test_dropout_element_uses_one_word_of_its_counter():
+    """Element e of the flattened input is decided by output word e mod 4 of
+    the generator at counter floor(e/4): checked one element at a time,
+    against single calls of the generator, with a 64-bit seed."""
+    seed, p = (5 << 32) | 77, 0.4
+    thr = O.dropout_threshold(p)
+    keep = O.dropout_keep(6, 64, p, seed).reshape(-1)
+    for e in (0, 1, 2, 3, 4, 7, 63, 64, 201, 383):
+        w = O.philox4x32_10([[e // 4, 0, 0, 0]], [[77, 5]])[0]
+        assert keep[e] == (int(w[e % 4]) >= thr)
 
 
 def test_dropout_p0_is_the_plain_layer():

@@ -192,11 +192,13 @@ size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int3
     if (rows < 0 || cols < 0 || M < 0 || r < 0 || r > 256) return 0;
     const size_t base = nf4::workspace_bytes(op & ~(QLORA_OP_BLOCK128 | QLORA_OP_DROPOUT), rows, cols, M, r,
                                              n_adapters);
-    // dropout: xd bf16 [M][in]; the backward also the fp32 dH Wb [M][in]
+    // dropout: xd bf16 [M][in]; the backward also the fp32 dH Wb [M][in] and the keep bits
     const int base_op = op & ~(QLORA_OP_BLOCK128 | QLORA_OP_DROPOUT);
+    const size_t mk = size_t(M) * size_t(cols);
     const size_t xd = (op & QLORA_OP_DROPOUT)
-                          ? (size_t(M) * size_t(cols) * 2 + 255) / 256 * 256 +
-                                (base_op == QLORA_OP_BACKWARD ? (size_t(M) * size_t(cols) * 4 + 255) / 256 * 256 : 0)
+                          ? (mk * 2 + 255) / 256 * 256 +
+                                (base_op == QLORA_OP_BACKWARD ? (mk * 4 + 255) / 256 * 256 + (mk / 8 + 255) / 256 * 256
+                                                              : 0)
                           : 0;
     return ((op & QLORA_OP_BLOCK128) ? expand_bytes(rows, cols) : 0) + xd + base;
 }
@@ -267,16 +269,19 @@ namespace {
 // The dropout settings: the keep threshold and 1/(1 - p); p in [0, 1).
 bool dropout_ok(const qlora_dropout* d) { return d && isfinite(d->p) && d->p >= 0.0f && d->p < 1.0f; }
 
-// xd = keep * x at the front of the workspace (after a block-128 expansion).
+// xd = keep * x at the front of the workspace (after a block-128 expansion);
+// with `bits`, the keep bits (M*cols/8 bytes) right after it.
 int dropout_input(const qlora_dropout* d, const uint16_t* x, int64_t M, int64_t cols, void** ws, size_t* ws_bytes,
-                  hipStream_t st, uint16_t** xd) {
+                  hipStream_t st, uint16_t** xd, uint8_t** bits) {
     const size_t xb = (size_t(M) * size_t(cols) * 2 + 255) / 256 * 256;
-    if (!*ws || *ws_bytes < xb || !al16(*ws)) return NF4_EWORKSPACE;
+    const size_t bb = bits ? (size_t(M) * size_t(cols) / 8 + 255) / 256 * 256 : 0;
+    if (!*ws || *ws_bytes < xb + bb || !al16(*ws)) return NF4_EWORKSPACE;
     *xd = static_cast<uint16_t*>(*ws);
-    const int rc = nf4::dropout_x(x, M, cols, nf4::dropout_threshold(d->p), d->seed, *xd, st);
+    if (bits) *bits = static_cast<uint8_t*>(*ws) + xb;
+    const int rc = nf4::dropout_x(x, M, cols, nf4::dropout_threshold(d->p), d->seed, *xd, bits ? *bits : nullptr, st);
     if (rc) return rc;
-    *ws = static_cast<char*>(*ws) + xb;
-    *ws_bytes -= xb;
+    *ws = static_cast<char*>(*ws) + xb + bb;
+    *ws_bytes -= xb + bb;
     return NF4_OK;
 }
 
@@ -300,7 +305,7 @@ int qlora_linear_forward_dropout(const nf4_tensor* W, const uint16_t* x, int64_t
     if ((rc = layer_view(&v, &ws, &ws_bytes, st))) return rc;
     if (r == 0) return nf4::forward_impl(v, x, M, A, B, 0, scale, h, nullptr, ws, ws_bytes, st);
     uint16_t* xd;
-    if ((rc = dropout_input(drop, x, M, v.cols, &ws, &ws_bytes, st, &xd))) return rc;
+    if ((rc = dropout_input(drop, x, M, v.cols, &ws, &ws_bytes, st, &xd, nullptr))) return rc;
     const float ik = float(1.0 / (1.0 - double(drop->p)));
     if ((rc = nf4::forward_impl(v, x, M, A, B, r, scale * ik, h, u_out, ws, ws_bytes, st, xd))) return rc;
     return u_out ? nf4::scale_f32(u_out, M * r, ik, st) : NF4_OK;
@@ -328,14 +333,14 @@ int qlora_linear_backward_dropout(const nf4_tensor* W, const uint16_t* x, const 
     }
     if ((rc = layer_view(&v, &ws, &ws_bytes, st))) return rc;
     uint16_t* xd;
-    if ((rc = dropout_input(drop, x, M, v.cols, &ws, &ws_bytes, st, &xd))) return rc;
+    uint8_t* bits;
+    if ((rc = dropout_input(drop, x, M, v.cols, &ws, &ws_bytes, st, &xd, &bits))) return rc;
     const size_t fb = (size_t(M) * size_t(v.cols) * 4 + 255) / 256 * 256;  // fp32 dH Wb
     if (ws_bytes < fb) return NF4_EWORKSPACE;
     float* dxf = static_cast<float*>(ws);
     ws = static_cast<char*>(ws) + fb;
     ws_bytes -= fb;
-    const nf4::BwdDropout bd{xd, dxf, float(1.0 / (1.0 - double(drop->p))), nf4::dropout_threshold(drop->p),
-                             drop->seed};
+    const nf4::BwdDropout bd{xd, dxf, bits, float(1.0 / (1.0 - double(drop->p)))};
     return nf4::backward_impl(v, x, dH, M, A, B, r, scale, u, dX, dA, dB, ws, ws_bytes, st, &bd);
 }
 

@@ -772,8 +772,7 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
                       LdRowMajor{duext, M, KL, KL, true}, LdDupCols{A, in, r}, KL, OutBF16{dX, in}, 1,
                       true);
         if (rc) return rc;
-        if (drop && (rc = dx_dropout_add(dX, dxp, Zdx, du, A, M, in, r, drop->thr, drop->seed, drop->inv_keep, st)))
-            return rc;
+        if (drop && (rc = dx_dropout_add(dX, dxp, Zdx, du, A, drop->bits, M, in, r, drop->inv_keep, st))) return rc;
     }
     return NF4_OK;
 }

@@ -85,13 +85,13 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
 }
 
 // Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
-// numbers: as easy as 1, 2, 3", SC 2011), first output word, for the counter
-// (lo, hi of idx, 0, 0) and the key (lo, hi of seed).  Each round forms the
-// 64-bit products of words 0 and 2 with the two multipliers; the new words
-// are (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)), and
-// the key advances by the two increments between rounds.
-__device__ __forceinline__ uint32_t philox_w0(uint64_t idx, uint64_t seed) {
-    uint32_t c0 = uint32_t(idx), c1 = uint32_t(idx >> 32), c2 = 0u, c3 = 0u;
+// numbers: as easy as 1, 2, 3", SC 2011): the four output words for the
+// counter (lo, hi of ctr, 0, 0) and the key (lo, hi of seed).  Each round
+// forms the 64-bit products of words 0 and 2 with the two multipliers; the
+// new words are (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)), and the key advances by the two increments between rounds.
+__device__ __forceinline__ uint4 philox4(uint64_t ctr, uint64_t seed) {
+    uint32_t c0 = uint32_t(ctr), c1 = uint32_t(ctr >> 32), c2 = 0u, c3 = 0u;
     uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
 #pragma unroll
     for (int rnd = 0; rnd < 10; ++rnd) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ uint32_t philox_w0(uint64_t idx, uint64_t seed) {
         c2 = hi0 ^ c3 ^ k1;
         c3 = lo0;
     }
-    return c0;
+    return make_uint4(c0, c1, c2, c3);
 }
 
 }  // namespace nf4dev

@@ -49,9 +49,8 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
 struct BwdDropout {
     const uint16_t* xd;
     float* dxf;  // [M][in] fp32: dH Wb, before the masked term and the one rounding
+    const uint8_t* bits;  // keep bits of x, M*in/8 bytes
     float inv_keep;
-    uint32_t thr;
-    uint64_t seed;
 };
 int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t M,
                   const uint16_t* A, const uint16_t* B, int r, float scale, const float* u,
@@ -59,10 +58,12 @@ int backward_impl(const QView& q, const uint16_t* x, const uint16_t* dH, int64_t
                   const BwdDropout* drop = nullptr);
 // dropout.hip
 uint32_t dropout_threshold(float p);  // ceil(p 2^32)
-int dropout_x(const uint16_t* x, int64_t M, int64_t K, uint32_t thr, uint64_t seed, uint16_t* xd, hipStream_t st);
+// bits: null, or M*K/8 bytes of keep bits (byte i: elements 8i .. 8i + 7, bit b for 8i + b)
+int dropout_x(const uint16_t* x, int64_t M, int64_t K, uint32_t thr, uint64_t seed, uint16_t* xd, uint8_t* bits,
+              hipStream_t st);
 int scale_f32(float* v, int64_t n, float f, hipStream_t st);
-int dx_dropout_add(uint16_t* dx, const float* part, int Z, const float* du, const uint16_t* A, int64_t M, int64_t K,
-                   int r, uint32_t thr, uint64_t seed, float f, hipStream_t st);
+int dx_dropout_add(uint16_t* dx, const float* part, int Z, const float* du, const uint16_t* A, const uint8_t* bits,
+                   int64_t M, int64_t K, int r, float f, hipStream_t st);
 // Profiling hook: the caller's events (or null) that bracket the dominant
 // kernel of a call, attached to kernel dispatches (hipExtLaunchKernelGGL).
 // The kernel launched just before the dominant one, when launched with

@@ -150,7 +150,7 @@ enum {
     QLORA_OP_FORWARD_MULTI = 3,
     QLORA_OP_BLOCK128 = 0x100,  /* OR'ed in: the weight has 128-element blocks */
     QLORA_OP_DROPOUT = 0x200    /* OR'ed in: the *_dropout calls (M*in*2 bytes more, the backward
-                                   M*in*6, each part rounded to 256) */
+                                   M*in*6 + M*in/8, each part rounded to 256) */
 };
 size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int32_t r,
                              int32_t n_adapters);

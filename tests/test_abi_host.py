@@ -159,7 +159,7 @@ def test_block128_layer_calls(F):
 def test_dropout_argument_errors(F):
     """A dropout rate outside [0, 1) or no settings at all is refused before
     anything is launched; the dropout workspace holds xd (M*in bf16) and, in
-    the backward, the fp32 dH Wb (M*in fp32)."""
+    the backward, the fp32 dH Wb (M*in fp32) and the keep bits (M*in/8 bytes)."""
     lib = F._lib
     t = _tensor(F)
     fwd = lambda d: lib.qlora_linear_forward_dropout(C.byref(t), FAKE, 4, FAKE, FAKE, 4, 2.0, d, FAKE, None,
@@ -171,11 +171,11 @@ def test_dropout_argument_errors(F):
         assert fwd(C.byref(d)) == F.NF4_EINVAL
         assert bwd(C.byref(d)) == F.NF4_EINVAL
     assert fwd(None) == F.NF4_EINVAL and bwd(None) == F.NF4_EINVAL
-    for op, per in ((F.QLORA_OP_FORWARD, 2), (F.QLORA_OP_BACKWARD, 6)):
+    for op, extra in ((F.QLORA_OP_FORWARD, 600 * 256 * 2), (F.QLORA_OP_BACKWARD, 600 * 256 * (6 + 1 / 8))):
         base = F.qlora_workspace_bytes(op, 128, 256, 600, 8)
-        assert F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT, 128, 256, 600, 8) == base + 600 * 256 * per
+        assert F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT, 128, 256, 600, 8) == base + extra
         both = F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT | F.QLORA_OP_BLOCK128, 128, 256, 600, 8)
-        assert both == base + 600 * 256 * per + 128 * 256 // 16
+        assert both == base + extra + 128 * 256 // 16
 
 
 def test_workspace_sizes_are_monotone(F):

@@ -462,11 +462,11 @@ def main():
             "train_7b_frac_mfma_peak": round(f7 / (t_7b128 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "dropout": {
-            "workload": "training passes with dropout p=%g on the adapter input (keep decisions from "
-                        "Philox-4x32-10, a new seed every step)" % P_DROP,
-            "train_70b_ms": round(t_trd, 4),
-            "train_70b_TFLOPs": round((ffwd + fbwd) / (t_trd * 1e-3) / 1e12, 2),
-            "train_70b_vs_p0": round(t_trd / t_tr, 4),
+            "workload": "the training pass (M=%d) and the 7B training pass with dropout p=%g on the adapter "
+                        "input (keep decisions from Philox-4x32-10, a new seed every step)" % (Mtrain, P_DROP),
+            "train_ms": round(t_trd, 4),
+            "train_TFLOPs": round((ffwd + fbwd) / (t_trd * 1e-3) / 1e12, 2),
+            "train_vs_p0": round(t_trd / t_tr, 4),
             "train_7b_ms": round(t_7bd, 4),
             "train_7b_TFLOPs": round(f7 / (t_7bd * 1e-3) / 1e12, 2),
             "train_7b_vs_p0": round(t_7bd / t_7b, 4),

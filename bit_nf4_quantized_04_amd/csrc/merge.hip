@@ -11,10 +11,13 @@
 // bf16 MFMA in chunks of 64 adapter rows: the B rows of a slab (64 x 64) and
 // the A rows (64 x 256, staged once for all four slabs when r <= 64) sit in
 // LDS with zero padding past r; the A operand (rows of B) is read row-wise,
-// the B operand (columns of A) transposed with ds_read_b64_tr_b16.  The epilogue goes through LDS one 32-row half at a
-// time, so that each thread finishes eight consecutive columns of a row: one
-// code dword, one block scale, a 16-byte store.  The time is in streaming the
-// codes in and the bf16 weight out.
+// the B operand (columns of A) transposed with ds_read_b64_tr_b16.  The
+// epilogue goes through LDS one 32-row half at a time, so that each thread
+// finishes eight consecutive columns of a row: one code dword, one block
+// scale, a 16-byte store.  The time is in streaming the codes in and the bf16
+// weight out, so the epilogue's code and scale loads of a slab are issued
+// with its B staging (one memory round trip per slab), and the workgroup
+// barriers wait for LDS only, leaving the stores and those loads in flight.
 #include "nf4_device.h"
 #include "nf4_internal.h"
 
@@ -35,8 +38,13 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f
                                                     c, 0, 0, 0);
 }
 
+// Workgroup barrier for LDS hazards only: the wave's LDS operations are
+// complete, global loads and stores may still be in flight (the compiler
+// waits for a load where its value is used).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool DQ, bool GSH>
-__global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_merge(nf4::QView q, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ B, int r, float scale,
                                                uint16_t* __restrict__ W_out) {
     __shared__ __attribute__((aligned(16))) uint16_t at[MG_KC * MG_AS];   // A chunk
@@ -59,19 +67,61 @@ __global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __r
     const bool bvec = (r & 7) == 0;        // 16-byte rows of B
     const char* codes = reinterpret_cast<const char*>(q.codes);
 
-    auto stage_a = [&](int kc) {  // A rows [kc, kc + 64) x the tile's 256 columns
-        for (int e = tid; e < MG_KC * (MG_COLS / 8); e += 256) {
-            const int kr = e >> 5, ch = e & 31;
-            const int64_t col = i0 + 8 * ch;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (kc + kr < r && col < K) v = *reinterpret_cast<const uint4*>(A + int64_t(kc + kr) * K + col);
-            *reinterpret_cast<uint4*>(at + kr * MG_AS + 8 * ch) = v;
+    // Staging loops have fixed trip counts and load from clamped (valid)
+    // addresses, the values past r or K replaced by zeros afterwards, so all
+    // of a loop's loads are in flight together before its LDS writes.
+    // (component-wise, so that the staged values stay in registers)
+    auto keep4 = [](bool ok, const uint4& v) {
+        return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+    };
+    auto stage_a = [&](int kc) {  // A rows [kc, kc + 64) x the tile's 256 columns, in two passes
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            uint4 v[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int e = tid + 256 * (4 * ps + it), kr = e >> 5, ch = e & 31;
+                const int64_t col = i0 + 8 * ch;
+                const int64_t rr = kc + kr < r ? kc + kr : r - 1, cc = col < K ? col : K - 8;
+                v[it] = *reinterpret_cast<const uint4*>(A + rr * K + cc);
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int e = tid + 256 * (4 * ps + it), kr = e >> 5, ch = e & 31;
+                const bool ok = kc + kr < r && i0 + 8 * ch < K;
+                *reinterpret_cast<uint4*>(at + kr * MG_AS + 8 * ch) = keep4(ok, v[it]);
+            }
         }
     };
 
     for (int sb = 0; sb < MG_SLABS; ++sb) {
         const int64_t o0 = r0 + int64_t(sb) * MG_ROWS;
         if (o0 >= N) break;  // workgroup-uniform
+        // the epilogue's loads: item tid + 256k of half hf is row (item >> 5)
+        // of the half, columns 8 (item & 31) .. + 7
+        uint32_t pcd[2][4];
+        int pq[2][4];
+        float pg[2][4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int item = tid + 256 * k;
+                // clamped to a valid element: the values of items past N or K are not used
+                int64_t o = o0 + 32 * hf + (item >> 5), col = i0 + 8 * (item & 31);
+                o = o < N ? o : N - 1;
+                col = col < K ? col : K - 8;
+                const int64_t el = o * K + col;
+                pcd[hf][k] = *reinterpret_cast<const uint32_t*>(codes + el / 2);
+                const int64_t b = el >> q.bshift;
+                if (DQ) {
+                    pq[hf][k] = q.qcodes[b];
+                    pg[hf][k] = q.gabs[GSH ? (b >> q.gshift) : (b / q.group)];
+                } else {
+                    pq[hf][k] = 0;
+                    pg[hf][k] = q.absmax[b];
+                }
+            }
         f32x16_t acc[2][2];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -81,27 +131,39 @@ __global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __r
                 for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
         for (int kc = 0; kc < rpad; kc += MG_KC) {
-            __syncthreads();  // the previous chunk's (or slab's) reads are done
+            lds_barrier();  // the previous chunk's (or slab's) reads are done
             if (!one_chunk || sb == 0) stage_a(kc);
             // B rows [o0, o0 + 64) x adapter columns [kc, kc + 64), zero past r
             if (bvec) {
-                for (int e = tid; e < MG_ROWS * (MG_KC / 8); e += 256) {
-                    const int ro = e >> 3, ch = e & 7;
-                    const int64_t o = o0 + ro;
-                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                    if (o < N && kc + 8 * ch < r) v = *reinterpret_cast<const uint4*>(B + o * r + kc + 8 * ch);
-                    *reinterpret_cast<uint4*>(bt + ro * MG_BS + 8 * ch) = v;
+                uint4 v[MG_ROWS * (MG_KC / 8) / 256];
+#pragma unroll
+                for (int it = 0; it < MG_ROWS * (MG_KC / 8) / 256; ++it) {
+                    const int e = tid + 256 * it, ro = e >> 3, ch = e & 7;
+                    const int64_t o = o0 + ro < N ? o0 + ro : N - 1;
+                    const int kk = kc + 8 * ch < r ? kc + 8 * ch : r - 8;
+                    v[it] = *reinterpret_cast<const uint4*>(B + o * r + kk);
+                }
+#pragma unroll
+                for (int it = 0; it < MG_ROWS * (MG_KC / 8) / 256; ++it) {
+                    const int e = tid + 256 * it, ro = e >> 3, ch = e & 7;
+                    const bool ok = o0 + ro < N && kc + 8 * ch < r;
+                    *reinterpret_cast<uint4*>(bt + ro * MG_BS + 8 * ch) = keep4(ok, v[it]);
                 }
             } else {
-                for (int e = tid; e < MG_ROWS * MG_KC; e += 256) {
-                    const int ro = e >> 6, kk = e & 63;
-                    const int64_t o = o0 + ro;
-                    uint16_t v = 0;
-                    if (o < N && kc + kk < r) v = B[o * r + kc + kk];
-                    bt[ro * MG_BS + kk] = v;
+                uint16_t v[MG_ROWS * MG_KC / 256];
+#pragma unroll
+                for (int it = 0; it < MG_ROWS * MG_KC / 256; ++it) {
+                    const int e = tid + 256 * it, ro = e >> 6, kk = e & 63;
+                    const int64_t o = o0 + ro < N ? o0 + ro : N - 1;
+                    v[it] = B[o * r + (kc + kk < r ? kc + kk : r - 1)];
+                }
+#pragma unroll
+                for (int it = 0; it < MG_ROWS * MG_KC / 256; ++it) {
+                    const int e = tid + 256 * it, ro = e >> 6, kk = e & 63;
+                    bt[ro * MG_BS + kk] = (o0 + ro < N && kc + kk < r) ? v[it] : uint16_t(0);
                 }
             }
-            __syncthreads();
+            lds_barrier();
             const int ksteps = (rpad - kc < MG_KC ? rpad - kc : MG_KC) / 16;
             for (int ks = 0; ks < ksteps; ++ks) {
                 // B operand: columns of A, 8 consecutive k per lane from two transposed reads
@@ -133,7 +195,7 @@ __global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __r
         // epilogue of the slab, one 32-row half at a time through LDS
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            if (hf) __syncthreads();  // the previous half is no longer read
+            if (hf) lds_barrier();  // the previous half is no longer read
             // D layout of the 32x32 MFMA: lane holds column lane%32, rows 8(v/4) + 4(lane/32) + v%4
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
@@ -141,7 +203,7 @@ __global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __r
                 for (int v = 0; v < 16; ++v)
                     stg[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * MG_SS + 64 * w + 32 * cb + (lane & 31)] =
                         acc[hf][cb][v];
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int item = tid + 256 * k;  // 32 rows x 32 chunks of 8 columns
@@ -149,15 +211,8 @@ __global__ __launch_bounds__(256) void k_merge(nf4::QView q, const uint16_t* __r
                 const int64_t o = o0 + 32 * hf + row, col = i0 + 8 * ch;
                 if (o >= N || col >= K) continue;
                 const int64_t el = o * K + col;
-                const uint32_t cd = *reinterpret_cast<const uint32_t*>(codes + el / 2);
-                const int64_t b = el >> q.bshift;
-                float s;
-                if (DQ) {
-                    const int64_t g = GSH ? (b >> q.gshift) : (b / q.group);
-                    s = __fmul_rn(q_over_127(q.qcodes[b]), q.gabs[g]);
-                } else {
-                    s = q.absmax[b];
-                }
+                const uint32_t cd = pcd[hf][k];
+                const float s = DQ ? __fmul_rn(q_over_127(pq[hf][k]), pg[hf][k]) : pg[hf][k];
                 const float4 p0 = *reinterpret_cast<const float4*>(stg + row * MG_SS + 8 * ch);
                 const float4 p1 = *reinterpret_cast<const float4*>(stg + row * MG_SS + 8 * ch + 4);
                 const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};

@@ -69,7 +69,28 @@ __global__ __launch_bounds__(256) void k_dx_dropout_add(uint16_t* __restrict__ d
         float acc[DXD_ROWS][2];
 #pragma unroll
         for (int mm = 0; mm < DXD_ROWS; ++mm) acc[mm][0] = acc[mm][1] = 0.0f;
-        for (int j = 0; j < r; ++j) {
+        // four adapter columns per step: the dU values of a row are then four
+        // consecutive floats (one wide scalar load)
+        int j = 0;
+        for (; j + 4 <= r; j += 4) {
+            float a0[4], a1[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                a0[jj] = bf16_f(A[int64_t(j + jj) * K + i]);
+                a1[jj] = bf16_f(A[int64_t(j + jj) * K + i + 1]);
+            }
+#pragma unroll
+            for (int mm = 0; mm < DXD_ROWS; ++mm) {
+                const int64_t m = m0 + mm < M ? m0 + mm : M - 1;  // uniform
+                const float* d = du + m * r + j;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    acc[mm][0] = __builtin_fmaf(d[jj], a0[jj], acc[mm][0]);
+                    acc[mm][1] = __builtin_fmaf(d[jj], a1[jj], acc[mm][1]);
+                }
+            }
+        }
+        for (; j < r; ++j) {
             const float a0 = bf16_f(A[int64_t(j) * K + i]), a1 = bf16_f(A[int64_t(j) * K + i + 1]);
 #pragma unroll
             for (int mm = 0; mm < DXD_ROWS; ++mm) {

@@ -104,8 +104,9 @@ def _check(rc: int, where: str) -> None:
 def _stream(stream=None):
     import torch
 
-    s = torch.cuda.current_stream() if stream is None else stream
-    return C.c_void_p(s.cuda_stream)
+    if stream is None:  # the current stream's raw handle (no Stream object made)
+        return C.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
+    return C.c_void_p(stream.cuda_stream)
 
 
 def _ptr(t):
@@ -268,10 +269,9 @@ def qlora_linear_forward(w: NF4Weight, x, A, B, scale: float, want_u: bool = Fal
     r = 0 if A is None else A.shape[0]
     h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
     u = torch.empty((M, r), dtype=torch.float32, device=x.device) if (want_u and r) else None
-    flags = w.op_flags | (QLORA_OP_DROPOUT if dropout is not None else 0)
-    need = qlora_workspace_bytes(QLORA_OP_FORWARD | flags, w.rows, w.cols, M, r)
-    if ws is None:
-        ws = _workspace(need, x.device)
+    if ws is None:  # (a given workspace is checked by the library)
+        flags = w.op_flags | (QLORA_OP_DROPOUT if dropout is not None else 0)
+        ws = _workspace(qlora_workspace_bytes(QLORA_OP_FORWARD | flags, w.rows, w.cols, M, r), x.device)
     t = w.c_struct()
     if dropout is None:
         _check(_lib.qlora_linear_forward(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale),

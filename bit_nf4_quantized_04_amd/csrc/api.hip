@@ -153,7 +153,9 @@ int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg, size_t*
     return NF4_OK;
 }
 
-int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* cfg, uint8_t* codes,
+namespace {
+
+int quantize_any(const void* W, bool bf16, int64_t rows, int64_t cols, const nf4_config* cfg, uint8_t* codes,
                  float* absmax, int8_t* scale_codes, float* group_absmax, void* stream) {
     if (!cfg) return NF4_EINVAL;
     if (cfg->block_size != 64 && cfg->block_size != 128) return NF4_EUNSUPPORTED;
@@ -165,8 +167,20 @@ int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* c
     if (n == 0) return NF4_OK;
     if (bad_ptr(W) || bad_ptr(codes) || bad_ptr(absmax)) return NF4_EINVAL;
     if (cfg->double_quant && (bad_ptr(scale_codes) || bad_ptr(group_absmax))) return NF4_EINVAL;
-    return nf4::launch_quantize(W, n, cfg->block_size, cfg->double_quant, cfg->dq_group, codes, absmax,
+    return nf4::launch_quantize(W, bf16, n, cfg->block_size, cfg->double_quant, cfg->dq_group, codes, absmax,
                                 scale_codes, group_absmax, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* cfg, uint8_t* codes,
+                 float* absmax, int8_t* scale_codes, float* group_absmax, void* stream) {
+    return quantize_any(W, false, rows, cols, cfg, codes, absmax, scale_codes, group_absmax, stream);
+}
+
+int nf4_quantize_bf16(const uint16_t* W, int64_t rows, int64_t cols, const nf4_config* cfg, uint8_t* codes,
+                      float* absmax, int8_t* scale_codes, float* group_absmax, void* stream) {
+    return quantize_any(W, true, rows, cols, cfg, codes, absmax, scale_codes, group_absmax, stream);
 }
 
 int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream) {

@@ -25,8 +25,9 @@ struct QView {  // a validated nf4_tensor
     int bshift;    // log2(block size): 6 (64 elements) or 7 (128)
 };
 
-int launch_quantize(const float* W, int64_t n, int block, int dq, int group, uint8_t* codes, float* absmax,
-                    int8_t* qcodes, float* gabs, hipStream_t s);
+// W: fp32, or bf16 bit patterns when `bf16`
+int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int group, uint8_t* codes,
+                    float* absmax, int8_t* qcodes, float* gabs, hipStream_t s);
 // Every 64-element half of a 128-element block takes its block's fp32 scale,
 // or with double quant its int8 scale code (the group of dq_group blocks is
 // then 2 dq_group halves), into s64[rows*cols/64]: the layer kernels see a

@@ -31,11 +31,19 @@ __device__ __forceinline__ uint32_t nearest_code(float w) {
     return c;
 }
 
+// Four consecutive input elements as fp32: an fp32 input, or bf16 bit
+// patterns widened exactly.
+__device__ __forceinline__ float4 load4(const float4* W, int64_t i) { return W[i]; }
+__device__ __forceinline__ float4 load4(const uint2* W, int64_t i) {
+    const uint2 p = W[i];
+    return make_float4(bits_f(p.x << 16), bits_f(p.x & 0xffff0000u), bits_f(p.y << 16), bits_f(p.y & 0xffff0000u));
+}
+
 // One thread = 4 consecutive elements; L lanes = one block of 4L elements
 // (16 lanes for 64, 32 for 128).  The absmax is an L-lane butterfly max;
 // codes of 4 elements pack into 2 bytes.
-template <int L>
-__global__ __launch_bounds__(256) void k_quant_blocks(const float4* __restrict__ W, int64_t n4,
+template <int L, typename In>
+__global__ __launch_bounds__(256) void k_quant_blocks(const In* __restrict__ W, int64_t n4,
                                                       uint16_t* __restrict__ codes,
                                                       float* __restrict__ absmax) {
     constexpr int LSH = L == 16 ? 4 : 5;
@@ -43,7 +51,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(const float4* __restrict__
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4; i += stride) {
         // n4 is a multiple of L and so is `stride`: the L lanes of a block
         // enter and leave the loop together.
-        const float4 v = W[i];
+        const float4 v = load4(W, i);
         float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
         for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
@@ -159,13 +167,19 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
 
 namespace nf4 {
 
-int launch_quantize(const float* W, int64_t n, int block, int dq, int group, uint8_t* codes, float* absmax,
-                    int8_t* qcodes, float* gabs, hipStream_t s) {
+int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int group, uint8_t* codes,
+                    float* absmax, int8_t* qcodes, float* gabs, hipStream_t s) {
     const int64_t n4 = n / 4;
-    auto kern = block == 128 ? k_quant_blocks<32> : k_quant_blocks<16>;
-    hipLaunchKernelGGL(kern, dim3(grid_for(n4, 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float4*>(W), n4, reinterpret_cast<uint16_t*>(codes),
-                       absmax);
+    uint16_t* c16 = reinterpret_cast<uint16_t*>(codes);
+    if (bf16) {
+        auto kern = block == 128 ? k_quant_blocks<32, uint2> : k_quant_blocks<16, uint2>;
+        hipLaunchKernelGGL(kern, dim3(grid_for(n4, 256)), dim3(256), 0, s, static_cast<const uint2*>(W), n4, c16,
+                           absmax);
+    } else {
+        auto kern = block == 128 ? k_quant_blocks<32, float4> : k_quant_blocks<16, float4>;
+        hipLaunchKernelGGL(kern, dim3(grid_for(n4, 256)), dim3(256), 0, s, static_cast<const float4*>(W), n4, c16,
+                           absmax);
+    }
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (dq) {
         const int64_t nb = n / block;

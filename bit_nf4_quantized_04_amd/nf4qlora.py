@@ -61,6 +61,7 @@ _SIGS = {
     "nf4_storage_sizes": (C.c_int, [_I64, _I64, C.POINTER(nf4_config), C.POINTER(C.c_size_t),
                                     C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "nf4_quantize": (C.c_int, [_P, _I64, _I64, C.POINTER(nf4_config), _P, _P, _P, _P, _P]),
+    "nf4_quantize_bf16": (C.c_int, [_P, _I64, _I64, C.POINTER(nf4_config), _P, _P, _P, _P, _P]),
     "nf4_dequantize": (C.c_int, [C.POINTER(nf4_tensor), _P, _P]),
     "nf4_dequantize_bf16": (C.c_int, [C.POINTER(nf4_tensor), _P, _P]),
     "qlora_workspace_bytes": (C.c_size_t, [C.c_int, _I64, _I64, _I64, C.c_int32, C.c_int32]),
@@ -213,7 +214,9 @@ class NF4Weight:
 
 
 def nf4_quantize(W, double_quant: bool, dq_group: int = 256, block_size: int = 64, stream=None) -> NF4Weight:
-    """Quantize a contiguous fp32 CUDA tensor [rows, cols] in blocks of 64 or 128."""
+    """Quantize a contiguous fp32 or bf16 CUDA tensor [rows, cols] in blocks of
+    64 or 128 (bf16 through nf4_quantize_bf16: the same codes as its exact fp32
+    values)."""
     import torch
 
     rows, cols = W.shape
@@ -227,8 +230,10 @@ def nf4_quantize(W, double_quant: bool, dq_group: int = 256, block_size: int = 6
         sc = torch.empty(max(nb, 16), dtype=torch.int8, device=dev)
         gab = torch.empty(max((nb + dq_group - 1) // dq_group, 4), dtype=torch.float32, device=dev)
     cfg = nf4_config(block_size, int(double_quant), dq_group)
-    _check(_lib.nf4_quantize(_ptr(W), rows, cols, C.byref(cfg), _ptr(codes), _ptr(absmax),
-                             _ptr(sc), _ptr(gab), _stream(stream)), "nf4_quantize")
+    fn, name = ((_lib.nf4_quantize_bf16, "nf4_quantize_bf16") if W.dtype == torch.bfloat16
+                else (_lib.nf4_quantize, "nf4_quantize"))
+    _check(fn(_ptr(W), rows, cols, C.byref(cfg), _ptr(codes), _ptr(absmax), _ptr(sc), _ptr(gab),
+              _stream(stream)), name)
     return NF4Weight(codes[: n // 2], absmax[:nb], None if sc is None else sc[:nb],
                      None if gab is None else gab[: (nb + dq_group - 1) // dq_group],
                      rows, cols, double_quant, dq_group, block_size)

@@ -131,6 +131,17 @@ int nf4_quantize(const float* W, int64_t rows, int64_t cols, const nf4_config* c
                  uint8_t* codes, float* absmax, int8_t* scale_codes, float* group_absmax,
                  void* stream);
 
+/* Quantize a bf16 matrix (bit patterns [rows, cols], device, 16-byte
+ * aligned): exactly nf4_quantize of its fp32 values (bf16 widens to fp32
+ * without rounding), with the same outputs, contract and errors.  It takes a
+ * merged 16-bit weight (qlora_merge) back to 4-bit storage [P3 "Merging and
+ * deploying": the merged model may be re-quantized to 4 bits for deployment;
+ * the pages name calibration-based GPTQ/AWQ there, this library's reading
+ * uses its own calibration-free NF4 quantizer]. */
+int nf4_quantize_bf16(const uint16_t* W, int64_t rows, int64_t cols, const nf4_config* cfg,
+                      uint8_t* codes, float* absmax, int8_t* scale_codes, float* group_absmax,
+                      void* stream);
+
 /* Dequantize to fp32 [rows, cols]: w~ = fl32(scale_b * NF4[code]) [P1
  * section 2, last item].  Bit-exact contract. */
 int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream);

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(F):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = C.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -68,10 +68,13 @@ def _cfg(F, bs=64, dq=1, g=256):
 FAKE = C.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails validation first
 
 
-def test_quantize_argument_errors(F):
+@pytest.mark.parametrize("entry", ["nf4_quantize", "nf4_quantize_bf16"])
+def test_quantize_argument_errors(F, entry):
+    """Both quantizer entry points (fp32 and bf16 input) validate alike."""
     lib = F._lib
     cfg = _cfg(F)
-    q = lambda W, r, c, cf, codes, ab, sc, ga: lib.nf4_quantize(W, r, c, cf, codes, ab, sc, ga, None)
+    fn = getattr(lib, entry)
+    q = lambda W, r, c, cf, codes, ab, sc, ga: fn(W, r, c, cf, codes, ab, sc, ga, None)
     assert q(None, 64, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
     assert q(FAKE, 64, 64, None, FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
     assert q(FAKE, -1, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL

@@ -490,3 +490,29 @@ def test_70b_workload_full_size_sampled(F):
         U.assert_close("dX cols M=%d" % xx.shape[0], gg[0][:, kcols], dd @ wc + du @ aa[:, kcols])
         U.assert_close("dA M=%d" % xx.shape[0], gg[1], du.T @ xx)
         U.assert_close("dB M=%d" % xx.shape[0], gg[2], s * (dd.T @ u))
+
+
+# The merged 16-bit weight taken back to NF4 storage: nf4_quantize_bf16 of
+# the merge output equals the oracle's quantizer on the same bf16 values
+# (widened exactly to fp32), bit for bit, codes and scales.
+@pytest.mark.parametrize("out,inp,r,dq,bs", [(300, 256, 16, True, 64), (512, 1024, 64, False, 64),
+                                             (96, 320, 8, True, 128)])
+def test_merged_weight_requantized(F, out, inp, r, dq, bs):
+    import torch
+
+    rng = np.random.default_rng(out + inp + r)
+    w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
+    a = O.rne_bf16_bits((rng.standard_normal((r, inp)) * np.sqrt(2.0 / inp)).astype(np.float32))
+    b = O.rne_bf16_bits((rng.standard_normal((out, r)) * 0.01).astype(np.float32))
+    q = F.nf4_quantize(U.f32(w), double_quant=dq, block_size=bs)
+    wm = F.qlora_merge(q, U.bf(a), U.bf(b), 2.0)
+    q2 = F.nf4_quantize(wm, double_quant=dq, block_size=bs)
+    torch.cuda.synchronize()
+    wm_f32 = O.bf16_bits_to_f32(wm.view(torch.int16).cpu().numpy().view(np.uint16))
+    ref = O.quantize(wm_f32, double_quant=dq, block_size=bs)
+    np.testing.assert_array_equal(q2.codes.cpu().numpy(), ref["codes"])
+    np.testing.assert_array_equal(q2.absmax.cpu().numpy().view(np.uint32), ref["absmax"].view(np.uint32))
+    if dq:
+        np.testing.assert_array_equal(q2.scale_codes.cpu().numpy(), ref["scale_codes"])
+        np.testing.assert_array_equal(q2.group_absmax.cpu().numpy().view(np.uint32),
+                                      ref["group_absmax"].view(np.uint32))

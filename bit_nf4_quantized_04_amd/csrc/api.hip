@@ -230,7 +230,9 @@ int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M, cons
     if (r > 0 && (bad_ptr(A) || bad_ptr(B))) return NF4_EINVAL;
     if (u_out && !al16(u_out)) return NF4_EINVAL;
     if (v.cols == 0) return NF4_EINVAL;
-    if ((rc = layer_view(&v, &ws, &ws_bytes, static_cast<hipStream_t>(stream)))) return rc;
+    // (the single-token kernel reads the scales of 128-element blocks as they are)
+    if (!nf4::gemv1_takes(v, M, r) && (rc = layer_view(&v, &ws, &ws_bytes, static_cast<hipStream_t>(stream))))
+        return rc;
     return nf4::forward_impl(v, x, M, A, B, r, scale, h, r > 0 ? u_out : nullptr, ws, ws_bytes,
                              static_cast<hipStream_t>(stream));
 }

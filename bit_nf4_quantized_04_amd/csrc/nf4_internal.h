@@ -107,6 +107,7 @@ void launch_dominant(Kernel kernel, dim3 grid, dim3 block, size_t shmem, hipStre
 constexpr int64_t kSkinnyMaxM = 16;
 constexpr int kSkinnyMaxR = 64;
 size_t skinny_ws_bytes(int64_t M, int r);
+bool gemv1_takes(const QView& q, int64_t M, int r);  // M = 1 kernel; it accepts bshift 6 or 7
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                    int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st,
                    const uint16_t* xl = nullptr);

@@ -282,7 +282,9 @@ __device__ __forceinline__ float lane_val(float v, int lane) {
 // neighbouring rows, and no counter or atomic is involved.
 constexpr int G1_NC = 3;  // rows per wave per chunk (and fetch ring slots)
 
-template <bool DQ, bool GSH>
+// SH: log2(block size / 64), 0 or 1 (the scales of 128-element blocks are
+// read as they are, one per two of the lanes' 64-element halves).
+template <bool DQ, bool GSH, int SH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv1(
     nf4::QView q, const uint16_t* __restrict__ x, const float* __restrict__ upart, int r,
     const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
@@ -349,7 +351,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const uint32_t off = crow * row_bytes + lane_bytes;
         f.c0 = *reinterpret_cast<const uint4*>(codes + off);
         f.c1 = *reinterpret_cast<const uint4*>(codes + off + 16u);
-        const uint32_t b = crow * uint32_t(nkb) + uint32_t(cb);
+        // the lane's 64-element half-block, and the index of its scale: the
+        // block itself, or with blocks of 128 the block holding the half
+        const uint32_t b = (crow * uint32_t(nkb) + uint32_t(cb)) >> SH;
         if (DQ) {
             const uint32_t gi = GSH ? (b >> q.gshift) : (b / uint32_t(q.group));
             f.qb = uint32_t(uint8_t(q.qcodes[b]));
@@ -491,20 +495,31 @@ size_t skinny_ws_bytes(int64_t M, int r) {
     return align256(size_t(DOWN_SPLIT) * size_t(M) * (r > 0 ? r : 0) * 4);
 }
 
+// The single-token product runs in k_gemv1 (the one kernel here that also
+// reads the scales of 128-element blocks directly).
+bool gemv1_takes(const QView& q, int64_t M, int r) {
+    const int64_t nkb = q.cols / 64;
+    // (32-bit byte offsets inside the kernel: codes under 4 GB)
+    return M == 1 && r <= kSkinnyMaxR && r <= 64 && nkb <= 256 && q.rows * q.cols / 2 < (int64_t(1) << 32);
+}
+
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
                    int r, float scale, uint16_t* h, float* u_out, char* ws, hipStream_t st, const uint16_t* xl) {
     float* part = reinterpret_cast<float*>(ws);
     const int64_t nkb = q.cols / 64;
     const int R = nkb <= 64 ? 1 : nkb <= 128 ? 2 : nkb <= 256 ? 4 : 0;
-    // (32-bit byte offsets inside the M = 1 kernel: codes under 4 GB)
-    const bool gemv1 = M == 1 && R > 0 && r <= 64 && q.rows * q.cols / 2 < (int64_t(1) << 32);
+    const bool gemv1 = gemv1_takes(q, M, r);
+    if (!gemv1 && q.bshift != 6) return NF4_EINVAL;  // the other kernels take 64-element scales only
     launch_before_dominant(k_down_small, dim3(unsigned(std::max<int64_t>(1, cdiv(r, 16))), DOWN_SPLIT),
                            dim3(256), 0, st, xl ? xl : x, int(M), q.cols, A, r, part);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (gemv1) {
-        auto kern = q.dq ? (q.gshift >= 0 ? k_gemv1<true, true> : k_gemv1<true, false>)
-                         : k_gemv1<false, true>;
-        const int slot = q.dq ? (q.gshift >= 0 ? 0 : 1) : 2;
+        const bool b128 = q.bshift == 7;
+        auto kern = b128 ? (q.dq ? (q.gshift >= 0 ? k_gemv1<true, true, 1> : k_gemv1<true, false, 1>)
+                                 : k_gemv1<false, true, 1>)
+                         : (q.dq ? (q.gshift >= 0 ? k_gemv1<true, true, 0> : k_gemv1<true, false, 0>)
+                                 : k_gemv1<false, true, 0>);
+        const int slot = (q.dq ? (q.gshift >= 0 ? 0 : 1) : 2) + (b128 ? 3 : 0);
         const int64_t rows_chunk = (4 / R) * G1_NC;
         const int64_t nchunks = cdiv(q.rows, rows_chunk);
         const int64_t grid = std::min<int64_t>(nchunks, resident_wgs(kern, 256, slot));

@@ -74,6 +74,8 @@ def test_quantize_dequantize_match_oracle(F, shape, dq, group):
 LAYER = [  # (M, out, in, r, dq, group)
     (1, 4096, 1024, 64, True, 256),     # decode GEMV
     (1, 512, 192, 8, False, 256),       # decode GEMV, blocks straddle rows
+    (1, 300, 8192, 16, True, 100),      # decode GEMV, two regions per row, group not a power of two
+    (1, 260, 2112, 32, True, 256),      # decode GEMV, double quant, blocks straddle rows
     (5, 256, 192, 8, True, 100),        # few tokens
     (40, 300, 384, 16, True, 256),      # tiled kernels, ragged out
     (40, 300, 384, 16, True, 10**6),    # one global constant

@@ -439,6 +439,7 @@ __global__ __launch_bounds__(256) void k_zero(float* __restrict__ p, int64_t n) 
 
 // --------------------------------------------------------------- planning
 inline int choose_splits(int64_t tiles, int64_t ksteps) {
+    if (tiles < 1) tiles = 1;  // (no tokens: a workspace query)
     int64_t z = (1024 + tiles - 1) / tiles;
     if (z > ksteps) z = ksteps;
     if (z > 64) z = 64;

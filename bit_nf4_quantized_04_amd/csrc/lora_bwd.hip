@@ -418,7 +418,7 @@ namespace nf4 {
 int nt_splits(int64_t M, int64_t K) {
     const int64_t slabs = cdiv(K, NT_SLAB);
     if (slabs < 8) return int(slabs);
-    const int64_t tiles = cdiv(M, NT_ROWS);
+    const int64_t tiles = std::max<int64_t>(1, cdiv(M, NT_ROWS));  // (M = 0: a workspace query)
     return int(8 * std::max<int64_t>(1, std::min<int64_t>(cdiv(512, 8 * tiles), slabs / 8)));
 }
 int64_t nt_chunk(int64_t K, int Z) { return cdiv(cdiv(K, Z), NT_SLAB) * NT_SLAB; }
@@ -427,7 +427,7 @@ int64_t nt_chunk(int64_t K, int Z) { return cdiv(cdiv(K, Z), NT_SLAB) * NT_SLAB;
 int64_t tn_chunk(int64_t RR, int64_t M) {
     const int64_t tiles = cdiv(RR, TN_COLS);
     const int64_t z = std::max<int64_t>(1, std::min<int64_t>(cdiv(512, tiles), cdiv(M, 64)));
-    return cdiv(cdiv(M, z), 64) * 64;
+    return std::max<int64_t>(1, cdiv(cdiv(M, z), 64)) * 64;  // (at least one step: M = 0 in a query)
 }
 int tn_splits(int64_t RR, int64_t M) { return int(cdiv(M, tn_chunk(RR, M))); }
 

@@ -208,3 +208,13 @@ def test_adamw_and_merge_argument_errors(F):
     assert mg(t, 4, None) == F.NF4_EINVAL
     assert mg(_tensor(F, codes=None), 4, FAKE) == F.NF4_EINVAL
 
+
+
+def test_workspace_queries_without_tokens(F):
+    """M = 0 is a valid call (a no-op forward, zero dA and dB): every
+    workspace query answers it, for the split plans of both adapter-product
+    schemes (r <= 64 with rows % 16 == 0, and r > 64) and long reductions."""
+    for rows, cols, r in ((128, 256, 8), (28672, 8192, 64), (300, 512, 256), (4096, 4096, 100)):
+        for op in (F.QLORA_OP_FORWARD, F.QLORA_OP_BACKWARD, F.QLORA_OP_FORWARD_MULTI,
+                   F.QLORA_OP_BACKWARD | F.QLORA_OP_DROPOUT, F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128):
+            assert F.qlora_workspace_bytes(op, rows, cols, 0, r, 4) >= 0

@@ -516,3 +516,55 @@ def test_merged_weight_requantized(F, out, inp, r, dq, bs):
         np.testing.assert_array_equal(q2.scale_codes.cpu().numpy(), ref["scale_codes"])
         np.testing.assert_array_equal(q2.group_absmax.cpu().numpy().view(np.uint32),
                                       ref["group_absmax"].view(np.uint32))
+
+
+# The largest accepted rank (256) through every layer call, on a few tokens
+# (general path) and one token.
+@pytest.mark.parametrize("M", [1, 40])
+def test_largest_rank(F, M):
+    import torch
+
+    out, inp, r, s = 300, 512, 256, 0.25
+    w, x, a, b, dh = _case(4242 + M, M, out, inp, r)
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    h, u = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), s, want_u=True)
+    dX, dA, dB = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), s, u=u)
+    hd, ud = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), s, want_u=True, dropout=(0.1, 9))
+    gd = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), s, u=ud, dropout=(0.1, 9))
+    wm = F.qlora_merge(q, U.bf(a), U.bf(b), s)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    href, uref = O.forward(wb, x, a, b, s)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+    U.assert_close("u", u.cpu().numpy(), uref)
+    g = O.backward(wb, x, dh, a, b, s)
+    U.assert_close("dX", U.bf16_to_f64(dX), g["dX"])
+    U.assert_close("dA", dA.cpu().numpy(), g["dA"])
+    U.assert_close("dB", dB.cpu().numpy(), g["dB"])
+    keep = O.dropout_keep(M, inp, 0.1, 9)
+    xf, af, bf_, dhf = O._bf(x), O._bf(a), O._bf(b), O._bf(dh)
+    hdr, udr = O.forward_dropout64(wb, xf, af, bf_, s, keep, 0.1)
+    U.assert_close("h dropout", U.bf16_to_f64(hd), hdr)
+    U.assert_close("u dropout", ud.cpu().numpy(), udr)
+    gdr = O.backward_dropout64(wb, xf, dhf, af, bf_, s, keep, 0.1)
+    U.assert_close("dX dropout", U.bf16_to_f64(gd[0]), gdr["dX"])
+    U.assert_close("dA dropout", gd[1].cpu().numpy(), gdr["dA"])
+    U.assert_close("dB dropout", gd[2].cpu().numpy(), gdr["dB"])
+    U.assert_close("merged", U.bf16_to_f64(wm), O.bf16_bits_to_f32(O.merge(wb, a, b, s)).astype(np.float64))
+
+
+# No tokens: the forward writes nothing, the backward gives zero dA and dB.
+def test_no_tokens(F):
+    import torch
+
+    out, inp, r = 128, 256, 8
+    w, x, a, b, dh = _case(77, 1, out, inp, r)
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    x0 = torch.empty((0, inp), dtype=torch.bfloat16, device=U.dev())
+    dh0 = torch.empty((0, out), dtype=torch.bfloat16, device=U.dev())
+    h = F.qlora_linear_forward(q, x0, U.bf(a), U.bf(b), 2.0)
+    assert tuple(h.shape) == (0, out)
+    dX, dA, dB = F.qlora_linear_backward(q, x0, dh0, U.bf(a), U.bf(b), 2.0)
+    torch.cuda.synchronize()
+    assert tuple(dX.shape) == (0, inp)
+    assert torch.count_nonzero(dA).item() == 0 and torch.count_nonzero(dB).item() == 0

@@ -146,3 +146,36 @@ def test_merge(F, out, inp, r, dq, group):
     np.testing.assert_array_equal(wz.view(torch.int16).cpu().numpy().view(np.uint16),
                                   O.rne_bf16_bits(O.dequantize(_ref_q(w, dq, group), w.shape, block_size=BS,
                                                                dq_group=group)))
+
+
+# Dropout on the adapter input with blocks of 128 (the dropout calls expand
+# the scales like the plain layer calls): few tokens, tiled, register-dequant.
+@pytest.mark.parametrize("M,out,inp,r,dq,group,p", [
+    (5, 256, 192, 8, True, 100, 0.3),
+    (40, 300, 384, 16, False, 256, 0.05),
+    (600, 2048, 1024, 64, True, 256, 0.1),
+])
+def test_dropout(F, M, out, inp, r, dq, group, p):
+    import torch
+
+    rng = np.random.default_rng(M * 13 + out + inp)
+    w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
+    x = _bits(rng, (M, inp), 1.0)
+    a = _bits(rng, (r, inp), np.sqrt(2.0 / inp))
+    b = _bits(rng, (out, r), 0.01)
+    dh = _bits(rng, (M, out), 1.0)
+    s, seed = 2.0, 1234 + M
+    q = F.nf4_quantize(U.f32(w), double_quant=dq, dq_group=group, block_size=BS)
+    h, u = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), s, want_u=True, dropout=(p, seed))
+    dX, dA, dB = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), s, u=u, dropout=(p, seed))
+    torch.cuda.synchronize()
+    wb = _ref_wb(w, dq, group)
+    keep = O.dropout_keep(M, inp, p, seed)
+    xf, af, bf_, dhf = O._bf(x), O._bf(a), O._bf(b), O._bf(dh)
+    href, uref = O.forward_dropout64(wb, xf, af, bf_, s, keep, p)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+    U.assert_close("u", u.cpu().numpy(), uref)
+    g = O.backward_dropout64(wb, xf, dhf, af, bf_, s, keep, p)
+    U.assert_close("dX", U.bf16_to_f64(dX), g["dX"])
+    U.assert_close("dA", dA.cpu().numpy(), g["dA"])
+    U.assert_close("dB", dB.cpu().numpy(), g["dB"])

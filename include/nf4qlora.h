@@ -206,12 +206,17 @@ int qlora_linear_backward(const nf4_tensor* W, const uint16_t* x, const uint16_t
  * adapter-branch diagram: h = W0 x + (alpha/r) B(A(dropout(x))); P3
  * "Concrete example: Fine-tuning Llama-3-8B on a 24 GB GPU": lora_dropout =
  * 0.05].  The pages give
- * the rate only; this library's reading: inverted dropout, element (m, k)
- * of x kept iff the first word of Philox-4x32-10 (Salmon, Moraes, Dror,
- * Shaw, SC 2011) with counter (lo, hi of m*in + k, 0, 0) and key (lo, hi of
- * seed) is >= ceil(p * 2^32), kept elements scaled by 1/(1 - p); the base
- * product always reads x.  The same (p, seed) in the backward regenerates the
- * same mask.  p must be finite and in [0, 1) (NF4_EINVAL otherwise). */
+ * the rate only; this library's reading: inverted dropout.  Element (m, k)
+ * of x has flat index e = m*in + k.  One call of Philox-4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, SC 2011) serves four consecutive elements: with
+ * counter (lo, hi of floor(e/4), 0, 0) and key (lo, hi of seed) it returns
+ * four 32-bit words w0..w3, and element e is kept iff word w_(e mod 4) is
+ * >= ceil(p * 2^32).  Kept elements are scaled by 1/(1 - p); the base
+ * product always reads x.  Example: seed = 0, p = 0.5, elements 0..3 of x
+ * are decided by the four words of the counter (0, 0, 0, 0), elements 4..7
+ * by those of the counter (1, 0, 0, 0).  The same (p, seed) in the backward
+ * regenerates the same mask.  p must be finite and in [0, 1) (NF4_EINVAL
+ * otherwise). */
 typedef struct qlora_dropout {
     float p;        /* dropout rate */
     uint32_t pad;   /* unused */

@@ -47,9 +47,12 @@ bf16/fp32 input values.  The code search is an exact arg-min (see
 "READING" in the docstrings.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values
-the pages print, closed forms, brute force or library routines.  The decode of
-the double-quantized scale (``decode_scales``) has no worked value on the
-pages; it is pinned by the round-trip identities only.
+the pages print, closed forms, brute force or library routines.  The double
+quant is pinned to the page's own listing run in torch float32 and, operation
+order included, to exact rational arithmetic at constants other than 1.  The
+decode of the double-quantized scale (``decode_scales``) has no worked value on
+the pages (they print no inverse); its reading is pinned by exact rational
+evaluation over every code and by the round-trip identities.
 """
 
 from __future__ import annotations
@@ -242,9 +245,11 @@ def double_quantize_scales(absmax, group: int = DQ_GROUP):
 def decode_scales(q, c, group: int = DQ_GROUP) -> np.ndarray:
     """s~_b = fl32( fl32(q_b / 127) * c_g ).
 
-    READING (parity unpinned by any worked value on the pages): the pages give
-    no inverse of the scale quantization; this is the step-by-step reverse of
-    ``double_quantize_scales``.  Pinned by round-trip identities in the tests.
+    READING: the pages give no inverse of the scale quantization (no worked
+    value exists); this is the step-by-step reverse of
+    ``double_quantize_scales``, two correctly rounded float32 steps.  Pinned
+    by exact rational evaluation of those two steps for every code 0..127 and
+    constants over the whole float32 range, and by round-trip identities.
     """
     qf = np.asarray(q, dtype=np.int8).astype(np.float32)
     cc = _as_f32(c)

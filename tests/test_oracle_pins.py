@@ -268,6 +268,164 @@ def test_double_quant_rounds_half_to_even():
     assert q.tolist() == [0, 2, 4, 6, 127]
 
 
+def _round_f32_exact(x: Fraction) -> Fraction:
+    """The binary32 value nearest to the exact rational x (ties to even),
+    subnormals included, as an exact Fraction.  Written from the definition:
+    the spacing of binary32 values in [2^e, 2^(e+1)) is 2^(e-23), and below
+    2^-126 it is 2^-149."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * quantum
+
+
+def _rint_half_even(x: Fraction) -> int:
+    lo = x.numerator // x.denominator
+    rem = x - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return lo
+
+
+def test_exact_float32_rounding_helper():
+    """The helper above against float32 values whose neighbours are known."""
+    for v in (1.0, 0.1, 3.0e-39, 1.0e-45, 0.338, 127.0 / 3.0):
+        f = np.float32(v)
+        assert _round_f32_exact(Fraction(float(f))) == Fraction(float(f))
+        up = np.nextafter(f, np.float32(np.inf))
+        mid = (Fraction(float(f)) + Fraction(float(up))) / 2
+        even = f if (int(np.array([f]).view(np.uint32)[0]) % 2 == 0) else up
+        assert _round_f32_exact(mid) == Fraction(float(even))
+        assert _round_f32_exact(mid - Fraction(1, 2 ** 200)) == Fraction(float(f))
+        assert _round_f32_exact(mid + Fraction(1, 2 ** 200)) == Fraction(float(up))
+
+
+@pytest.mark.parametrize("grouped", [True, False])
+def test_double_quant_matches_the_page_listing_in_torch(grouped):
+    """"QLoRA explained", "Double quantization": the scales are divided by
+    their absmax, multiplied by 127, rounded (torch's round, half to even) and
+    cast to int8, all in torch float32.  That listing, run as printed on
+    torch's CPU tensors, against the oracle on 2^22 block scales whose
+    constants are far from 1: in groups of 256 ("From LoRA to QLoRA",
+    "Pillar 2"), and as the listing's single global constant."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    n = 1 << 22
+    ng = n // 256
+    # block absmax values as the first level makes them (the absmax of 64
+    # normal weights is about 2.5 sigma), sigma spread over many binades
+    sigma = 2.0 ** rng.uniform(-14.0, 3.0, ng)
+    s = (np.abs(rng.standard_normal((ng, 256))) * sigma[:, None]).astype(np.float32).reshape(-1)
+    st = torch.from_numpy(s.copy())
+    if grouped:
+        st = st.view(ng, 256)
+        scale_absmax = st.abs().amax(dim=1, keepdim=True)
+        q_page = (st / scale_absmax * 127).round().to(torch.int8).reshape(-1).numpy()
+        c_page = scale_absmax.reshape(-1).numpy()
+        q, c = O.double_quantize_scales(s, 256)
+    else:
+        scale_absmax = st.abs().max()
+        q_page = (st / scale_absmax * 127).round().to(torch.int8).numpy()
+        c_page = np.array([scale_absmax.item()], dtype=np.float32)
+        q, c = O.double_quantize_scales(s, n)
+    assert not np.any(c == 1.0)
+    np.testing.assert_array_equal(c, c_page)
+    np.testing.assert_array_equal(q, q_page)
+
+
+def _dq_pairs_where_the_page_orders_differ(n_wanted=5):
+    """Scale / constant pairs (c != 1) on which dividing first ("QLoRA
+    explained") and forming 127/c first ("From LoRA to QLoRA", "Vanilla
+    Uniform Quantization") give different codes."""
+    rng = np.random.default_rng(42)
+    c = (rng.uniform(1.0, 2.0, 4_000_000) * 2.0 ** rng.integers(-12, 3, 4_000_000)).astype(np.float32)
+    s = (c * rng.uniform(0.0, 1.0, c.size)).astype(np.float32)
+    div_first = np.rint(((s / c).astype(np.float32) * np.float32(127)).astype(np.float32))
+    recip_first = np.rint(((np.float32(127) / c).astype(np.float32) * s).astype(np.float32))
+    idx = np.nonzero(div_first != recip_first)[0]
+    assert idx.size >= n_wanted
+    return s, c, idx[:n_wanted]
+
+
+def test_double_quant_order_by_exact_arithmetic():
+    """q = rint(fl32(fl32(s/c) * 127)) evaluated in exact rational arithmetic
+    with correctly rounded float32 steps, at constants c != 1: on random pairs
+    and on pairs where the other page's order (127/c first) disagrees, so a
+    swapped order fails here."""
+    s, c, diff = _dq_pairs_where_the_page_orders_differ()
+    rng = np.random.default_rng(43)
+    pick = np.concatenate([diff, rng.choice(s.size, 400, replace=False)])
+    ss, cc = s[pick], c[pick]
+    # one group of two blocks per pair: the constant is c itself (s <= c)
+    inter = np.empty(2 * pick.size, dtype=np.float32)
+    inter[0::2], inter[1::2] = ss, cc
+    q, cg = O.double_quantize_scales(inter, 2)
+    np.testing.assert_array_equal(cg, cc)
+    assert np.all(q[1::2] == 127)
+    for i in range(pick.size):
+        ratio = _round_f32_exact(Fraction(float(ss[i])) / Fraction(float(cc[i])))
+        want = _rint_half_even(_round_f32_exact(ratio * 127))
+        assert int(q[2 * i]) == want, (ss[i], cc[i])
+    for i in range(diff.size):  # the other order really differs here
+        recip = _round_f32_exact(Fraction(127) / Fraction(float(cc[i])))
+        other = _rint_half_even(_round_f32_exact(recip * Fraction(float(ss[i]))))
+        assert other != int(q[2 * i])
+
+
+def test_double_quant_partial_last_group_exact():
+    """A partial last group takes the maximum of its own blocks only."""
+    rng = np.random.default_rng(44)
+    s = (np.abs(rng.standard_normal(256 + 37)) * 0.013).astype(np.float32)
+    q, c = O.double_quantize_scales(s, 256)
+    assert c.shape == (2,) and c[1] == s[256:].max() and c[0] == s[:256].max()
+    for b in list(range(0, 256, 17)) + list(range(256, 293)):
+        cg = c[b // 256]
+        ratio = _round_f32_exact(Fraction(float(s[b])) / Fraction(float(cg)))
+        assert int(q[b]) == _rint_half_even(_round_f32_exact(ratio * 127))
+
+
+def test_decode_scales_by_exact_arithmetic():
+    """The scale decode (the step-by-step inverse of the double quant; the
+    pages print no inverse) is s~ = fl32(fl32(q/127) * c): every code 0..127
+    against 1,200 constants spread over 2^-126 .. 2^40 (subnormal results
+    included), in exact rational arithmetic.  Plausible other orders of the
+    same decode give different bits on this set, so each fails here."""
+    rng = np.random.default_rng(45)
+    nc = 1200
+    cs = (rng.uniform(1.0, 2.0, nc) * 2.0 ** rng.integers(-126, 41, nc)).astype(np.float32)
+    cs[:4] = np.array([1.0, 0.338, 1.0e-38, 3.0e38 / 127.0], dtype=np.float32)
+    q = np.tile(np.arange(128, dtype=np.int8), nc)
+    got = O.decode_scales(q, cs, 128).reshape(nc, 128)
+    frac = [_round_f32_exact(Fraction(k, 127)) for k in range(128)]
+    want = np.empty((nc, 128), dtype=np.float32)
+    for i in range(nc):
+        cf = Fraction(float(cs[i]))
+        for k in range(128):
+            want[i, k] = np.float32(float(_round_f32_exact(frac[k] * cf)))
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    # q = 127 gives the constant back exactly (the group's largest scale)
+    np.testing.assert_array_equal(got[:, 127], cs)
+    qf = np.arange(128, dtype=np.float32)[None, :]
+    c2 = cs[:, None]
+    others = {
+        "q*c first": ((qf * c2).astype(np.float32) / np.float32(127)).astype(np.float32),
+        "c/127 first": (qf * (c2 / np.float32(127)).astype(np.float32)).astype(np.float32),
+    }
+    for name, alt in others.items():
+        assert np.any(alt.view(np.uint32) != want.view(np.uint32)), name
+
+
 # -------------------------------------------- blocks of 128 (the pages allow 64 or 128)
 def test_block128_codes_by_exact_argmin():
     """Blocks of 128 contiguous elements of the row-major flattening ("QLoRA
@@ -666,3 +824,20 @@ def test_tolerance_helper():
     assert ok and worst < 1
     ok, _ = O.tolerance_ok(ref + np.array([0, 0, 0.01, 0]), ref)
     assert not ok
+
+
+def test_header_dropout_contract_matches_the_oracle():
+    """The dropout mask as the public header states it (word e mod 4 of the
+    generator at counter floor(e/4), kept iff the word is >= ceil(p 2^32)),
+    and the header's own example (seed 0, p = 0.5, elements 0..7), against
+    the oracle's mask."""
+    hdr = open(os.path.join(os.path.dirname(GOLDEN), "..", "include", "nf4qlora.h")).read()
+    flat = " ".join(" ".join(ln.strip().lstrip("/*").strip() for ln in hdr.splitlines()).split())
+    assert "counter (lo, hi of floor(e/4), 0, 0)" in flat
+    assert "element e is kept iff word w_(e mod 4) is >= ceil(p * 2^32)" in flat
+    assert "e = m*in + k" in flat
+    keep = O.dropout_keep(1, 8, 0.5, 0)[0]
+    w0 = O.philox4x32_10([[0, 0, 0, 0]], [[0, 0]])[0]
+    w1 = O.philox4x32_10([[1, 0, 0, 0]], [[0, 0]])[0]
+    want = [int(v) >= 2 ** 31 for v in list(w0) + list(w1)]
+    assert keep.tolist() == want

@@ -3,8 +3,10 @@
     python -m bit_nf4_quantized_04_amd.build
 
 Each .hip file under csrc/ is compiled with hipcc for gfx950 only and the
-objects are linked into bit_nf4_quantized_04_amd/libnf4qlora.so.  Packed fp32
-instructions are disabled for all device code.
+objects are linked into bit_nf4_quantized_04_amd/libnf4qlora.so.  The
+measurement kernels under csrc/calib/ (a plain read and an MFMA loop, the
+achievable ceilings the benchmark quotes) go into libnf4calib.so.  Packed
+fp32 instructions are disabled for all device code.
 """
 
 from __future__ import annotations
@@ -18,6 +20,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libnf4qlora.so")
+CALIB_OUT = os.path.join(HERE, "libnf4calib.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -38,8 +41,8 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d=CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
@@ -66,21 +69,27 @@ def _torch_lib_dir():
     return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     tl = _torch_lib_dir()
     link = ["-L" + tl, "-Wl,-rpath," + tl] if tl else []
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link, "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    calib = sources(os.path.join(CSRC, "calib"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(calib))) as ex:
+        objs = list(ex.map(_compile, srcs + calib))
+    _link(objs[:len(srcs)], OUT)
+    _link(objs[len(srcs):], CALIB_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", CALIB_OUT)
     return OUT
 
 

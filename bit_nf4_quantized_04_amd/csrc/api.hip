@@ -10,6 +10,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+int g_prof_mode = 0;
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -91,6 +92,7 @@ void prof_events(hipEvent_t* start, hipEvent_t* stop) {
     *start = g_prof_start;
     *stop = g_prof_stop;
 }
+bool prof_start_before() { return g_prof_mode == 1; }
 bool& prof_start_taken() { return g_prof_start_taken; }
 int launch_status() {
     const hipError_t e = hipGetLastError();
@@ -101,17 +103,21 @@ int launch_status() {
 
 extern "C" {
 
-const float* nf4_table(void) {
-    static float t[16];
-    static bool init = false;
-    if (!init) {  // idempotent: every thread writes the same bits
+namespace {
+struct LevelTable {
+    float v[16];
+    LevelTable() {
         for (int i = 0; i < 16; ++i) {
             const uint32_t b = nf4dev::level_bits(i);
-            memcpy(&t[i], &b, 4);
+            memcpy(&v[i], &b, 4);
         }
-        init = true;
     }
-    return t;
+};
+}  // namespace
+
+const float* nf4_table(void) {
+    static const LevelTable t;  // initialised once, thread-safe (C++11 function-local static)
+    return t.v;
 }
 
 const char* nf4_strerror(int code) {
@@ -130,10 +136,11 @@ int nf4_version(void) { return NF4QLORA_VERSION; }
 
 int nf4_last_hip_error(void) { return g_last_hip_error; }
 
-int nf4_profile_events(void* start, void* stop) {
-    if ((start == nullptr) != (stop == nullptr)) return NF4_EINVAL;
+int nf4_profile_events(void* start, void* stop, int mode) {
+    if ((start == nullptr) != (stop == nullptr) || (mode != 0 && mode != 1)) return NF4_EINVAL;
     g_prof_start = static_cast<hipEvent_t>(start);
     g_prof_stop = static_cast<hipEvent_t>(stop);
+    g_prof_mode = mode;
     nf4::prof_start_taken() = false;
     return NF4_OK;
 }

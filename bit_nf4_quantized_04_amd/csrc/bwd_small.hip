@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     nf4::QView q, const uint16_t* __restrict__ dh, int M, int nslab, int rows_chunk,
     const uint16_t* __restrict__ B, int r, int64_t pstride, float* __restrict__ part) {
     __shared__ __attribute__((aligned(16))) uint32_t tbl[4][16][64];  // [wave][entry][lane]
-    __shared__ float q127[128];
+    __shared__ float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
     __shared__ __attribute__((aligned(16))) float red[4][DV_SLAB * 64];  // per-wave column sums
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int cb = blk_ok ? blk : nkb - 1;
     const int n_it = int((row_end - row0 + DV_ROWS - 1) / DV_ROWS);
 
-    if (DQ && tid < 128) q127[tid] = q_over_127(tid);
+    if (DQ) q127[tid] = q_over_127(int8_t(tid));
     char* tb = reinterpret_cast<char*>(&tbl[0][0][0]);
     char* mine = tb + (w * 16 * 64 + l) * 4;  // slot (w, 0, l); entry stride 256 B
 #pragma unroll
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
     auto put = [&](int e, uint16_t v) { *reinterpret_cast<uint16_t*>(mine + e * 256 + 2) = v; };
     auto process = [&](const Fetch& f) {
-        const float sc = DQ ? __fmul_rn(q127[f.qb & 127u], f.cg) : bits_f(f.qb);
+        const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
         const float s = f.ok ? sc : 0.0f;
         // entries 0 and 15 are -s and +s exactly; entry 7 (level 0) stays 0
         const uint32_t pe = pack_bf16x2(-s, s);

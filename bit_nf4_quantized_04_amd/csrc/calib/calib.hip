@@ -1,0 +1,115 @@
+// calib.hip -- the measurement kernels declared in include/nf4calib.h: a
+// plain streaming read (the achievable HBM read rate for a given size) and a
+// loop of bf16 matrix-core instructions (the achievable MFMA rate under a
+// sustained load).  Nothing here is used by the layer's kernels.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4calib.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Each thread reads 16-byte pieces strided by the whole grid, four loads in
+// flight per thread per iteration; the XOR of all words is reduced per wave
+// and one atomic per wave folds it into sink.
+__global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ p, int64_t n16, uint32_t* __restrict__ sink) {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+    if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+}
+
+// 8 independent accumulator sets per wave, so consecutive instructions do
+// not wait on each other; the operands change every iteration (a register
+// add) so nothing is hoisted.
+__global__ __launch_bounds__(512) void k_mfma(int iters, float* __restrict__ sink) {
+    const int l = threadIdx.x & 63;
+    bf16x8_t a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(float((l + e) & 7) * 0.125f);
+        b[e] = (__bf16)(float((l * 3 + e) & 7) * 0.0625f);
+    }
+    f32x16_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+        asm volatile("" : "+v"(a));
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[t][e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (threadIdx.x == 0) sink[blockIdx.x] = s;
+}
+
+int resident(const void* kern, int threads) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || cus <= 0 ||
+        per <= 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return cus * per;
+}
+
+int cus_of_device() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4calib_default_workgroups(int which) {
+    if (which == 0) return resident(reinterpret_cast<const void*>(k_read), 256);
+    return 4 * cus_of_device();
+}
+
+int nf4calib_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
+    if (!buf || !sink || (reinterpret_cast<uintptr_t>(buf) & 15) || bytes % 16 || workgroups < 0) return 1;
+    if (workgroups == 0) workgroups = nf4calib_default_workgroups(0);
+    if (workgroups <= 0) return 5;
+    hipLaunchKernelGGL(k_read, dim3(unsigned(workgroups)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4*>(buf), int64_t(bytes / 16), sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int nf4calib_mfma(int iters, int workgroups, int waves, float* sink, void* stream) {
+    if (!sink || iters < 1 || workgroups < 0 || waves < 1 || waves > 8) return 1;
+    if (workgroups == 0) workgroups = nf4calib_default_workgroups(1);
+    if (workgroups <= 0) return 5;
+    hipLaunchKernelGGL(k_mfma, dim3(unsigned(workgroups)), dim3(unsigned(64 * waves)), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+}  // extern "C"

@@ -26,7 +26,7 @@ struct Smem {
     uint16_t As[BM][BKP];
     uint16_t Bs[BN][BKP];
     float lv[16];
-    float q127[128];
+    float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
 };
 
 // ----------------------------------------------------------------- loaders
@@ -101,7 +101,7 @@ struct LdColMajor {
 };
 
 __device__ __forceinline__ float block_scale(const nf4::QView& q, int64_t b, const Smem& sm) {
-    if (q.dq) return __fmul_rn(sm.q127[q.qcodes[b]], q.gabs[b / q.group]);
+    if (q.dq) return __fmul_rn(sm.q127[uint8_t(q.qcodes[b])], q.gabs[b / q.group]);
     return q.absmax[b];
 }
 
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(NT) void k_gemm(LA1 la1, LB1 lb1, int64_t K1, LA2 l
                                              int splits) {
     __shared__ Smem sm;
     if (threadIdx.x < 16) sm.lv[threadIdx.x] = bits_f(level_bits(threadIdx.x));
-    if (threadIdx.x < 128) sm.q127[threadIdx.x] = q_over_127(threadIdx.x);
+    if (threadIdx.x < 256) sm.q127[threadIdx.x] = q_over_127(int8_t(threadIdx.x));
     const int64_t n0 = int64_t(blockIdx.x) * BN, m0 = int64_t(blockIdx.y) * BM;
     const int z = blockIdx.z;
     const int64_t S1 = (K1 + BK - 1) / BK, S2 = (K2 + BK - 1) / BK, S = S1 + S2;

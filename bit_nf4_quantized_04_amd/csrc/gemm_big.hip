@@ -90,7 +90,7 @@ struct RowsBF16 {
 
 // Scale of a block from its raw loads: fl32(fl32(q/127) * c_g) or the fp32 absmax.
 __device__ __forceinline__ float blk_scale(const nf4::QView& q, uint32_t qb, float cg) {
-    return q.dq ? __fmul_rn(q_over_127(int(qb & 127u)), cg) : __builtin_bit_cast(float, qb);
+    return q.dq ? __fmul_rn(q_over_127(int8_t(qb & 255u)), cg) : __builtin_bit_cast(float, qb);
 }
 
 // The 16 fp32 levels (constant-folded when e is a constant).

@@ -67,11 +67,12 @@ int dx_dropout_add(uint16_t* dx, const float* part, int Z, const float* du, cons
                    int64_t M, int64_t K, int r, float f, hipStream_t st);
 // Profiling hook: the caller's events (or null) that bracket the dominant
 // kernel of a call, attached to kernel dispatches (hipExtLaunchKernelGGL).
-// The kernel launched just before the dominant one, when launched with
-// launch_before_dominant, records the start event at its end: the pair then
-// spans the dominant kernel alone, with no marker packet of its own in the
-// queue.  Otherwise both events attach to the dominant kernel's dispatch.
+// Mode 0: both events attach to the dominant kernel's own dispatch.  Mode 1:
+// the kernel launched just before the dominant one, when launched with
+// launch_before_dominant, records the start event at its end (the pair then
+// also spans the gap between the two kernels).
 void prof_events(hipEvent_t* start, hipEvent_t* stop);
+bool prof_start_before();  // mode 1
 bool& prof_start_taken();  // per thread: the start event was attached to the previous kernel
 
 template <typename Kernel, typename... Args>
@@ -79,7 +80,7 @@ void launch_before_dominant(Kernel kernel, dim3 grid, dim3 block, size_t shmem, 
                             Args... args) {
     hipEvent_t a, b;
     prof_events(&a, &b);
-    if (a && b) {
+    if (a && b && prof_start_before()) {
         hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, nullptr, a, 0, args...);
         prof_start_taken() = true;
     } else {

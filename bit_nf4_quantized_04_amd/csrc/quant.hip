@@ -40,8 +40,9 @@ __device__ __forceinline__ float4 load4(const uint2* W, int64_t i) {
 }
 
 // One thread = 4 consecutive elements; L lanes = one block of 4L elements
-// (16 lanes for 64, 32 for 128).  The absmax is an L-lane butterfly max;
-// codes of 4 elements pack into 2 bytes.
+// (16 lanes for 64, 32 for 128).  The absmax is an L-lane butterfly max of
+// the magnitude bits (the integer order of |w| for finite w; Inf and NaN
+// sort above every finite value); codes of 4 elements pack into 2 bytes.
 template <int L, typename In>
 __global__ __launch_bounds__(256) void k_quant_blocks(const In* __restrict__ W, int64_t n4,
                                                       uint16_t* __restrict__ codes,
@@ -52,11 +53,18 @@ __global__ __launch_bounds__(256) void k_quant_blocks(const In* __restrict__ W, 
         // n4 is a multiple of L and so is `stride`: the L lanes of a block
         // enter and leave the loop together.
         const float4 v = load4(W, i);
-        float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        constexpr uint32_t MAG = 0x7fffffffu;
+        uint32_t mb = max(max(f_bits(v.x) & MAG, f_bits(v.y) & MAG), max(f_bits(v.z) & MAG, f_bits(v.w) & MAG));
 #pragma unroll
-        for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+        for (int off = L / 2; off >= 1; off >>= 1) mb = max(mb, uint32_t(__shfl_xor(int(mb), off, L)));
+        float m = bits_f(mb);
         uint32_t packed;
-        if (m == 0.0f) {
+        if (mb >= 0x7f800000u) {
+            // a block holding Inf or NaN: scale NaN, every code level 7, so
+            // the whole block dequantizes to NaN
+            packed = 0x7777u;
+            m = bits_f(0x7fc00000u);
+        } else if (mb == 0u) {
             packed = 0x7777u;  // an all-zero block: every element is level 7 (0.0)
         } else {
             const uint32_t c0 = nearest_code(__fdiv_rn(v.x, m));
@@ -81,13 +89,20 @@ __global__ __launch_bounds__(256) void k_dq_scales(const float* __restrict__ abs
     const int64_t b0 = g * G;
     const int64_t len = (nb - b0 < G) ? (nb - b0) : G;
     float m = 0.0f;
-    for (int64_t j = lane; j < len; j += 64) m = fmaxf(m, absmax[b0 + j]);
+    int bad = 0;  // a NaN scale (a block that held Inf or NaN) in the group
+    for (int64_t j = lane; j < len; j += 64) {
+        const float v = absmax[b0 + j];
+        bad |= v != v;
+        m = fmaxf(m, v);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (lane == 0) gabs[g] = m;
+    bad = __any(bad);
+    // such a group gets constant NaN and codes 0: all its weights dequantize to NaN
+    if (lane == 0) gabs[g] = bad ? bits_f(0x7fc00000u) : m;
     for (int64_t j = lane; j < len; j += 64) {
         int code = 0;
-        if (m != 0.0f) code = (int)rintf(__fmul_rn(__fdiv_rn(absmax[b0 + j], m), 127.0f));
+        if (!bad && m != 0.0f) code = (int)rintf(__fmul_rn(__fdiv_rn(absmax[b0 + j], m), 127.0f));
         q[b0 + j] = int8_t(code);
     }
 }

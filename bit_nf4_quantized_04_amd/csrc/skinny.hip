@@ -82,7 +82,7 @@ struct SkinnySmem {
     // holds the cross-wave reduction.
     uint16_t tbl[SKW][16][128];
     uint16_t xs[SKW][MT][256];  // x slice of the current block-step, per wave
-    float q127[128];
+    float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
     float us[16 * 64];  // u for the epilogue (r <= 64 here)
 };
 
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
     const int64_t N = q.rows, K = q.cols;
     const int nkb = int(K / 64);  // block indices fit in 32 bits (checked by the API)
     const int64_t o0 = int64_t(blockIdx.x) * 16;
-    if (DQ && tid < 128) sm.q127[tid] = q_over_127(tid);
+    if (DQ) sm.q127[tid] = q_over_127(int8_t(tid));
     // The lookup addresses assume the table starts at LDS offset 0.
     __syncthreads();
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             if (m < M) *reinterpret_cast<uint2*>(&sm.xs[w][m][4 * l]) = f.xv[m];
-        const float sc = DQ ? __fmul_rn(sm.q127[f.qb & 127u], f.cg) : bits_f(f.qb);
+        const float sc = DQ ? __fmul_rn(sm.q127[f.qb], f.cg) : bits_f(f.qb);
         const float sblk = f.ok ? sc : 0.0f;
         // the block's 16 products, bf16, into this lane's table column
 #pragma unroll
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
     float* __restrict__ u_out, int R, int nchunks) {
     __shared__ __attribute__((aligned(16))) uint32_t tbl[4][16][64];  // [wave][entry][lane]
-    __shared__ float q127[128];
+    __shared__ float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
     __shared__ float dlds[2][4][G1_NC];  // the wave's region sum per (parity, wave, row)
     __shared__ float us[64];
     const int tid = threadIdx.x, l = tid & 63;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int nkb = int(K / 64);
     const int S = 4 / R, rows_chunk = S * G1_NC;
     const int rho = w % R, sub = w / R;
-    if (DQ && tid < 128) q127[tid] = q_over_127(tid);
+    if (DQ) q127[tid] = q_over_127(int8_t(tid));
     char* tb = reinterpret_cast<char*>(&tbl[0][0][0]);
     char* mine = tb + (w * 16 * 64 + l) * 4;  // slot (w, 0, l); entry stride 256 B
 #pragma unroll
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 
     auto put = [&](int e, uint16_t v) { *reinterpret_cast<uint16_t*>(mine + e * 256 + 2) = v; };
     auto process = [&](const Fetch& f, int par, int i) {
-        const float sc = DQ ? __fmul_rn(q127[f.qb & 127u], f.cg) : bits_f(f.qb);
+        const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
         const float s = f.ok ? sc : 0.0f;
         // entries 0 and 15 are -s and +s exactly; entry 7 (level 0) stays 0
         const uint32_t pe = pack_bf16x2(-s, s);

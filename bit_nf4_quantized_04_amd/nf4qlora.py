@@ -57,7 +57,7 @@ _SIGS = {
     "nf4_strerror": (C.c_char_p, [C.c_int]),
     "nf4_version": (C.c_int, []),
     "nf4_last_hip_error": (C.c_int, []),
-    "nf4_profile_events": (C.c_int, [_P, _P]),
+    "nf4_profile_events": (C.c_int, [_P, _P, C.c_int]),
     "nf4_storage_sizes": (C.c_int, [_I64, _I64, C.POINTER(nf4_config), C.POINTER(C.c_size_t),
                                     C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "nf4_quantize": (C.c_int, [_P, _I64, _I64, C.POINTER(nf4_config), _P, _P, _P, _P, _P]),
@@ -141,11 +141,12 @@ def qlora_workspace_bytes(op: int, rows: int, cols: int, M: int, r: int, n_adapt
     return int(_lib.qlora_workspace_bytes(op, rows, cols, M, r, n_adapters))
 
 
-def nf4_profile_events(start=None, stop=None) -> None:
+def nf4_profile_events(start=None, stop=None, mode: int = 0) -> None:
     """Record a pair of raw hipEvent_t handles (ints) around the dominant
-    kernel of later layer calls (None, None disables)."""
+    kernel of later layer calls (None, None disables); mode 0 attaches both
+    to that kernel's dispatch, mode 1 starts at the end of the kernel before."""
     _check(_lib.nf4_profile_events(None if start is None else C.c_void_p(start),
-                                   None if stop is None else C.c_void_p(stop)),
+                                   None if stop is None else C.c_void_p(stop), int(mode)),
            "nf4_profile_events")
 
 

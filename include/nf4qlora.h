@@ -45,8 +45,12 @@
  *  - Every call returns NF4_OK (0) or an error code; on error nothing has been
  *    enqueued (except NF4_ELAUNCH, after which the HIP error is available from
  *    nf4_last_hip_error(), per thread).  No exception crosses the ABI.
- *  - Inputs must be finite.  The quantizer does not check this; a block that
- *    holds Inf or NaN gets unspecified codes and scale.
+ *  - Weights should be finite.  The calls are asynchronous and never
+ *    synchronize, so a status cannot depend on device data: instead a block
+ *    that holds Inf or NaN is quantized to scale NaN with code 7 everywhere
+ *    (with double quant its group gets constant NaN and scale codes 0), so
+ *    every weight of that block (group) dequantizes to NaN and every output
+ *    that reads it is NaN.  Activations and adapters are used as given.
  */
 #ifndef NF4QLORA_H
 #define NF4QLORA_H
@@ -84,10 +88,13 @@ typedef struct nf4_config {
  *                the high nibble of byte e/2 when e is even, the low nibble
  *                when e is odd [P5 "Pillar 1", byte packing].
  *  absmax:       rows*cols/block_size fp32 block scales (read when double_quant == 0).
- *  scale_codes:  rows*cols/block_size int8 codes q_b in [0, 127] (double_quant == 1).
+ *  scale_codes:  rows*cols/block_size int8 codes q_b (double_quant == 1); nf4_quantize
+ *                writes codes in [0, 127].
  *  group_absmax: ceil(nblocks/dq_group) fp32 group constants c_g (double_quant == 1).
  * The scale used for block b is s_b, or fl32(fl32(q_b/127) * c_g) with
- * g = b / dq_group (the operation-by-operation inverse of the quantizer). */
+ * g = b / dq_group (the operation-by-operation inverse of the quantizer).
+ * Every call decodes a scale code this way, a negative code from another
+ * producer included (it gives a negative scale). */
 typedef struct nf4_tensor {
     const uint8_t* codes;
     const float* absmax;
@@ -270,12 +277,17 @@ int qlora_adamw_step(float* p, const float* g, float* m, float* v, uint16_t* p_b
                      float weight_decay, void* stream);
 
 /* Profiling hook (for benchmarks; not thread-safe).  When both are non-NULL,
- * `start` and `stop` (hipEvent_t handles owned by the caller) are recorded on
- * the call's stream immediately before and after the dominant kernel of every
+ * `start` and `stop` (hipEvent_t handles owned by the caller) are attached to
+ * kernel dispatches on the call's stream around the dominant kernel of every
  * later qlora_linear_forward / _multi (the fused dequant product) and
  * qlora_linear_backward (the fused dequant dX product), so
- * hipEventElapsedTime gives that kernel's duration.  NULL, NULL disables. */
-int nf4_profile_events(void* start, void* stop);
+ * hipEventElapsedTime gives that kernel's duration.  mode 0: both events on
+ * the dominant kernel's own dispatch.  mode 1: on the few-token paths the
+ * start event is recorded at the end of the kernel launched just before the
+ * dominant one, so the pair also spans the gap between the two (an upper
+ * bound on the kernel's time).  NULL, NULL disables.  NF4_EINVAL for one
+ * NULL handle or another mode. */
+int nf4_profile_events(void* start, void* stop, int mode);
 
 #ifdef __cplusplus
 }

@@ -144,8 +144,6 @@ def split_blocks(w, block_size: int = BLOCK_SIZE) -> np.ndarray:
     a = _as_f32(w).reshape(-1)
     if a.size % block_size:
         raise ValueError("element count %d is not a multiple of %d" % (a.size, block_size))
-    if not np.all(np.isfinite(a)):
-        raise ValueError("non-finite weight")
     return a.reshape(-1, block_size)
 
 
@@ -202,12 +200,20 @@ def unpack_codes(packed) -> np.ndarray:
 
 
 def quantize_first_level(w, block_size: int = BLOCK_SIZE):
-    """Blockwise NF4 quantization: returns (codes[unpacked], absmax[fp32])."""
+    """Blockwise NF4 quantization: returns (codes[unpacked], absmax[fp32]).
+
+    READING (the pages assume finite weights): a block that holds Inf or NaN
+    has no absmax scale; it is stored with scale NaN and code 7 (level 0) for
+    every element, so all of it dequantizes to NaN.
+    """
     blocks = split_blocks(w, block_size)
-    s = block_absmax(blocks)
-    wn = normalize(blocks, s)
+    bad = ~np.all(np.isfinite(blocks), axis=1)
+    clean = np.where(bad[:, None], np.float32(0), blocks).astype(np.float32)
+    s = block_absmax(clean)
+    wn = normalize(clean, s)
     codes = nearest_code(wn)
     codes[s == 0, :] = 7  # all-zero block: every normalized value is 0 -> level 0.0
+    s[bad] = np.float32(np.nan)
     return codes.reshape(-1), s
 
 
@@ -223,7 +229,9 @@ def double_quantize_scales(absmax, group: int = DQ_GROUP):
     READINGS: group size 256 as on "From LoRA to QLoRA" (the n4n.ai listing
     uses one global constant, i.e. group >= number of blocks); the order
     divide-then-multiply of the n4n.ai listing; the last group may be partial;
-    a group whose constant is 0 gets codes 0.
+    a group whose constant is 0 gets codes 0; a group holding a NaN scale (a
+    block that held Inf or NaN) gets constant NaN and codes 0, so every
+    weight of the group dequantizes to NaN.
     """
     s = _as_f32(absmax).reshape(-1)
     nb = s.size
@@ -232,6 +240,9 @@ def double_quantize_scales(absmax, group: int = DQ_GROUP):
     q = np.zeros(nb, dtype=np.int8)
     for g in range(ng):
         sl = s[g * group:(g + 1) * group]
+        if np.any(np.isnan(sl)):
+            c[g] = np.float32(np.nan)
+            continue
         cg = np.max(sl) if sl.size else np.float32(0)  # scales are >= 0
         c[g] = cg
         if cg == 0:

@@ -105,3 +105,30 @@ def oracle_weight_cols(w: np.ndarray, cols_idx, dq: bool = True, group: int = 25
             sel = (idx >= lo) & (idx < hi)
             res[o, sel] = wb[idx[sel] - lo]
     return res
+
+
+def oracle_rows_dequant(qref, o0: int, o1: int, cols: int, group: int = 256) -> np.ndarray:
+    """Oracle Wb (float64) of rows [o0, o1) of a weight the oracle quantized
+    as a whole (double quant): the slice of its codes, scale codes and group
+    constants, decoded by the oracle.  The slice must start on a group."""
+    b0, b1 = o0 * cols // 64, o1 * cols // 64
+    assert b0 % group == 0
+    g0, g1 = b0 // group, (b1 + group - 1) // group
+    part = {"codes": qref["codes"][o0 * cols // 2:o1 * cols // 2], "absmax": qref["absmax"][b0:b1],
+            "scale_codes": qref["scale_codes"][b0:b1], "group_absmax": qref["group_absmax"][g0:g1]}
+    return O.compute_weight(part, (o1 - o0, cols), dq_group=group)
+
+
+def weight_from_oracle(F, qref, rows: int, cols: int, dq: bool, group: int = 256):
+    """An NF4Weight on the GPU holding the oracle's own storage (codes,
+    scales): the layer calls then read exactly what the oracle dequantizes."""
+    import torch
+
+    d = dev()
+    codes = torch.from_numpy(np.ascontiguousarray(qref["codes"])).to(d)
+    absmax = torch.from_numpy(np.ascontiguousarray(qref["absmax"])).to(d)
+    sc = ga = None
+    if dq:
+        sc = torch.from_numpy(np.ascontiguousarray(qref["scale_codes"])).to(d)
+        ga = torch.from_numpy(np.ascontiguousarray(qref["group_absmax"])).to(d)
+    return F.NF4Weight(codes, absmax, sc, ga, rows, cols, dq, group)

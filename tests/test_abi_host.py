@@ -23,10 +23,19 @@ def F():
     return nf4qlora
 
 
-def declared_functions():
-    text = open(HEADER).read()
+CALIB_HEADER = os.path.join(ROOT, "include", "nf4calib.h")
+CALIB_LIB = os.path.join(ROOT, "bit_nf4_quantized_04_amd", "libnf4calib.so")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_headers_are_the_two_libraries():
+    """Every header under include/ belongs to one of the two libraries."""
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["nf4calib.h", "nf4qlora.h"]
 
 
 def test_every_declared_function_is_exported(F):
@@ -36,6 +45,32 @@ def test_every_declared_function_is_exported(F):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(F.EXPORTS)
+
+
+@pytest.mark.skipif(not os.path.exists(CALIB_LIB), reason="libnf4calib.so not built")
+def test_calibration_library_exports_and_argument_errors():
+    from bit_nf4_quantized_04_amd import calib
+
+    names = declared_functions(CALIB_HEADER)
+    assert set(names) == set(calib.EXPORTS)
+    lib = C.CDLL(CALIB_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    L = calib._lib
+    assert L.nf4calib_read(None, 64, FAKE, 0, None) == 1
+    assert L.nf4calib_read(C.c_void_p(0x100004), 64, FAKE, 0, None) == 1  # misaligned
+    assert L.nf4calib_read(FAKE, 65, FAKE, 0, None) == 1                  # not whole 16-byte pieces
+    assert L.nf4calib_read(FAKE, 64, None, 0, None) == 1
+    assert L.nf4calib_mfma(0, 4, 4, FAKE, None) == 1
+    assert L.nf4calib_mfma(10, 4, 9, FAKE, None) == 1
+    assert L.nf4calib_mfma(10, 4, 4, None, None) == 1
+
+
+def test_profile_hook_arguments(F):
+    lib = F._lib
+    assert lib.nf4_profile_events(FAKE, None, 0) == F.NF4_EINVAL
+    assert lib.nf4_profile_events(FAKE, FAKE, 2) == F.NF4_EINVAL
+    assert lib.nf4_profile_events(None, None, 0) == F.NF4_OK
 
 
 def test_version_table_and_strings(F):
@@ -218,3 +253,32 @@ def test_workspace_queries_without_tokens(F):
         for op in (F.QLORA_OP_FORWARD, F.QLORA_OP_BACKWARD, F.QLORA_OP_FORWARD_MULTI,
                    F.QLORA_OP_BACKWARD | F.QLORA_OP_DROPOUT, F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128):
             assert F.qlora_workspace_bytes(op, rows, cols, 0, r, 4) >= 0
+
+
+def test_level_table_from_many_threads(F):
+    """nf4_table() is safe to call from several threads at once (its table is
+    initialised once) and every caller sees the 16 levels."""
+    import threading
+
+    from oracle import nf4_oracle as O
+
+    lib = C.CDLL(LIB)
+    lib.nf4_table.restype = C.POINTER(C.c_float)
+    seen, errs = [], []
+
+    def run():
+        try:
+            for _ in range(200):
+                p = lib.nf4_table()
+                seen.append(np.ctypeslib.as_array(p, shape=(16,)).copy())
+        except Exception as e:  # pragma: no cover
+            errs.append(e)
+
+    th = [threading.Thread(target=run) for _ in range(8)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs and len(seen) == 1600
+    for v in seen:
+        np.testing.assert_array_equal(v, O.NF4_LEVELS)

@@ -841,3 +841,36 @@ def test_header_dropout_contract_matches_the_oracle():
     w1 = O.philox4x32_10([[1, 0, 0, 0]], [[0, 0]])[0]
     want = [int(v) >= 2 ** 31 for v in list(w0) + list(w1)]
     assert keep.tolist() == want
+
+
+def test_non_finite_blocks_dequantize_to_nan():
+    """A block holding Inf or NaN has no absmax scale: it is stored with
+    scale NaN and level 0 everywhere (so all of it dequantizes to NaN); the
+    other blocks are untouched, and with double quant the NaN scale's group
+    gets constant NaN and codes 0 (all its weights NaN), the other groups
+    what they get without it."""
+    rng = np.random.default_rng(51)
+    w = (rng.standard_normal((4, 64 * 8)) * 0.02).astype(np.float32)
+    clean = O.quantize(w, double_quant=False)
+    bad = w.copy()
+    bad[0, 3] = np.inf
+    bad[2, 64 * 5 + 9] = np.nan
+    bad[3, 70] = -np.inf
+    codes, s = O.quantize_first_level(bad)
+    nb = [3 // 64, (2 * 512 + 64 * 5 + 9) // 64, (3 * 512 + 70) // 64]
+    for b in range(s.size):
+        if b in nb:
+            assert np.isnan(s[b]) and np.all(codes[64 * b:64 * b + 64] == 7)
+        else:
+            assert s[b] == clean["absmax"][b]
+            np.testing.assert_array_equal(codes[64 * b:64 * b + 64],
+                                          O.unpack_codes(clean["codes"])[64 * b:64 * b + 64])
+    d = O.dequantize(O.quantize(bad, double_quant=False), bad.shape).reshape(-1, 64)
+    assert np.all(np.isnan(d[nb])) and not np.any(np.isnan(np.delete(d, nb, axis=0)))
+    q, c = O.double_quantize_scales(s, 8)  # groups of 8 blocks = one matrix row each
+    qc, cc = O.double_quantize_scales(clean["absmax"], 8)
+    assert np.isnan(c[0]) and np.isnan(c[2]) and np.isnan(c[3]) and c[1] == cc[1]
+    assert np.all(q[0:8] == 0) and np.all(q[16:32] == 0)
+    np.testing.assert_array_equal(q[8:16], qc[8:16])
+    dd = O.dequantize(O.quantize(bad, double_quant=True, dq_group=8), bad.shape, dq_group=8)
+    assert np.all(np.isnan(dd[[0, 2, 3]])) and not np.any(np.isnan(dd[1]))

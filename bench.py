@@ -302,7 +302,7 @@ def main():
         print("%s pass: %.4f ms/step over %d steps" % (args.only, t, K), flush=True)
 
     # ------------------------------------------------ ceilings of this GPU
-    sink_u = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink_u = torch.zeros(max(CAL.default_workgroups(0), 1), dtype=torch.int32, device=dev)
 
     def read_rate(nbytes, n_bufs, steps):
         bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(n_bufs)]

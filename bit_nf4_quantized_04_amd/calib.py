@@ -37,7 +37,8 @@ def default_workgroups(which: int) -> int:
 
 
 def read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0) -> None:
-    """Read every byte of `buf` once (a contiguous device tensor)."""
+    """Read every byte of `buf` once (a contiguous device tensor); `sink` has
+    one int32 per workgroup (default_workgroups(0) of them for 0)."""
     rc = _lib.nf4calib_read(C.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
                             C.c_void_p(sink.data_ptr()), workgroups, _stream())
     if rc:

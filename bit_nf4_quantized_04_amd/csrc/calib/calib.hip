@@ -13,9 +13,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Each thread reads 16-byte pieces strided by the whole grid, four loads in
-// flight per thread per iteration; the XOR of all words is reduced per wave
-// and one atomic per wave folds it into sink.
+// flight per thread per iteration; the XOR of all words is reduced per
+// workgroup and stored to sink[workgroup] (plain stores: atomics on one
+// address would serialize thousands of waves at the end).
 __global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ p, int64_t n16, uint32_t* __restrict__ sink) {
+    __shared__ uint32_t red[4];
     const int64_t stride = int64_t(gridDim.x) * 256;
     int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
     uint32_t acc = 0;
@@ -29,7 +31,9 @@ __global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ p, int64
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
-    if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = (red[0] ^ red[1]) ^ (red[2] ^ red[3]);
 }
 
 // 8 independent accumulator sets per wave, so consecutive instructions do

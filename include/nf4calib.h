@@ -23,8 +23,8 @@ extern "C" {
 /* Read `bytes` of device memory at `buf` (16-byte aligned, bytes a multiple
  * of 16) once, with 16-byte loads from `workgroups` workgroups of 256
  * threads (0: the number that are resident on the device at once); the XOR
- * of everything read is written to sink[0] (one uint32, device), so no load
- * can be dropped.  Returns 1 for a bad argument, 5 for a failed launch. */
+ * of what each workgroup read is written to sink[workgroup] (uint32, device,
+ * one entry per workgroup launched), so no load can be dropped.  Returns 1 for a bad argument, 5 for a failed launch. */
 int nf4calib_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 /* Run `iters` iterations of 8 independent v_mfma_f32_32x32x16_bf16 per wave

@@ -3,6 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "nf4_device.h"
 #include "nf4_internal.h"
 
@@ -82,6 +85,42 @@ int layer_view(nf4::QView* v, void** ws, size_t* ws_bytes, hipStream_t st) {
 
 inline bool bad_ptr(const void* p) { return !p || !al16(p); }
 
+// Scratch memory of qlora_linear_forward_noalloc: one array in every
+// device's global memory (allocated with the code object, held until the
+// process ends).  Host code never passes `scratch` itself to a kernel (in
+// host code the name is a host-side stand-in): the device address comes
+// from hipGetSymbolAddress, once per device, and only that pointer is used.
+constexpr size_t kNoAllocScratch = size_t(QLORA_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The calling thread's current device's copy of `scratch`.
+int scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return NF4_EINVAL;
+    }
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                g_last_hip_error = int(e != hipSuccess ? e : hipErrorInvalidSymbol);
+                (void)hipGetLastError();
+                return NF4_ELAUNCH;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return NF4_OK;
+}
+
 }  // namespace
 
 namespace nf4 {
@@ -128,6 +167,9 @@ const char* nf4_strerror(int code) {
         case NF4_EUNSUPPORTED: return "unsupported configuration (block_size must be 64 or 128, dq_group >= 1)";
         case NF4_EWORKSPACE: return "workspace missing or smaller than qlora_workspace_bytes()";
         case NF4_ELAUNCH: return "HIP kernel launch failed (see nf4_last_hip_error)";
+        case NF4_ETOOLARGE:
+            return "the call needs more scratch than qlora_linear_forward_noalloc holds "
+                   "(QLORA_NOALLOC_SCRATCH_BYTES); use qlora_linear_forward with a workspace";
         default: return "unknown error code";
     }
 }
@@ -242,6 +284,22 @@ int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M, cons
         return rc;
     return nf4::forward_impl(v, x, M, A, B, r, scale, h, r > 0 ? u_out : nullptr, ws, ws_bytes,
                              static_cast<hipStream_t>(stream));
+}
+
+int qlora_linear_forward_noalloc(const nf4_tensor* W, const uint16_t* x, int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float scale, uint16_t* h, float* u_out,
+                                 void* stream) {
+    nf4::QView v;
+    int rc = view_of(W, true, &v);
+    if (rc) return rc;
+    if (M < 0 || r < 0 || r > 256 || !isfinite(scale)) return NF4_EINVAL;
+    const int rr = (A && B) ? r : 0;
+    const int op = QLORA_OP_FORWARD | (v.bshift == 7 ? QLORA_OP_BLOCK128 : 0);
+    if (qlora_workspace_bytes(op, v.rows, v.cols, M, rr, 0) > kNoAllocScratch) return NF4_ETOOLARGE;
+    if (M == 0 || v.rows == 0) return NF4_OK;
+    void* ws = nullptr;
+    if ((rc = scratch_ptr(&ws))) return rc;
+    return qlora_linear_forward(W, x, M, A, B, r, scale, h, u_out, ws, kNoAllocScratch, stream);
 }
 
 int qlora_linear_forward_multi(const nf4_tensor* W, const uint16_t* x, int64_t M,

@@ -24,7 +24,8 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("libnf4qlora.so is not built; run `python -m bit_nf4_quantized_04_amd.build`")
 _lib = C.CDLL(LIB_PATH)
 
-NF4_OK, NF4_EINVAL, NF4_ESHAPE, NF4_EUNSUPPORTED, NF4_EWORKSPACE, NF4_ELAUNCH = range(6)
+NF4_OK, NF4_EINVAL, NF4_ESHAPE, NF4_EUNSUPPORTED, NF4_EWORKSPACE, NF4_ELAUNCH, NF4_ETOOLARGE = range(7)
+QLORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 QLORA_OP_FORWARD, QLORA_OP_BACKWARD, QLORA_OP_FORWARD_MULTI = 1, 2, 3
 QLORA_OP_BLOCK128 = 0x100  # OR'ed into a workspace query for a weight with 128-element blocks
 QLORA_OP_DROPOUT = 0x200   # OR'ed into a workspace query for the *_dropout calls
@@ -67,6 +68,8 @@ _SIGS = {
     "qlora_workspace_bytes": (C.c_size_t, [C.c_int, _I64, _I64, _I64, C.c_int32, C.c_int32]),
     "qlora_linear_forward": (C.c_int, [C.POINTER(nf4_tensor), _P, _I64, _P, _P, C.c_int32,
                                        C.c_float, _P, _P, _P, C.c_size_t, _P]),
+    "qlora_linear_forward_noalloc": (C.c_int, [C.POINTER(nf4_tensor), _P, _I64, _P, _P, C.c_int32,
+                                               C.c_float, _P, _P, _P]),
     "qlora_linear_forward_multi": (C.c_int, [C.POINTER(nf4_tensor), _P, _I64, _P, _P, C.c_int32,
                                              C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "qlora_linear_backward": (C.c_int, [C.POINTER(nf4_tensor), _P, _P, _I64, _P, _P, C.c_int32,
@@ -288,6 +291,25 @@ def qlora_linear_forward(w: NF4Weight, x, A, B, scale: float, want_u: bool = Fal
         _check(_lib.qlora_linear_forward_dropout(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale),
                                                  C.byref(d), _ptr(h), _ptr(u), _ptr(ws), ws.numel(),
                                                  _stream(stream)), "qlora_linear_forward_dropout")
+    return (h, u) if want_u else h
+
+
+def qlora_linear_forward_noalloc(w: NF4Weight, x, A, B, scale: float, want_u: bool = False, out=None, u_out=None,
+                                 stream=None):
+    """qlora_linear_forward on the library's own device scratch (the C call
+    allocates nothing; pass `out` and `u_out` to allocate nothing here
+    either).  Returns h (and u)."""
+    import torch
+
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    h = out if out is not None else torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    u = u_out
+    if u is None and want_u and r:
+        u = torch.empty((M, r), dtype=torch.float32, device=x.device)
+    t = w.c_struct()
+    _check(_lib.qlora_linear_forward_noalloc(C.byref(t), _ptr(x), M, _ptr(A), _ptr(B), r, float(scale), _ptr(h),
+                                             _ptr(u), _stream(stream)), "qlora_linear_forward_noalloc")
     return (h, u) if want_u else h
 
 

@@ -70,7 +70,8 @@ enum {
     NF4_ESHAPE = 2,        /* rows*cols not a multiple of the block; linear calls: cols % 64 != 0 */
     NF4_EUNSUPPORTED = 3,  /* block_size not 64 or 128, dq_group < 1 */
     NF4_EWORKSPACE = 4,    /* workspace pointer NULL or smaller than qlora_workspace_bytes() */
-    NF4_ELAUNCH = 5        /* a HIP launch failed; see nf4_last_hip_error() */
+    NF4_ELAUNCH = 5,       /* a HIP launch failed; see nf4_last_hip_error() */
+    NF4_ETOOLARGE = 6      /* qlora_linear_forward_noalloc: more scratch needed than it holds */
 };
 
 /* Quantization settings [P2 "Hyperparameters"].  The quant type is NF4 and
@@ -185,6 +186,26 @@ size_t qlora_workspace_bytes(int op, int64_t rows, int64_t cols, int64_t M, int3
 int qlora_linear_forward(const nf4_tensor* W, const uint16_t* x, int64_t M,
                          const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                          uint16_t* h, float* u_out, void* ws, size_t ws_bytes, void* stream);
+
+/* qlora_linear_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels, results, arguments
+ * and errors as qlora_linear_forward; instead of a caller's workspace it uses
+ * a scratch array that the library keeps in each device's global memory
+ * (QLORA_NOALLOC_SCRATCH_BYTES = 64 MiB per device the library runs on, held
+ * until the process ends).  A call whose workspace query,
+ * qlora_workspace_bytes(QLORA_OP_FORWARD [| QLORA_OP_BLOCK128], ...),
+ * exceeds that size returns NF4_ETOOLARGE before anything is enqueued
+ * (every decode shape fits; for example 8192 -> 28672 at M = 4096 needs
+ * 24 MiB, 4096 -> 11008 at M = 2048 about 52 MiB).  The scratch array is
+ * shared by every call on a device and keeps the last call's contents; the
+ * kernels read nothing from it that the same call did not write first.
+ * Calls that overlap on one device (concurrent streams or threads) race on
+ * it: serialize them. */
+#define QLORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qlora_linear_forward_noalloc(const nf4_tensor* W, const uint16_t* x, int64_t M,
+                                 const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                                 uint16_t* h, float* u_out, void* stream);
 
 /* Multi-adapter forward [P5 "The Real-World Bottleneck"]: token t uses
  * adapter ids[t] (device int32 [M]):

@@ -40,7 +40,7 @@ def test_headers_are_the_two_libraries():
 
 def test_every_declared_function_is_exported(F):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = C.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -78,8 +78,8 @@ def test_version_table_and_strings(F):
 
     assert F.nf4_version() == 1
     np.testing.assert_array_equal(F.nf4_table(), O.NF4_LEVELS)
-    for code in range(6):
-        assert F.nf4_strerror(code)
+    for code in range(7):
+        assert F.nf4_strerror(code) and "unknown" not in F.nf4_strerror(code)
     assert "unknown" in F.nf4_strerror(99)
 
 
@@ -214,6 +214,28 @@ def test_dropout_argument_errors(F):
         assert F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT, 128, 256, 600, 8) == base + extra
         both = F.qlora_workspace_bytes(op | F.QLORA_OP_DROPOUT | F.QLORA_OP_BLOCK128, 128, 256, 600, 8)
         assert both == base + extra + 128 * 256 // 16
+
+
+def test_noalloc_forward_refuses_oversized_calls(F):
+    """The allocation-free forward checks its need against its fixed scratch
+    before anything is launched: a shape whose workspace query exceeds
+    QLORA_NOALLOC_SCRATCH_BYTES is refused with NF4_ETOOLARGE, bad arguments
+    as the plain forward, and M = 0 is a no-op."""
+    lib = F._lib
+    big = _tensor(F, rows=4096, cols=4096)
+    need = F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, 4096, 4096, 2048, 16)
+    assert need > F.QLORA_NOALLOC_SCRATCH_BYTES
+    call = lambda tt, M, r, s=2.0, x=FAKE: lib.qlora_linear_forward_noalloc(C.byref(tt), x, M, FAKE, FAKE, r, s,
+                                                                           FAKE, None, None)
+    assert call(big, 2048, 16) == F.NF4_ETOOLARGE
+    assert "scratch" in F.nf4_strerror(F.NF4_ETOOLARGE)
+    assert call(big, -1, 16) == F.NF4_EINVAL
+    assert call(big, 4, 300) == F.NF4_EINVAL
+    assert call(big, 4, 16, float("nan")) == F.NF4_EINVAL
+    assert call(_tensor(F, cols=96), 4, 16) == F.NF4_ESHAPE
+    assert call(big, 0, 16) == F.NF4_OK
+    for (o, i, M, r) in ((28672, 8192, 1, 64), (28672, 8192, 16, 64), (28672, 8192, 4096, 64), (11008, 4096, 2048, 64)):
+        assert F.qlora_workspace_bytes(F.QLORA_OP_FORWARD, o, i, M, r) <= F.QLORA_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_sizes_are_monotone(F):

@@ -37,25 +37,48 @@ __global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ p, int64
 }
 
 // 8 independent accumulator sets per wave, so consecutive instructions do
-// not wait on each other; the operands change every iteration (a register
-// add) so nothing is hoisted.
+// not wait on each other.  The operands are bf16 values with random mantissa
+// bits (magnitudes in [0.5, 1)) whose mantissas change every iteration (an
+// XOR with a per-iteration pattern), as in a real GEMM: a loop on constant or
+// low-entropy operands draws less power and keeps a higher clock than a GEMM
+// on random data can.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t mix32(uint32_t v) {
+    v ^= v >> 16;
+    v *= 0x7feb352dU;
+    v ^= v >> 15;
+    v *= 0x846ca68bU;
+    v ^= v >> 16;
+    return v;
+}
+
 __global__ __launch_bounds__(512) void k_mfma(int iters, float* __restrict__ sink) {
-    const int l = threadIdx.x & 63;
-    bf16x8_t a, b;
+    const uint32_t seed = blockIdx.x * 512u + threadIdx.x;
+    u32x4_t a, b;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = (__bf16)(float((l + e) & 7) * 0.125f);
-        b[e] = (__bf16)(float((l * 3 + e) & 7) * 0.0625f);
+    for (int e = 0; e < 4; ++e) {
+        a[e] = (mix32(seed * 8u + e) & 0x807F807Fu) | 0x3F003F00u;
+        b[e] = (mix32(seed * 8u + 4u + e) & 0x807F807Fu) | 0x3F003F00u;
     }
     f32x16_t acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+    uint32_t pat = mix32(seed ^ 0x9E3779B9u) & 0x007F007Fu;
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
-        asm volatile("" : "+v"(a));
+        for (int t = 0; t < 8; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, (t & 1) ? b : a),
+                                                             __builtin_bit_cast(bf16x8_t, (t & 1) ? a : b), acc[t],
+                                                             0, 0, 0);
+        pat = (pat * 5u + 0x00130029u) & 0x007F007Fu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] ^= pat;
+            b[e] ^= pat >> 1 & 0x007F007Fu;
+        }
     }
     float s = 0.0f;
 #pragma unroll

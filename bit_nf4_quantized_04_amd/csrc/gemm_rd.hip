@@ -176,37 +176,50 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int XBUF = RM * 8;  // one x tile: 256 rows x 8 chunks of 16 bytes
-// Per-wave weight slot: codes [row j][64 lanes][16 B], then scales [j][64][4 B].
-constexpr int WSLOT = 2 * 64 * 16 + 2 * 64 * 4;  // bytes per wave
-// DMA instructions per lane: 8 per x tile, 4 per weight slot.  Issue order:
-// step t DMAs x tile t+3 in its first slice and weights t+3 in its second.
-// At the wait in step t's second slice (x tile t+1 and weights t+1 needed)
-// x tile t+2, weights t+2 and x tile t+3 may still be in flight.
-constexpr int VM_XTILE = 8, VM_WSLOT = 4;
-constexpr int VM_STEP_WAIT = 2 * VM_XTILE + VM_WSLOT;
+
+// The forward kernel's shape for NW waves: wave w owns the 256 x (256/NW)
+// slab of weight rows [CPW w, CPW w + CPW), i.e. J = CPW/32 column groups of
+// the 32x32 MFMA; each lane DMAs XD 16-byte chunks of every x tile.
+template <int NW>
+struct FwdShape {
+    static constexpr int CPW = RN / NW;
+    static constexpr int J = CPW / 32;
+    static constexpr int XD = RM * 8 / (64 * NW);
+    // per-wave weight slot: codes [j][64 lanes][16 B], then scales [j][64][4 B]
+    static constexpr int WSLOT = J * 64 * 16 + J * 64 * 4;
+    // DMA instructions per lane: XD per x tile, 2J per weight slot.  Issue
+    // order: step t DMAs x tile t+3 in its first slice and weights t+3 in its
+    // second.  At the wait in step t's second slice (x tile t+1 and weights
+    // t+1 needed) x tile t+2, weights t+2 and x tile t+3 may be in flight.
+    static constexpr int VM_XTILE = XD, VM_WSLOT = 2 * J;
+    static constexpr int VM_STEP_WAIT = 2 * VM_XTILE + VM_WSLOT;
+};
 
 struct Frag { u32x4_t v[8]; };
 
+template <int NW>
 struct FwdCtx {
+    using Sh = FwdShape<NW>;
+    static constexpr int J = Sh::J, XD = Sh::XD, WSLOT = Sh::WSLOT;
     const FwdArgs& a;
     int S1, S;
     int nl, hh, w, lane;
-    bool wok[2];
-    uint32_t xoff[8], eoff[8];  // byte offsets of this lane's x / extension DMA sources
-    uint32_t coff[2];           // byte offset of this lane's code half-block, step 0
-    uint32_t soff[2];           // byte offset of row j's block scale, step 0
+    bool wok[J];
+    uint32_t xoff[XD], eoff[XD];  // byte offsets of this lane's x / extension DMA sources
+    uint32_t coff[J];             // byte offset of this lane's code half-block, step 0
+    uint32_t soff[J];             // byte offset of row j's block scale, step 0
     DecK dk;
 
     // x tile of step s into LDS tile `dst`: DMA instruction i of wave w fills
-    // chunk positions 64(8w + i) .. +63 (one 16-byte chunk per lane).
+    // chunk positions 64(XD w + i) .. +63 (one 16-byte chunk per lane).
     __device__ __forceinline__ void xdma(int s, uint4* dst) const {
         const bool main = s < S1;
         const char* base = main ? reinterpret_cast<const char*>(a.x) + int64_t(s) * (RKS * 2)
                                 : reinterpret_cast<const char*>(a.ext) + int64_t(s - S1) * (RKS * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < XD; ++i)
             __builtin_amdgcn_global_load_lds((glb_void_t*)(base + (main ? xoff[i] : eoff[i])),
-                                             (lds_void_t*)(dst + 64 * (8 * w + i)), 16, 0, 0);
+                                             (lds_void_t*)(dst + 64 * (XD * w + i)), 16, 0, 0);
     }
     // this lane's codes and block scales of step s into its wave's slot
     __device__ __forceinline__ void wdma(int s, char* slot) const {
@@ -214,18 +227,19 @@ struct FwdCtx {
         const char* cb = reinterpret_cast<const char*>(a.codes) + int64_t(s) * 32;
         const char* sb = reinterpret_cast<const char*>(a.scales) + int64_t(s) * 4;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < J; ++j)
             __builtin_amdgcn_global_load_lds((glb_void_t*)(cb + coff[j]), (lds_void_t*)(mine + j * 1024), 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(sb + soff[j]), (lds_void_t*)(mine + 2048 + j * 256), 4, 0, 0);
+        for (int j = 0; j < J; ++j)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(sb + soff[j]), (lds_void_t*)(mine + J * 1024 + j * 256), 4,
+                                             0, 0);
     }
-    __device__ __forceinline__ void wread(const char* slot, uint4 (&cw)[2], float (&sc)[2]) const {
+    __device__ __forceinline__ void wread(const char* slot, uint4 (&cw)[J], float (&sc)[J]) const {
         const char* mine = slot + w * WSLOT;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < J; ++j) {
             cw[j] = *reinterpret_cast<const uint4*>(mine + j * 1024 + lane * 16);
-            const float v = *reinterpret_cast<const float*>(mine + 2048 + j * 256 + lane * 4);
+            const float v = *reinterpret_cast<const float*>(mine + J * 1024 + j * 256 + lane * 4);
             sc[j] = wok[j] ? v : 0.0f;
         }
     }
@@ -247,25 +261,27 @@ struct FwdCtx {
 #pragma unroll
         for (int t = 0; t < 4; ++t) out[t] = uint32_t(e[2 * t]) | (uint32_t(e[2 * t + 1]) << 16);
     }
-    __device__ __forceinline__ void lookups(const Planes (&p)[2], const uint4 (&cw)[2], int sl, u32x4_t (&bf)[2]) const {
+    __device__ __forceinline__ void lookups(const Planes (&p)[J], const uint4 (&cw)[J], int sl, u32x4_t (&bf)[J]) const {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < J; ++j)
             lookup8(dk, p[j], sl == 0 ? cw[j].x : sl == 1 ? cw[j].y : sl == 2 ? cw[j].z : cw[j].w, bf[j]);
     }
 };
 
-__device__ __forceinline__ void mma(f32x16_t (&acc)[8][2], const Frag& af, const u32x4_t (&bf)[2]) {
+template <int J>
+__device__ __forceinline__ void mma(f32x16_t (&acc)[8][J], const Frag& af, const u32x4_t (&bf)[J]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af.v[i], bf[j], acc[i][j]);
+        for (int j = 0; j < J; ++j) acc[i][j] = mfma32(af.v[i], bf[j], acc[i][j]);
 }
 
-// Interleave the 16 MFMAs of a slice with the slice's other work: after each
+// Interleave the N MFMAs of a slice with the slice's other work: after each
 // MFMA one LDS read, up to four VALU operations and one DMA.
+template <int N>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < N; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
@@ -277,47 +293,63 @@ constexpr uint32_t vmcnt_imm(int n) {  // s_waitcnt vmcnt(n), other counters unc
     return uint32_t((n & 15) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// One 16-k slice: acc[i][j] += f.v[i] * b[j] for the eight A fragments, each
+// MFMA followed by the LDS read of fragment i of the next slice (x tile
+// `nb`, slice `nsl`) into the register it frees, so a single set of A
+// fragments is live; after each MFMA the schedule places that read, up to
+// four VALU operations of the next slice's dequantization and one DMA.
+template <int NW, int J>
+__device__ __forceinline__ void slice_mma(const FwdCtx<NW>& c, f32x16_t (&acc)[8][J], Frag& f, const u32x4_t (&b)[J],
+                                          const uint4* nb, int nsl) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) acc[i][j] = mfma32(f.v[i], b[j], acc[i][j]);
+        f.v[i] = __builtin_bit_cast(u32x4_t, nb[xpos(32 * i + c.nl, 4 * c.hh + nsl)]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8 * J; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (k % J == J - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+}
+
 // One NF4 step t.  x tiles: `cur` = step t, `nxt` = step t+1, `xd` receives
 // step t+3.  Weight slot `wn` holds step t+1: it is read in the second slice
-// and then receives step t+3 (the other slot holds step t+2).  On entry
-// fa/ba are slice 0's operands and cw/pl the codes and planes of step t; the
-// step builds cwn/pln for step t+1 and leaves fa/ba as its slice 0 operands.
-__device__ __forceinline__ void nf4_step(const FwdCtx& c, int t, const uint4* cur, const uint4* nxt,
-                                         uint4* xd, char* wn, f32x16_t (&acc)[8][2], Frag& fa,
-                                         u32x4_t (&ba)[2], const uint4 (&cw)[2], const Planes (&pl)[2],
-                                         uint4 (&cwn)[2], Planes (&pln)[2]) {
-    Frag fb;
-    u32x4_t bb[2];
-    float sc[2];
-    // slice 0: prepare slice 1; DMA the x tile of step t+3
-    c.aread(cur, 1, fb);
+// and then receives step t+3 (the other slot holds step t+2).  On entry f/ba
+// are slice 0's operands and cw/pl the codes and planes of step t; the step
+// builds cwn/pln for step t+1 and leaves f/ba as its slice 0 operands.
+template <int NW, int J = FwdShape<NW>::J>
+__device__ __forceinline__ void nf4_step(const FwdCtx<NW>& c, int t, const uint4* cur, const uint4* nxt,
+                                         uint4* xd, char* wn, f32x16_t (&acc)[8][J], Frag& f,
+                                         u32x4_t (&ba)[J], const uint4 (&cw)[J], const Planes (&pl)[J],
+                                         uint4 (&cwn)[J], Planes (&pln)[J]) {
+    constexpr int VM_STEP_WAIT = FwdShape<NW>::VM_STEP_WAIT;
+    u32x4_t bb[J];
+    float sc[J];
+    // slice 0: slice 1's B operand; DMA the x tile of step t+3
     c.lookups(pl, cw, 1, bb);
     c.xdma(t + 3 < c.S ? t + 3 : c.S - 1, xd);
-    mma(acc, fa, ba);
-    interleave();
+    slice_mma<NW, J>(c, acc, f, ba, cur, 1);
     // slice 1: this lane's weights of step t+1 (and x tile t+1) complete; they
-    // go to registers, the slot receives step t+3's; prepare slice 2
+    // go to registers, the slot receives step t+3's; slice 2's B operand
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM_STEP_WAIT));
     c.wread(wn, cwn, sc);
     c.wdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, wn);
-    c.aread(cur, 2, fa);
     c.lookups(pl, cw, 2, ba);
     pln[0] = make_planes(sc[0]);
-    mma(acc, fb, bb);
-    interleave();
-    // slice 2: prepare slice 3
-    c.aread(cur, 3, fb);
+    slice_mma<NW, J>(c, acc, f, bb, cur, 2);
+    // slice 2: slice 3's B operand
     c.lookups(pl, cw, 3, bb);
-    pln[1] = make_planes(sc[1]);
-    mma(acc, fa, ba);
-    interleave();
-    // slice 3: every wave's share of x tile t+1 is in; prepare step t+1's
-    // first slice
+    if constexpr (J > 1) pln[J - 1] = make_planes(sc[J - 1]);
+    slice_mma<NW, J>(c, acc, f, ba, cur, 3);
+    // slice 3: every wave's share of x tile t+1 is in (its fragments are read
+    // during this slice); step t+1's first B operand
     __builtin_amdgcn_s_barrier();
-    c.aread(nxt, 0, fa);
     c.lookups(pln, cwn, 0, ba);
-    mma(acc, fb, bb);
-    interleave();
+    slice_mma<NW, J>(c, acc, f, bb, nxt, 0);
 }
 
 // XCD-aware tile order (workgroups are dealt round-robin to the 8 XCDs): a
@@ -335,12 +367,15 @@ __device__ __forceinline__ void tile_of(int64_t lin, int64_t nMt, int64_t nNt, i
     tn = (lin % gsz) / gm;
 }
 
-template <bool MULTI>
-__global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
+template <bool MULTI, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_fwd_rd(FwdArgs a) {
+    using Sh = FwdShape<NW>;
+    constexpr int J = Sh::J, CPW = Sh::CPW;
+    static_assert(!MULTI || NW == 4, "the gathered epilogue stages 64-column slabs");
     // the ring of x tiles and the two weight slots: separate arrays, so that
     // the compiler can see that a DMA into one never overlaps reads of another
     __shared__ __attribute__((aligned(16))) uint4 xs0[XBUF], xs1[XBUF], xs2[XBUF], xs3[XBUF];
-    __shared__ __attribute__((aligned(16))) char wb0[4 * WSLOT], wb1[4 * WSLOT];
+    __shared__ __attribute__((aligned(16))) char wb0[NW * Sh::WSLOT], wb1[NW * Sh::WSLOT];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t N = a.N, K = a.K, M = a.M;
@@ -371,7 +406,7 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     tile_of(lin, nMt, nNt, tm, tn);
     const int64_t m0 = tm * RM, n0 = tn * RN;
 
-    FwdCtx c{a};
+    FwdCtx<NW> c{a};
     c.S1 = int(K / RKS);
     c.S = c.S1 + (a.ext ? a.KL / RKS : 0);
     c.nl = lane & 31;
@@ -379,18 +414,18 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     c.w = w;
     c.lane = lane;
     c.dk.init();
-    int64_t wrow[2];
+    int64_t wrow[J];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t rr = n0 + 64 * w + 32 * j + c.nl;
+    for (int j = 0; j < J; ++j) {
+        const int64_t rr = n0 + CPW * w + 32 * j + c.nl;
         c.wok[j] = rr < N;
         wrow[j] = c.wok[j] ? rr : N - 1;
         c.coff[j] = uint32_t(wrow[j] * (K / 2) + 16 * c.hh);
         c.soff[j] = uint32_t(wrow[j] * (K / 64) * 4);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int p = 64 * (8 * w + i) + lane;  // chunk position this lane's DMA writes
+    for (int i = 0; i < Sh::XD; ++i) {
+        const int p = 64 * (Sh::XD * w + i) + lane;  // chunk position this lane's DMA writes
         const int m = p >> 3;
         const int ch = (p & 7) ^ ((m >> 1) & 7);  // logical chunk stored there
         int64_t row = m0 + m;
@@ -399,11 +434,11 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
         c.eoff[i] = uint32_t((row * a.KL + 8 * ch) * 2);
     }
 
-    f32x16_t acc[8][2];
+    f32x16_t acc[8][J];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < J; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -419,29 +454,29 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     c.xdma(sb + 1 < S ? sb + 1 : S - 1, xs1);
     c.wdma(sb + 1 < S1 ? sb + 1 : S1 - 1, wb1);
     c.xdma(sb + 2 < S ? sb + 2 : S - 1, xs2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * VM_XTILE + VM_WSLOT));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Sh::VM_XTILE + Sh::VM_WSLOT));
     __syncthreads();  // x tile sb and the step-sb weights ready
-    uint4 cw[2], cw2[2];
-    Planes pl[2], pl2[2];
+    uint4 cw[J], cw2[J];
+    Planes pl[J], pl2[J];
     {
-        float sc[2];
+        float sc[J];
         c.wread(wb0, cw, sc);
         c.wdma(sb + 2 < S1 ? sb + 2 : S1 - 1, wb0);
-        pl[0] = make_planes(sc[0]);
-        pl[1] = make_planes(sc[1]);
+#pragma unroll
+        for (int j = 0; j < J; ++j) pl[j] = make_planes(sc[j]);
     }
     Frag fa;
-    u32x4_t ba[2];
+    u32x4_t ba[J];
     c.aread(xs0, 0, fa);
     c.lookups(pl, cw, 0, ba);
 
     // four steps per iteration so every ring index is static (the launcher
     // guarantees S1 % 4 == 0)
     for (int t = sb; t < se; t += 4) {
-        nf4_step(c, t, xs0, xs1, xs3, wb1, acc, fa, ba, cw, pl, cw2, pl2);
-        nf4_step(c, t + 1, xs1, xs2, xs0, wb0, acc, fa, ba, cw2, pl2, cw, pl);
-        nf4_step(c, t + 2, xs2, xs3, xs1, wb1, acc, fa, ba, cw, pl, cw2, pl2);
-        nf4_step(c, t + 3, xs3, xs0, xs2, wb0, acc, fa, ba, cw2, pl2, cw, pl);
+        nf4_step<NW>(c, t, xs0, xs1, xs3, wb1, acc, fa, ba, cw, pl, cw2, pl2);
+        nf4_step<NW>(c, t + 1, xs1, xs2, xs0, wb0, acc, fa, ba, cw2, pl2, cw, pl);
+        nf4_step<NW>(c, t + 2, xs2, xs3, xs1, wb1, acc, fa, ba, cw, pl, cw2, pl2);
+        nf4_step<NW>(c, t + 3, xs3, xs0, xs2, wb0, acc, fa, ba, cw2, pl2, cw, pl);
     }
 
     // ---- rank-r steps (at most three, all already DMA'd): x tile from the
@@ -454,11 +489,11 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
             Frag f;
-            u32x4_t bf[2];
+            u32x4_t bf[J];
             c.aread(tl, sl, f);
-            c.bload(s, wrow[0], c.wok[0], sl, bf[0]);
-            c.bload(s, wrow[1], c.wok[1], sl, bf[1]);
-            mma(acc, f, bf);
+#pragma unroll
+            for (int j = 0; j < J; ++j) c.bload(s, wrow[j], c.wok[j], sl, bf[j]);
+            mma<J>(acc, f, bf);
         }
     }
 
@@ -467,8 +502,8 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     if (nz > 1 && gridDim.y == 1) {  // a split tail tile: tile-local fp32 partials
         float* pz = a.part + (int64_t(z) * (T - a.tfull) + tt) * (RM * RN);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int ln = 64 * w + 32 * j + c.nl;
+        for (int j = 0; j < J; ++j) {
+            const int ln = CPW * w + 32 * j + c.nl;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -477,8 +512,8 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
     } else if (gridDim.y > 1) {  // one split of the reduction: fp32 partials
         float* pz = a.part + int64_t(z) * M * N;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + 64 * w + 32 * j + c.nl;
+        for (int j = 0; j < J; ++j) {
+            const int64_t n = n0 + CPW * w + 32 * j + c.nl;
             if (n >= N) continue;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -490,8 +525,8 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
         }
     } else if constexpr (!MULTI) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + 64 * w + 32 * j + c.nl;
+        for (int j = 0; j < J; ++j) {
+            const int64_t n = n0 + CPW * w + 32 * j + c.nl;
             if (n >= N) continue;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -512,7 +547,7 @@ __global__ __launch_bounds__(RT, 1) void k_fwd_rd(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     stg[(8 * (v >> 2) + 4 * c.hh + (v & 3)) * 64 + 32 * j + c.nl] = acc[i][j][v];
@@ -687,15 +722,15 @@ __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, 
     c.hdma(t + 3 < c.S ? t + 3 : c.S - 1, bd);
     c.sdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, bd);
     c.aread(bc, 1, fb);
-    mma(acc, fa, ba);
+    mma<2>(acc, fa, ba);
     // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
     // (the scheduling barrier keeps the staging reads below the wait)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
     __builtin_amdgcn_sched_barrier(0);
     c.dequant(bn, wn);
-    interleave();
-    mma(acc, fb, bb);
-    interleave();
+    interleave<16>();
+    mma<2>(acc, fb, bb);
+    interleave<16>();
     // W tile t+1 (LDS writes) complete before the barrier; no fence: nothing
     // else must be waited for
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP) & ~0xf00u);
@@ -809,8 +844,8 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
         c.bread(wt0, b0, b1);
         c.aread(ht, 0, f0);
         c.aread(ht, 1, f1);
-        mma(acc, f0, b0);
-        mma(acc, f1, b1);
+        mma<2>(acc, f0, b0);
+        mma<2>(acc, f1, b1);
         __syncthreads();
     }
 
@@ -977,6 +1012,14 @@ int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, 
     return NF4_OK;
 }
 
+// Waves of the single-adapter forward kernel: eight (two per SIMD, each
+// with a 256 x 32 accumulator slab) so that one wave's dequantization and
+// waits overlap the other's MFMAs.
+#ifndef NF4_FWD_WAVES
+#define NF4_FWD_WAVES 8
+#endif
+constexpr int kFwdWaves = NF4_FWD_WAVES;
+
 struct TailPlan {
     int64_t T, tfull, grid;
     int z, spl;
@@ -1022,7 +1065,7 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, r > 0 ? ext : nullptr, B, h,
               M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0, tail_ws, int(q.cols / RKS),
               tp.tfull, tp.z, tp.spl};
-    launch_dominant(k_fwd_rd<false>, dim3(unsigned(tp.grid)), dim3(RT), 0, st, a);
+    launch_dominant(k_fwd_rd<false, kFwdWaves>, dim3(unsigned(tp.grid)), dim3(64 * kFwdWaves), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (tp.z > 1) {
         hipLaunchKernelGGL(k_tail_sum, dim3(unsigned((tp.T - tp.tfull) * (RM / 4))), dim3(256), 0, st, a);
@@ -1065,7 +1108,7 @@ int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* 
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, nullptr, nullptr, h,
               M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl, 0, 1, spl};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
-    launch_dominant(k_fwd_rd<true>, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
+    launch_dominant(k_fwd_rd<true, 4>, dim3(unsigned(T), unsigned(Z)), dim3(256), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (Z > 1) {
         if (ms) return multi_fin_seg(*ms, part_ws, Z, M, q.rows, su, r, Bb, h, st);

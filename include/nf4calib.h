@@ -28,7 +28,9 @@ extern "C" {
 int nf4calib_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 /* Run `iters` iterations of 8 independent v_mfma_f32_32x32x16_bf16 per wave
- * (operands in registers, fp32 accumulators) on `workgroups` workgroups of
+ * (operands in registers: bf16 values with random mantissa bits that change
+ * every iteration, as a GEMM's operands do; fp32 accumulators) on
+ * `workgroups` workgroups of
  * `waves` waves (64 threads each; 0 workgroups: 4 per compute unit).  Each
  * instruction is 32*32*16 multiply-adds, i.e. 32768 flops; the total is
  * workgroups * waves * iters * 8 * 32768.  The accumulators' sum goes to

@@ -54,70 +54,11 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f
                                                     __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
 // x tile [256 rows][64 k] bf16 in LDS: row-major 128 B rows of eight 16-byte
 // chunks, chunk c of row m stored at position c ^ ((m >> 1) & 7).  Sixteen
 // consecutive rows then cover all 64 banks once for a given chunk, so both
 // the fragment reads and the tile writes are conflict-free.
 __device__ __forceinline__ int xpos(int m, int c) { return m * 8 + (c ^ ((m >> 1) & 7)); }
-
-// Byte planes of a block's 16 bf16 products: pl[0..3] low bytes of entries
-// 0-3, 4-7, 8-11, 12-15, pl[4..7] the high bytes.
-struct Planes { uint32_t v[8]; };
-
-__device__ __forceinline__ Planes make_planes(float s) {
-    float p[16];
-    p[0] = -s;
-    p[7] = 0.0f;
-    p[15] = s;
-#pragma unroll
-    for (int e = 1; e < 15; ++e)
-        if (e != 7) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
-    uint32_t w[8];  // w[i] = bf16 pair (entry 2i, entry 2i+1)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-    Planes t;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        t.v[g] = perm(w[2 * g + 1], w[2 * g], 0x06040200u);      // low bytes of entries 4g..4g+3
-        t.v[4 + g] = perm(w[2 * g + 1], w[2 * g], 0x07050301u);  // high bytes
-    }
-    return t;
-}
-
-// Constants of the nibble decode, held in VGPRs so that the selector
-// arithmetic fuses into single VOP3 operations.
-struct DecK {
-    uint32_t m7, m4, id, sa, sb;
-    __device__ __forceinline__ void init() {
-        m7 = 0x07070707u;
-        m4 = 0x04040404u;
-        id = 0x03020100u;
-        sa = 0x05010400u;
-        sb = 0x07030602u;
-        asm volatile("" : "+v"(m7), "+v"(m4), "+v"(id), "+v"(sa), "+v"(sb));
-    }
-};
-
-// Eight nibbles (one code dword: element 2i in the high nibble of byte i,
-// element 2i+1 in the low nibble) -> four bf16 pairs in element order.
-__device__ __forceinline__ void lookup8(const DecK& k, const Planes& t, uint32_t cd, u32x4_t& out) {
-    const uint32_t c4 = cd >> 4;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        // bytes: element 4h, 4h+1, 4h+2, 4h+3 codes in the low nibbles
-        const uint32_t raw = perm(cd, c4, half ? k.sb : k.sa);
-        const uint32_t s3 = raw & k.m7;
-        const uint32_t s2 = ((raw >> 1) & k.m4) | k.id;  // byte i, or 4+i if bit 3
-        const uint32_t lo = perm(perm(t.v[3], t.v[2], s3), perm(t.v[1], t.v[0], s3), s2);
-        const uint32_t hi = perm(perm(t.v[7], t.v[6], s3), perm(t.v[5], t.v[4], s3), s2);
-        out[2 * half] = perm(hi, lo, k.sa);      // elements 4h, 4h+1
-        out[2 * half + 1] = perm(hi, lo, k.sb);  // elements 4h+2, 4h+3
-    }
-}
 
 struct FwdArgs {
     const uint8_t* codes;  // [N][K/2]

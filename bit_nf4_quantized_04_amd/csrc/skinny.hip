@@ -239,6 +239,14 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
     }
 }
 
+// The table slot {0, bf16(v)} (low half zero, the product in the high half)
+// in one conversion: v_cvt_pk_bf16_f32 with a constant 0 for the low half.
+__device__ __forceinline__ uint32_t slot_bf16(float v) {
+    uint32_t d;
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(d) : "v"(v));
+    return d;
+}
+
 // v as held by another lane of the same quad (DPP quad_perm: 0x55 reads quad
 // position 1, 0xAA position 2, 0xFF position 3), and one lane's v for the
 // whole wave
@@ -281,10 +289,16 @@ __device__ __forceinline__ float lane_val(float v, int lane) {
 // b + 2G, ... of the G-strided sequence: neighbouring workgroups stream
 // neighbouring rows, and no counter or atomic is involved.
 constexpr int G1_NC = 3;  // rows per wave per chunk (and fetch ring slots)
+#ifndef NF4_GEMV_NV
+#define NF4_GEMV_NV 0
+#endif
 
 // SH: log2(block size / 64), 0 or 1 (the scales of 128-element blocks are
-// read as they are, one per two of the lanes' 64-element halves).
-template <bool DQ, bool GSH, int SH>
+// read as they are, one per two of the lanes' 64-element halves).  NV: code
+// dwords of each lane's block (of 8) whose weights come from register byte
+// planes instead of the LDS table, which moves that share of the lookups
+// from the LDS pipe to the VALU.
+template <bool DQ, bool GSH, int SH, int NV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv1(
     nf4::QView q, const uint16_t* __restrict__ x, const float* __restrict__ upart, int r,
     const uint16_t* __restrict__ B, float scale, uint16_t* __restrict__ h,
@@ -295,15 +309,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     __shared__ float us[64];
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int64_t N = q.rows, K = q.cols;
-    const int nkb = int(K / 64);
+    const int N = int(q.rows);  // rows < 2^31 (the launcher checks the code bytes)
+    const int nkb = int(q.cols / 64);
     const int S = 4 / R, rows_chunk = S * G1_NC;
     const int rho = w % R, sub = w / R;
     if (DQ) q127[tid] = q_over_127(int8_t(tid));
     char* tb = reinterpret_cast<char*>(&tbl[0][0][0]);
     char* mine = tb + (w * 16 * 64 + l) * 4;  // slot (w, 0, l); entry stride 256 B
-#pragma unroll
-    for (int e = 0; e < 16; ++e) *reinterpret_cast<uint32_t*>(mine + e * 256) = 0u;
+    // entry 7 (level 0) stays {0, 0}; the others are rewritten for every row
+    *reinterpret_cast<uint32_t*>(mine + 7 * 256) = 0u;
     // u = sum of the down-projection partials, in a fixed order
     for (int idx = tid; idx < r; idx += 256) {
         float a = 0.0f;
@@ -327,6 +341,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     // nibble mask kept in a VGPR so that (c & mask) | P is one v_and_or_b32
     uint32_t nmask = 0x0F0F0F0Fu;
     asm volatile("" : "+v"(nmask));
+    DecK dk;
+    if constexpr (NV > 0) dk.init();
     const bool lora = r > 0 && rho == 0;  // wave-uniform: region-0 waves add s*u.B
     const bool lane_r = l < r;
     const uint32_t lane_rc = uint32_t(lane_r ? l : 0);  // clamped B column
@@ -336,18 +352,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         uint32_t qb;
         float cg;
         uint32_t bv;
-        bool ok;
     };
-    // byte offsets from wave-uniform bases (32 bits: the launcher keeps the
-    // code array under 4 GB), so every load is base + one VGPR offset
-    const uint32_t row_bytes = uint32_t(K / 2);
+    // every load is a uniform base plus a 32-bit per-lane byte offset (the
+    // launcher keeps the code array under 4 GB)
+    const uint32_t row_bytes = uint32_t(q.cols / 2);
     const uint32_t lane_bytes = uint32_t(cb) * 32u;
     const char* codes = reinterpret_cast<const char*>(q.codes);
-    const char* bbase = reinterpret_cast<const char*>(B);
-    auto fetch = [&](int64_t row, Fetch& f) {
-        const bool rok = row < N;  // uniform
-        const uint32_t crow = uint32_t(rok ? row : N - 1);
-        f.ok = blk_ok && rok;
+    // the adapter's B row of the lane (without an adapter the load reads the
+    // codes instead: the same load count on every path, the value unused)
+    const char* bsrc = lora ? reinterpret_cast<const char*>(B) : codes;
+    const uint32_t bstride = lora ? uint32_t(r) * 2u : 0u;
+    const uint32_t boff = lora ? lane_rc * 2u : 0u;
+    auto fetch = [&](int row, Fetch& f) {  // row: wave-uniform
+        const uint32_t crow = uint32_t(row < N ? row : N - 1);
         const uint32_t off = crow * row_bytes + lane_bytes;
         f.c0 = *reinterpret_cast<const uint4*>(codes + off);
         f.c1 = *reinterpret_cast<const uint4*>(codes + off + 16u);
@@ -356,61 +373,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const uint32_t b = (crow * uint32_t(nkb) + uint32_t(cb)) >> SH;
         if (DQ) {
             const uint32_t gi = GSH ? (b >> q.gshift) : (b / uint32_t(q.group));
-            f.qb = uint32_t(uint8_t(q.qcodes[b]));
-            f.cg = q.gabs[gi];
+            f.qb = uint32_t(*reinterpret_cast<const uint8_t*>(reinterpret_cast<const char*>(q.qcodes) + b));
+            f.cg = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(q.gabs) + (gi << 2));
         } else {
-            f.qb = __builtin_bit_cast(uint32_t, q.absmax[b]);
+            f.qb = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(q.absmax) + (b << 2));
             f.cg = 0.0f;
         }
-        // (without an adapter the load reads the codes instead: the same load
-        // count on every path, the value unused)
-        f.bv = *reinterpret_cast<const uint16_t*>(lora ? bbase + (crow * uint32_t(r) + lane_rc) * 2u : codes);
+        f.bv = *reinterpret_cast<const uint16_t*>(bsrc + (crow * bstride + boff));
     };
     __syncthreads();  // q127, us ready
     // A fragment of the rank-r step: {hi, lo} of s*u[l] in the first dword
-    uint32_t ua0 = 0u;
+    // (zeros after it, so the B fragment may repeat one dword)
+    u32x4_t ua = {0u, 0u, 0u, 0u};
     if (lora && lane_r) {
         uint16_t hi, lo;
         split_bf16(__fmul_rn(scale, us[l]), hi, lo);
-        ua0 = uint32_t(hi) | (uint32_t(lo) << 16);
+        ua[0] = uint32_t(hi) | (uint32_t(lo) << 16);
     }
 
-    auto put = [&](int e, uint16_t v) { *reinterpret_cast<uint16_t*>(mine + e * 256 + 2) = v; };
-    auto process = [&](const Fetch& f, int par, int i) {
+    auto process = [&](const Fetch& f, bool ok, int par, int i) {
         const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
-        const float s = f.ok ? sc : 0.0f;
-        // entries 0 and 15 are -s and +s exactly; entry 7 (level 0) stays 0
-        const uint32_t pe = pack_bf16x2(-s, s);
-        put(0, uint16_t(pe));
-        put(15, uint16_t(pe >> 16));
-        auto pair = [&](int e0, int e1) {
-            const uint32_t pk = pack_bf16x2(__fmul_rn(s, bits_f(level_bits(e0))),
-                                            __fmul_rn(s, bits_f(level_bits(e1))));
-            put(e0, uint16_t(pk));
-            put(e1, uint16_t(pk >> 16));
-        };
-        pair(1, 2);
-        pair(3, 4);
-        pair(5, 6);
-        pair(8, 9);
-        pair(10, 11);
-        pair(12, 13);
-        put(14, to_bf16(__fmul_rn(s, bits_f(level_bits(14)))));
+        const float s = (ok && blk_ok) ? sc : 0.0f;
+        // the block's 16 products; the LDS table holds them as {0, v} slots,
+        // written two per instruction (entries e and e+1 are 256 B apart)
+        float p[16];
+        p[0] = -s;
+        p[7] = 0.0f;
+        p[15] = s;
+#pragma unroll
+        for (int e = 1; e < 15; ++e)
+            if (e != 7) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (e != 7) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(p[e]);
+        Planes pl;
+        if constexpr (NV > 0) {
+            uint32_t wp[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) wp[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+            pl = planes_of_pairs(wp);
+        }
         const uint32_t cw[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         if (lora) {
-            // zeros made in place (a hoisted constant vector would be spilled)
-            uint32_t z, bv = f.bv;
-            asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-            asm volatile("" : "+v"(bv));  // keep the B load's use here, not in the fetch
-            bv = lane_r ? bv : 0u;
-            const u32x4_t ua = {ua0, z, z, z};
-            const u32x4_t bb = {bv | (bv << 16), z, z, z};
+            uint32_t bv = lane_r ? f.bv * 0x10001u : 0u;  // {B[o][l], B[o][l]}
+            const u32x4_t bb = {bv, bv, bv, bv};
             acc = mfma16(ua, bb, acc);
         }
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             const uint32_t cd = cw[st];
+            if (st >= 8 - NV) {  // register byte planes: four bf16 pairs, one MFMA
+                u32x4_t wv;
+                lookup8(dk, pl, cd, wv);
+                acc = mfma16(xa[st], wv, acc);
+                continue;
+            }
             const uint32_t clo = (cd & nmask) | P;         // odd elements (low nibbles)
             const uint32_t chi = ((cd >> 4) & nmask) | P;  // even elements (high nibbles)
             u32x4_t we, wo;
@@ -442,7 +460,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int G = int(gridDim.x);
     int c = blockIdx.x;
     auto seq_row = [&](int cc, int j) {  // row j of the ring, counted from chunk cc
-        return int64_t(cc + (j / G1_NC) * G) * rows_chunk + sub * G1_NC + (j % G1_NC);
+        return (cc + (j / G1_NC) * G) * rows_chunk + sub * G1_NC + (j % G1_NC);
     };
     Fetch ring[G1_NC];
 #pragma unroll
@@ -452,14 +470,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         for (int i = 0; i < G1_NC; ++i) {
             fetch(seq_row(c, i + G1_NC - 1), ring[(i + G1_NC - 1) % G1_NC]);
             __builtin_amdgcn_sched_barrier(0);
-            process(ring[i], k & 1, i);
+            process(ring[i], seq_row(c, i) < N, k & 1, i);
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
         // finish the chunk's rows: regions summed, in order
         if (tid < rows_chunk) {
             const int sb = tid / G1_NC, i = tid % G1_NC;
-            const int64_t o = int64_t(c) * rows_chunk + tid;
+            const int o = c * rows_chunk + tid;
             float v = 0.0f;
             for (int rr = 0; rr < R; ++rr) v += dlds[k & 1][sb * R + rr][i];
             if (o < N) h[o] = to_bf16(v);
@@ -500,7 +518,8 @@ size_t skinny_ws_bytes(int64_t M, int r) {
 bool gemv1_takes(const QView& q, int64_t M, int r) {
     const int64_t nkb = q.cols / 64;
     // (32-bit byte offsets inside the kernel: codes under 4 GB)
-    return M == 1 && r <= kSkinnyMaxR && r <= 64 && nkb <= 256 && q.rows * q.cols / 2 < (int64_t(1) << 32);
+    return M == 1 && r <= kSkinnyMaxR && r <= 64 && nkb <= 256 && q.rows * q.cols / 2 < (int64_t(1) << 32) &&
+           q.rows < (int64_t(1) << 31);
 }
 
 int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
@@ -515,10 +534,11 @@ int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t*
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (gemv1) {
         const bool b128 = q.bshift == 7;
-        auto kern = b128 ? (q.dq ? (q.gshift >= 0 ? k_gemv1<true, true, 1> : k_gemv1<true, false, 1>)
-                                 : k_gemv1<false, true, 1>)
-                         : (q.dq ? (q.gshift >= 0 ? k_gemv1<true, true, 0> : k_gemv1<true, false, 0>)
-                                 : k_gemv1<false, true, 0>);
+        constexpr int NV = NF4_GEMV_NV;
+        auto kern = b128 ? (q.dq ? (q.gshift >= 0 ? k_gemv1<true, true, 1, NV> : k_gemv1<true, false, 1, NV>)
+                                 : k_gemv1<false, true, 1, NV>)
+                         : (q.dq ? (q.gshift >= 0 ? k_gemv1<true, true, 0, NV> : k_gemv1<true, false, 0, NV>)
+                                 : k_gemv1<false, true, 0, NV>);
         const int slot = (q.dq ? (q.gshift >= 0 ? 0 : 1) : 2) + (b128 ? 3 : 0);
         const int64_t rows_chunk = (4 / R) * G1_NC;
         const int64_t nchunks = cdiv(q.rows, rows_chunk);

@@ -403,9 +403,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
         for (int e = 1; e < 15; ++e)
             if (e != 7) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+        if constexpr (NV < 8) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (e != 7) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(p[e]);
+            for (int e = 0; e < 16; ++e)
+                if (e != 7) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(p[e]);
+        }
         Planes pl;
         if constexpr (NV > 0) {
             uint32_t wp[8];

@@ -168,7 +168,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     auto process = [&](const Fetch& f) {
         const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
         const float s = f.ok ? sc : 0.0f;
-        // entries 0 and 15 are -s and +s exactly; entry 7 (level 0) stays 0
+        // entries 0 and 15 are -s and +s exactly; entry 7 is s * 0 (NaN for
+        // the NaN scale of a non-finite block)
         const uint32_t pe = pack_bf16x2(-s, s);
         put(0, uint16_t(pe));
         put(15, uint16_t(pe >> 16));
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         pair(8, 9);
         pair(10, 11);
         pair(12, 13);
-        put(14, to_bf16(__fmul_rn(s, bits_f(level_bits(14)))));
+        pair(7, 14);
         const float d = f.ok ? bf16_f(uint16_t(f.dv)) : 0.0f;
         const uint32_t cw[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
         // the lookups of code dword st+1 are issued before the FMAs of dword

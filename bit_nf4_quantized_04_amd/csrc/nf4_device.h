@@ -136,11 +136,10 @@ __device__ __forceinline__ Planes planes_of_pairs(const uint32_t (&w)[8]) {
 __device__ __forceinline__ Planes make_planes(float s) {
     float p[16];
     p[0] = -s;
-    p[7] = 0.0f;
     p[15] = s;
+    // (level 0 too: s * 0 is -0 for a negative scale and NaN for a NaN one)
 #pragma unroll
-    for (int e = 1; e < 15; ++e)
-        if (e != 7) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+    for (int e = 1; e < 15; ++e) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
     uint32_t w[8];  // w[i] = bf16 pair (entry 2i, entry 2i+1)
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);

@@ -316,8 +316,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     if (DQ) q127[tid] = q_over_127(int8_t(tid));
     char* tb = reinterpret_cast<char*>(&tbl[0][0][0]);
     char* mine = tb + (w * 16 * 64 + l) * 4;  // slot (w, 0, l); entry stride 256 B
-    // entry 7 (level 0) stays {0, 0}; the others are rewritten for every row
-    *reinterpret_cast<uint32_t*>(mine + 7 * 256) = 0u;
     // u = sum of the down-projection partials, in a fixed order
     for (int idx = tid; idx < r; idx += 256) {
         float a = 0.0f;
@@ -396,17 +394,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const float s = (ok && blk_ok) ? sc : 0.0f;
         // the block's 16 products; the LDS table holds them as {0, v} slots,
         // written two per instruction (entries e and e+1 are 256 B apart)
+        // (level 0 included: s * 0 is NaN for the NaN scale of a non-finite block)
         float p[16];
         p[0] = -s;
-        p[7] = 0.0f;
         p[15] = s;
 #pragma unroll
-        for (int e = 1; e < 15; ++e)
-            if (e != 7) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+        for (int e = 1; e < 15; ++e) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
         if constexpr (NV < 8) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (e != 7) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(p[e]);
+            for (int e = 0; e < 16; ++e) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(p[e]);
         }
         Planes pl;
         if constexpr (NV > 0) {

@@ -28,6 +28,49 @@ def F():
     return nf4qlora
 
 
+def _nan_close(name, got, ref):
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref), err_msg=name + ": NaN pattern")
+    ok = ~np.isnan(ref)
+    assert ok.any() and (~ok).any()
+    U.assert_close(name, got[ok], ref[ok])
+
+
+@pytest.mark.parametrize("dq", [False, True])
+@pytest.mark.parametrize("M", [1, 4, 16, 64, 300, 1100])
+def test_non_finite_weights_through_the_layer(F, M, dq):
+    """A weight with one NaN and one Inf element, through the forward and the
+    backward at token counts that reach every product kernel (the single-token
+    GEMV, the few-token kernels, the tiled GEMMs): an output reading a
+    non-finite block is NaN, as in the oracle (s * T[c] with s NaN, for level
+    0 too), and every other output matches the oracle."""
+    import torch
+
+    out, inp, r, s = 4096, 1024, 16, 2.0
+    rng = np.random.default_rng(83 + M + dq)
+    w = (rng.standard_normal((out, inp)) * 0.02).astype(np.float32)
+    w[100, 70] = np.nan
+    w[3000, 1000] = -np.inf
+    ref = O.quantize(w, double_quant=dq)
+    x = O.rne_bf16_bits(rng.standard_normal((M, inp)).astype(np.float32))
+    a = O.rne_bf16_bits((rng.standard_normal((r, inp)) * 0.05).astype(np.float32))
+    b = O.rne_bf16_bits((rng.standard_normal((out, r)) * 0.01).astype(np.float32))
+    dh = O.rne_bf16_bits(rng.standard_normal((M, out)).astype(np.float32))
+    q = F.nf4_quantize(U.f32(w), double_quant=dq)
+    h, u = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), s, want_u=True)
+    dX, dA, dB = F.qlora_linear_backward(q, U.bf(x), U.bf(dh), U.bf(a), U.bf(b), s, u=u)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(ref, w.shape)
+    href, _ = O.forward(wb, x, a, b, s)
+    g = O.backward(wb, x, dh, a, b, s)
+    _nan_close("h", U.bf16_to_f64(h), href)
+    if dq:  # a NaN group constant reaches every dX column
+        assert np.isnan(g["dX"]).all() and np.isnan(U.bf16_to_f64(dX)).all()
+    else:
+        _nan_close("dX", U.bf16_to_f64(dX), g["dX"])
+    U.assert_close("dA", dA.cpu().numpy(), g["dA"])
+    U.assert_close("dB", dB.cpu().numpy(), g["dB"])
+
+
 @pytest.mark.parametrize("dq,block", [(False, 64), (True, 64), (True, 128)])
 def test_non_finite_blocks(F, dq, block):
     import torch

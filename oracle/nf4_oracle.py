@@ -89,6 +89,40 @@ NF4_LEVELS = np.array(
     dtype=np.float32,
 )
 
+# ---------------------------------------------------------------------------
+# FP4, the other 4-bit quant type ("QLoRA Specification for EMEP Fine-Tuning",
+# "Hyperparameters": nf4 or fp4).  The pages say only that FP4 is an
+# IEEE-style exponent/mantissa format ("QLoRA explained", "Common
+# misconceptions").  READING: the 4-bit float with one sign, two exponent
+# (bias 1) and one mantissa bit, no infinities or NaN -- the E2M1 element type
+# of the OCP Microscaling Formats specification (v1.0) -- with the code being
+# its bit pattern; its values are divided by their maximum, 6, so that the
+# block's absmax maps to +-1 exactly as with NF4.
+# ---------------------------------------------------------------------------
+def e2m1_value(code: int) -> float:
+    """Value of the E2M1 bit pattern ``code`` (0..15): sign bit 3, exponent
+    bits 2..1, mantissa bit 0; exponent field 0 is subnormal (m * 2**-1),
+    otherwise 2**(e - 1) * (1 + m / 2)."""
+    sign = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1.0 + m * 0.5)
+    return sign * mag
+
+
+# fl32(value / 6): one float32 division of exact operands
+FP4_LEVELS = np.array([np.float32(e2m1_value(c)) / np.float32(6) for c in range(16)], dtype=np.float32)
+
+QUANT_TYPES = ("nf4", "fp4")
+
+
+def levels(quant_type: str = "nf4") -> np.ndarray:
+    if quant_type == "nf4":
+        return NF4_LEVELS
+    if quant_type == "fp4":
+        return FP4_LEVELS
+    raise ValueError("quant type %r" % (quant_type,))
+
+
 BLOCK_SIZE = 64  # "QLoRA Finetuner", section 2: static blocks of 64 elements
 DQ_GROUP = 256  # "From LoRA to QLoRA", Pillar 2: second pass block size 256
 
@@ -182,6 +216,28 @@ def nearest_code(wn) -> np.ndarray:
     return np.argmin(d, axis=-1).astype(np.uint8)
 
 
+def nearest_code_fp4(wn) -> np.ndarray:
+    """FP4 code of each normalized value: the sign bit of w' and the nearest
+    of the eight magnitudes FP4_LEVELS[0..7] to |w'|.
+
+    As in ``nearest_code`` the distances are exact where they decide.
+    READING: IEEE-style conversion keeps the sign (a zero or a value that
+    rounds to zero keeps the sign of w') and breaks an exact tie to the even
+    code (mantissa bit 0), as IEEE round-to-nearest-even does.
+    """
+    w = _as_f32(wn)
+    mag = np.abs(w.astype(np.float64))
+    lv = FP4_LEVELS[:8].astype(np.float64)
+    d = np.abs(mag[..., None] - lv)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among the tied candidates (at most two, adjacent) take the even one
+    even = cand & ((np.arange(8) & 1) == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    neg = np.signbit(w)
+    return (code + 8 * neg).astype(np.uint8)
+
+
 def pack_codes(codes) -> np.ndarray:
     """Two 4-bit codes per byte, element 2i in the high nibble
     ("From LoRA to QLoRA", worked example, "Byte Packing")."""
@@ -199,20 +255,27 @@ def unpack_codes(packed) -> np.ndarray:
     return out
 
 
-def quantize_first_level(w, block_size: int = BLOCK_SIZE):
-    """Blockwise NF4 quantization: returns (codes[unpacked], absmax[fp32]).
+def zero_code(quant_type: str = "nf4") -> int:
+    """The code of level 0.0: 7 for NF4, 0 (+0) for FP4."""
+    return 7 if quant_type == "nf4" else 0
+
+
+def quantize_first_level(w, block_size: int = BLOCK_SIZE, quant_type: str = "nf4"):
+    """Blockwise 4-bit quantization: returns (codes[unpacked], absmax[fp32]).
 
     READING (the pages assume finite weights): a block that holds Inf or NaN
-    has no absmax scale; it is stored with scale NaN and code 7 (level 0) for
-    every element, so all of it dequantizes to NaN.
+    has no absmax scale; it is stored with scale NaN and the code of level 0
+    (7 for NF4, 0 for FP4) for every element, so all of it dequantizes to NaN.
+    An all-zero block gets that code too.
     """
+    levels(quant_type)
     blocks = split_blocks(w, block_size)
     bad = ~np.all(np.isfinite(blocks), axis=1)
     clean = np.where(bad[:, None], np.float32(0), blocks).astype(np.float32)
     s = block_absmax(clean)
     wn = normalize(clean, s)
-    codes = nearest_code(wn)
-    codes[s == 0, :] = 7  # all-zero block: every normalized value is 0 -> level 0.0
+    codes = nearest_code(wn) if quant_type == "nf4" else nearest_code_fp4(wn)
+    codes[s == 0, :] = zero_code(quant_type)  # all-zero block: every normalized value is 0 -> level 0.0
     s[bad] = np.float32(np.nan)
     return codes.reshape(-1), s
 
@@ -269,10 +332,13 @@ def decode_scales(q, c, group: int = DQ_GROUP) -> np.ndarray:
     return (frac * cc[gidx]).astype(np.float32)
 
 
-def quantize(w, double_quant: bool, block_size: int = BLOCK_SIZE, dq_group: int = DQ_GROUP):
-    """The full storage format: dict(codes=packed u8, absmax, scale_codes, group_absmax)."""
-    codes, s = quantize_first_level(w, block_size)
-    out = {"codes": pack_codes(codes), "absmax": s, "scale_codes": None, "group_absmax": None}
+def quantize(w, double_quant: bool, block_size: int = BLOCK_SIZE, dq_group: int = DQ_GROUP,
+             quant_type: str = "nf4"):
+    """The full storage format: dict(codes=packed u8, absmax, scale_codes,
+    group_absmax, quant_type)."""
+    codes, s = quantize_first_level(w, block_size, quant_type)
+    out = {"codes": pack_codes(codes), "absmax": s, "scale_codes": None, "group_absmax": None,
+           "quant_type": quant_type}
     if double_quant:
         q, c = double_quantize_scales(s, dq_group)
         out["scale_codes"] = q
@@ -288,11 +354,12 @@ def block_scales(qt, block_size: int = BLOCK_SIZE, dq_group: int = DQ_GROUP) -> 
 
 
 def dequantize(qt, shape, block_size: int = BLOCK_SIZE, dq_group: int = DQ_GROUP) -> np.ndarray:
-    """w~ = fl32(scale_b * T[code])  ("QLoRA Finetuner", section 2, last item)."""
+    """w~ = fl32(scale_b * T[code])  ("QLoRA Finetuner", section 2, last item),
+    T the level table of the weight's quant type (NF4 unless stated)."""
     codes = unpack_codes(qt["codes"])
     sc = block_scales(qt, block_size, dq_group)
     per_elem = np.repeat(sc, block_size)
-    w = (per_elem * NF4_LEVELS[codes]).astype(np.float32)
+    w = (per_elem * levels(qt.get("quant_type", "nf4"))[codes]).astype(np.float32)
     return w.reshape(shape)
 
 

@@ -874,3 +874,111 @@ def test_non_finite_blocks_dequantize_to_nan():
     np.testing.assert_array_equal(q[8:16], qc[8:16])
     dd = O.dequantize(O.quantize(bad, double_quant=True, dq_group=8), bad.shape, dq_group=8)
     assert np.all(np.isnan(dd[[0, 2, 3]])) and not np.any(np.isnan(dd[1]))
+
+
+# ---------------------------------------------------------------- FP4 (E2M1)
+# The published E2M1 element values (OCP Microscaling Formats v1.0, the FP4
+# table): positive codes 0..7, negative codes 8..15 in the same order.
+E2M1_PUBLISHED = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_fp4_levels_are_the_published_e2m1_values_over_six():
+    for c in range(16):
+        v = E2M1_PUBLISHED[c & 7] * (-1.0 if c & 8 else 1.0)
+        assert O.e2m1_value(c) == v
+        want = _f32_from_fraction(Fraction(v).limit_denominator(2) / 6)
+        assert O.FP4_LEVELS[c] == want, c
+        assert np.signbit(O.FP4_LEVELS[c]) == bool(c & 8)
+    assert O.FP4_LEVELS[7] == 1.0 and O.FP4_LEVELS[15] == -1.0
+    assert np.all(np.diff(O.FP4_LEVELS[:8]) > 0)
+
+
+def _exact_fp4_code(w: np.float32) -> int:
+    """Exact rational arg-min of |w| over the 8 magnitudes, ties to the even
+    code, sign bit of w."""
+    m = abs(Fraction(float(w)))
+    d = [abs(m - Fraction(float(t))) for t in O.FP4_LEVELS[:8]]
+    best = min(d)
+    cands = [k for k in range(8) if d[k] == best]
+    k = [c for c in cands if c % 2 == 0][0] if len(cands) > 1 else cands[0]
+    return k + (8 if np.signbit(w) else 0)
+
+
+def test_fp4_code_matches_exact_rational_argmin():
+    rng = np.random.default_rng(401)
+    w = rng.uniform(-1, 1, 3000).astype(np.float32)
+    lv = O.FP4_LEVELS[:8].astype(np.float64)
+    mids = []
+    for i in range(7):  # around every midpoint, a few ulps each side
+        mid = np.float32((lv[i] + lv[i + 1]) / 2)
+        for k in range(-3, 4):
+            v = mid
+            for _ in range(abs(k)):
+                v = np.nextafter(v, np.float32(np.inf if k > 0 else -np.inf), dtype=np.float32)
+            mids += [v, -v]
+    w = np.concatenate([w, np.array(mids, dtype=np.float32), O.FP4_LEVELS, np.float32([0.0, -0.0, 1e-30, -1e-30])])
+    got = O.nearest_code_fp4(w)
+    want = np.array([_exact_fp4_code(v) for v in w], dtype=np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_fp4_exact_ties_go_to_the_even_code():
+    # of the seven midpoints only the one between 0 and fl32(1/12) is a
+    # float32 value; there the even code is also the lower one (0)
+    lv = O.FP4_LEVELS[:8]
+    hit = 0
+    for i in range(7):
+        mid = (Fraction(float(lv[i])) + Fraction(float(lv[i + 1]))) / 2
+        f = np.float32(float(mid))
+        if Fraction(float(f)) != mid:
+            continue  # not a float32: no float32 input can tie there
+        hit += 1
+        even = i if i % 2 == 0 else i + 1
+        assert O.nearest_code_fp4(np.float32([f]))[0] == even
+        assert O.nearest_code_fp4(np.float32([-f]))[0] == even + 8
+    assert hit == 1
+
+
+def test_fp4_signed_zero_and_zero_block():
+    w = np.zeros(64, dtype=np.float32)
+    w[3] = -0.0
+    codes, s = O.quantize_first_level(w, quant_type="fp4")
+    assert s[0] == 0 and np.all(codes == 0)  # all-zero block: +0 everywhere
+    w = np.full(64, 1e-9, dtype=np.float32)
+    w[0], w[1] = 1.0, -1e-9
+    codes, s = O.quantize_first_level(w, quant_type="fp4")
+    assert codes[0] == 7 and codes[2] == 0 and codes[1] == 8  # -tiny rounds to -0
+
+
+def test_fp4_grid_values_round_trip():
+    # a block holding s * level for every code (s a power of two, so every
+    # product and quotient is exact) quantizes to those codes and back
+    for s in (np.float32(1.0), np.float32(0.25), np.float32(2.0 ** -20)):
+        codes = np.array([c for c in range(16) if c != 8] * 5)[:64]
+        w = (O.FP4_LEVELS[codes] * s).astype(np.float32)
+        q = O.quantize(w, double_quant=False, quant_type="fp4")
+        np.testing.assert_array_equal(O.unpack_codes(q["codes"]), codes)
+        np.testing.assert_array_equal(O.dequantize(q, w.shape), w)
+
+
+def test_fp4_error_bound_and_differs_from_nf4():
+    rng = np.random.default_rng(402)
+    w = (rng.standard_normal(64 * 200) * 0.02).astype(np.float32)
+    q = O.quantize(w, double_quant=False, quant_type="fp4")
+    d = O.dequantize(q, w.shape)
+    s = np.repeat(q["absmax"], 64)
+    # the largest gap between neighbouring levels is 1/3 (between 2/3 and 1);
+    # one fl32 rounding of w/s and one of s*T add at most a few ulps of s
+    assert np.all(np.abs(d - w) <= s * (1.0 / 6) * (1 + 1e-6) + 4 * np.spacing(s))
+    qn = O.quantize(w, double_quant=False)
+    assert not np.array_equal(q["codes"], qn["codes"])
+    np.testing.assert_array_equal(q["absmax"], qn["absmax"])
+
+
+def test_fp4_non_finite_block_dequantizes_to_nan():
+    w = np.ones(128, dtype=np.float32) * 0.5
+    w[70] = np.inf
+    q = O.quantize(w, double_quant=False, quant_type="fp4")
+    assert np.all(O.unpack_codes(q["codes"])[64:] == 0) and np.isnan(q["absmax"][1])
+    d = O.dequantize(q, w.shape)
+    assert np.all(np.isnan(d[64:])) and np.all(d[:64] == 0.5)

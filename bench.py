@@ -624,15 +624,16 @@ def main():
         print("warning: the GEMV's event-measured time %.5f ms exceeds the step's %.5f ms" % (k_ms, t_dec),
               file=sys.stderr)
     extra_timings(line, args, timed, torch, F, wl, dev, bf, ws, copies_of, qs, A, B, x1, scale, sh, out, inp, r,
-                  ngroups, Mtrain, xt, dH, ht, t_tr, ffwd, fbwd, q7, x7, dH7, A7, B7, s7, sh7, M7, r7, h7, f7, t_7b)
+                  ngroups, Mtrain, xt, dH, ht, t_tr, ffwd, fbwd, q7, x7, dH7, A7, B7, s7, sh7, M7, r7, h7, f7, t_7b, settle)
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["cpu_baseline_other"] = cpu_baselines()
     print(json.dumps(line), flush=True)
 
 
 def extra_timings(line, args, timed, torch, F, wl, dev, bf, ws, copies_of, qs, A, B, x1, scale, sh, out, inp, r,
-                  ngroups, Mtrain, xt, dH, ht, t_tr, ffwd, fbwd, q7, x7, dH7, A7, B7, s7, sh7, M7, r7, h7, f7, t_7b):
-    """The rows beyond the hot path: merge, AdamW, blocks of 128, dropout."""
+                  ngroups, Mtrain, xt, dH, ht, t_tr, ffwd, fbwd, q7, x7, dH7, A7, B7, s7, sh7, M7, r7, h7, f7, t_7b,
+                  settle):
+    """The rows beyond the hot path: merge, AdamW, blocks of 128, FP4, dropout."""
     K, W = args.steps, args.warmup
     wm = torch.empty((out, inp), dtype=torch.bfloat16, device=dev)
     t_mg, _ = timed(lambda i: F.qlora_merge(qs[i % len(qs)], A, B, scale, out=wm), K, W)
@@ -653,9 +654,31 @@ def extra_timings(line, args, timed, torch, F, wl, dev, bf, ws, copies_of, qs, A
                                out, inp, True, 256, 128) for _ in range(2)]
     h1 = torch.empty((1, out), dtype=torch.bfloat16, device=dev)
     ws_d128 = ws(F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128, out, inp, 1, r)
-    t_d128, _ = timed(lambda i: F.qlora_linear_forward(q128[i % len(q128)], x1, A, B, scale, ws=ws_d128, out=h1),
-                      K, W)
+    d128_step = (lambda i: F.qlora_linear_forward(q128[i % len(q128)], x1, A, B, scale, ws=ws_d128, out=h1))
+    settle(d128_step)
+    t_d128, _ = timed(d128_step, K, W)
     del q128, q0
+    # FP4 codes (the other quant type): the decode step and the 7B training pass
+    wt = torch.from_numpy(wl.weight(4)).to(dev)
+    q0 = F.nf4_quantize(wt, double_quant=True, quant_type="fp4")
+    del wt
+    qf4 = [q0] + [F.NF4Weight(q0.codes.clone(), q0.absmax.clone(), q0.scale_codes.clone(), q0.group_absmax.clone(),
+                              out, inp, True, 256, 64, "fp4") for _ in range(len(qs) - 1)]
+    ws_f1 = ws(F.QLORA_OP_FORWARD, out, inp, 1, r)
+    f4_step = (lambda i: F.qlora_linear_forward(qf4[i % len(qf4)], x1, A, B, scale, ws=ws_f1, out=h1))
+    settle(f4_step)
+    t_f4, _ = timed(f4_step, K, W)
+    del qf4, q0
+    q7f = F.nf4_quantize(torch.from_numpy(wl.weight(3)).to(dev), double_quant=True, quant_type="fp4")
+    wsf7f = ws(F.QLORA_OP_FORWARD, sh7["out"], sh7["inp"], M7, r7)
+    wsb7f = ws(F.QLORA_OP_BACKWARD, sh7["out"], sh7["inp"], M7, r7)
+
+    def train7_fp4_step(i):
+        _, u = F.qlora_linear_forward(q7f, x7, A7, B7, s7, want_u=True, ws=wsf7f, out=h7)
+        F.qlora_linear_backward(q7f, x7, dH7, A7, B7, s7, u=u, ws=wsb7f)
+
+    t_7bf4, _ = timed(train7_fp4_step, K, W)
+    del q7f, wsf7f, wsb7f
     q7b = F.nf4_quantize(torch.from_numpy(wl.weight(3)).to(dev), double_quant=True, block_size=128)
     wsf7b = ws(F.QLORA_OP_FORWARD | F.QLORA_OP_BLOCK128, sh7["out"], sh7["inp"], M7, r7)
     wsb7b = ws(F.QLORA_OP_BACKWARD | F.QLORA_OP_BLOCK128, sh7["out"], sh7["inp"], M7, r7)
@@ -708,6 +731,17 @@ def extra_timings(line, args, timed, torch, F, wl, dev, bf, ws, copies_of, qs, A
         "train_7b_ms": round(t_7b128, 4),
         "train_7b_TFLOPs": round(f7 / (t_7b128 * 1e-3) / 1e12, 2),
         "train_7b_frac_mfma_peak": round(f7 / (t_7b128 * 1e-3) / 1e12 / MF, 4),
+    }
+    f4_bytes = decode_bytes(out, inp, 1, r, ngroups)
+    line["fp4"] = {
+        "workload": "weights quantized to FP4 (E2M1 codes, levels value/6; blocks of 64, double quant in groups "
+                    "of 256): the 70B decode step and the 7B training pass",
+        "decode_ms": round(t_f4, 5),
+        "decode_GBps": round(f4_bytes / (t_f4 * 1e-3) / 1e9, 2),
+        "decode_frac_hbm_peak": round(f4_bytes / (t_f4 * 1e-3) / 1e9 / HB, 4),
+        "train_7b_ms": round(t_7bf4, 4),
+        "train_7b_TFLOPs": round(f7 / (t_7bf4 * 1e-3) / 1e12, 2),
+        "train_7b_frac_mfma_peak": round(f7 / (t_7bf4 * 1e-3) / 1e12 / MF, 4),
     }
     line["dropout"] = {
         "workload": "the training pass (M=%d) and the 7B training pass with dropout p=%g on the adapter "

@@ -25,6 +25,7 @@ int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
     if (t->rows < 0 || t->cols < 0) return NF4_EINVAL;
     if (t->cfg.double_quant != 0 && t->cfg.double_quant != 1) return NF4_EINVAL;
     if (t->cfg.double_quant && t->cfg.dq_group < 1) return NF4_EUNSUPPORTED;
+    if (t->cfg.quant_type != NF4_QUANT_NF4 && t->cfg.quant_type != NF4_QUANT_FP4) return NF4_EUNSUPPORTED;
     const int64_t n = t->rows * t->cols;
     if ((linear && t->cols % 64 != 0) || n % t->cfg.block_size != 0) return NF4_ESHAPE;
     if (n / 64 >= (int64_t(1) << 31)) return NF4_EINVAL;  // block indices are 32-bit
@@ -48,6 +49,7 @@ int view_of(const nf4_tensor* t, bool linear, nf4::QView* v) {
     for (int sh = 0; sh < 31; ++sh)
         if ((1 << sh) == v->group) v->gshift = sh;
     v->bshift = t->cfg.block_size == 128 ? 7 : 6;
+    v->qt = t->cfg.quant_type;
     return NF4_OK;
 }
 
@@ -145,9 +147,9 @@ extern "C" {
 namespace {
 struct LevelTable {
     float v[16];
-    LevelTable() {
+    explicit LevelTable(int qt) {
         for (int i = 0; i < 16; ++i) {
-            const uint32_t b = nf4dev::level_bits(i);
+            const uint32_t b = nf4dev::qt_level_bits(qt, i);
             memcpy(&v[i], &b, 4);
         }
     }
@@ -155,8 +157,14 @@ struct LevelTable {
 }  // namespace
 
 const float* nf4_table(void) {
-    static const LevelTable t;  // initialised once, thread-safe (C++11 function-local static)
+    static const LevelTable t(NF4_QUANT_NF4);  // initialised once, thread-safe (C++11 function-local static)
     return t.v;
+}
+
+const float* nf4_levels(int32_t quant_type) {
+    static const LevelTable fp4(NF4_QUANT_FP4);
+    if (quant_type == NF4_QUANT_NF4) return nf4_table();
+    return quant_type == NF4_QUANT_FP4 ? fp4.v : nullptr;
 }
 
 const char* nf4_strerror(int code) {
@@ -164,7 +172,8 @@ const char* nf4_strerror(int code) {
         case NF4_OK: return "ok";
         case NF4_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad rank or scale)";
         case NF4_ESHAPE: return "shape not a multiple of the 64-element block (linear calls: cols % 64 != 0)";
-        case NF4_EUNSUPPORTED: return "unsupported configuration (block_size must be 64 or 128, dq_group >= 1)";
+        case NF4_EUNSUPPORTED:
+            return "unsupported configuration (block_size must be 64 or 128, dq_group >= 1, quant_type NF4 or FP4)";
         case NF4_EWORKSPACE: return "workspace missing or smaller than qlora_workspace_bytes()";
         case NF4_ELAUNCH: return "HIP kernel launch failed (see nf4_last_hip_error)";
         case NF4_ETOOLARGE:
@@ -210,14 +219,15 @@ int quantize_any(const void* W, bool bf16, int64_t rows, int64_t cols, const nf4
     if (cfg->block_size != 64 && cfg->block_size != 128) return NF4_EUNSUPPORTED;
     if (cfg->double_quant != 0 && cfg->double_quant != 1) return NF4_EINVAL;
     if (cfg->double_quant && cfg->dq_group < 1) return NF4_EUNSUPPORTED;
+    if (cfg->quant_type != NF4_QUANT_NF4 && cfg->quant_type != NF4_QUANT_FP4) return NF4_EUNSUPPORTED;
     if (rows < 0 || cols < 0) return NF4_EINVAL;
     const int64_t n = rows * cols;
     if (n % cfg->block_size != 0) return NF4_ESHAPE;
     if (n == 0) return NF4_OK;
     if (bad_ptr(W) || bad_ptr(codes) || bad_ptr(absmax)) return NF4_EINVAL;
     if (cfg->double_quant && (bad_ptr(scale_codes) || bad_ptr(group_absmax))) return NF4_EINVAL;
-    return nf4::launch_quantize(W, bf16, n, cfg->block_size, cfg->double_quant, cfg->dq_group, codes, absmax,
-                                scale_codes, group_absmax, static_cast<hipStream_t>(stream));
+    return nf4::launch_quantize(W, bf16, n, cfg->block_size, cfg->double_quant, cfg->dq_group, cfg->quant_type,
+                                codes, absmax, scale_codes, group_absmax, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace

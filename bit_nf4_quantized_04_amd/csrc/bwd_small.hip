@@ -164,28 +164,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
     for (int c = 0; c < 64; ++c) acc[c] = 0.0f;
 
+    // the levels of the weight's quant type (wave-uniform)
+    float lvf[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lvf[e] = uniform_level(q.qt, e);
     auto put = [&](int e, uint16_t v) { *reinterpret_cast<uint16_t*>(mine + e * 256 + 2) = v; };
     auto process = [&](const Fetch& f) {
         const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
         const float s = f.ok ? sc : 0.0f;
-        // entries 0 and 15 are -s and +s exactly; entry 7 is s * 0 (NaN for
-        // the NaN scale of a non-finite block)
-        const uint32_t pe = pack_bf16x2(-s, s);
-        put(0, uint16_t(pe));
-        put(15, uint16_t(pe >> 16));
+        // every entry is s * T[e], level 0 included (NaN for the NaN scale of
+        // a non-finite block)
         auto pair = [&](int e0, int e1) {
-            const uint32_t pk = pack_bf16x2(__fmul_rn(s, bits_f(level_bits(e0))),
-                                            __fmul_rn(s, bits_f(level_bits(e1))));
+            const uint32_t pk = pack_bf16x2(__fmul_rn(s, lvf[e0]), __fmul_rn(s, lvf[e1]));
             put(e0, uint16_t(pk));
             put(e1, uint16_t(pk >> 16));
         };
-        pair(1, 2);
-        pair(3, 4);
-        pair(5, 6);
-        pair(8, 9);
-        pair(10, 11);
-        pair(12, 13);
-        pair(7, 14);
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) pair(e, e + 1);
         const float d = f.ok ? bf16_f(uint16_t(f.dv)) : 0.0f;
         const uint32_t cw[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
         // the lookups of code dword st+1 are issued before the FMAs of dword

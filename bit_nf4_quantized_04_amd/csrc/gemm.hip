@@ -241,13 +241,20 @@ struct OutMulti {
     }
 };
 
+// Quant type of the NF4 operand among a product's loaders (NF4 when none).
+template <class L>
+__device__ __forceinline__ int loader_qt(const L&) { return 0; }
+__device__ __forceinline__ int loader_qt(const LdNF4Rows& l) { return l.q.qt; }
+__device__ __forceinline__ int loader_qt(const LdNF4Cols& l) { return l.q.qt; }
+
 // ------------------------------------------------------------------ kernel
 template <class LA1, class LB1, class LA2, class LB2, class OUT>
 __global__ __launch_bounds__(NT) void k_gemm(LA1 la1, LB1 lb1, int64_t K1, LA2 la2, LB2 lb2,
                                              int64_t K2, OUT out, int64_t Mr, int64_t Nc,
                                              int splits) {
     __shared__ Smem sm;
-    if (threadIdx.x < 16) sm.lv[threadIdx.x] = bits_f(level_bits(threadIdx.x));
+    const int qt = loader_qt(la1) | loader_qt(lb1) | loader_qt(la2) | loader_qt(lb2);
+    if (threadIdx.x < 16) sm.lv[threadIdx.x] = bits_f(qt_level_bits(qt, threadIdx.x));
     if (threadIdx.x < 256) sm.q127[threadIdx.x] = q_over_127(int8_t(threadIdx.x));
     const int64_t n0 = int64_t(blockIdx.x) * BN, m0 = int64_t(blockIdx.y) * BM;
     const int z = blockIdx.z;

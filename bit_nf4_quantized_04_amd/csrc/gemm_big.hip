@@ -93,8 +93,6 @@ __device__ __forceinline__ float blk_scale(const nf4::QView& q, uint32_t qb, flo
     return q.dq ? __fmul_rn(q_over_127(int8_t(qb & 255u)), cg) : __builtin_bit_cast(float, qb);
 }
 
-// The 16 fp32 levels (constant-folded when e is a constant).
-__device__ __forceinline__ float level(int e) { return bits_f(level_bits(e)); }
 
 // NF4 weight rows (forward): element (n, k) = Wb[n][k].  Producer waves 0-3:
 // thread t < 256 owns the 64-element block of row row0 + t in this K step.
@@ -129,7 +127,8 @@ struct NF4Rows {
         const float s = r.ok ? blk_scale(q, r.qb, r.cg) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-            const uint32_t pk = pack_bf16x2(__fmul_rn(s, level(e)), __fmul_rn(s, level(e + 1)));
+            const uint32_t pk = pack_bf16x2(__fmul_rn(s, bits_f(qt_level_bits(q.qt, e))),
+                                            __fmul_rn(s, bits_f(qt_level_bits(q.qt, e + 1))));
             sm.tb[w][e][2 * l] = uint16_t(pk);
             sm.tb[w][e + 1][2 * l] = uint16_t(pk >> 16);
         }
@@ -204,8 +203,8 @@ struct NF4Cols {
                 const uint32_t cd = r.c[i][rr];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    w[rr][2 * j] = __fmul_rn(s, bits_f(level_bits((cd >> (8 * j + 4)) & 15u)));
-                    w[rr][2 * j + 1] = __fmul_rn(s, bits_f(level_bits((cd >> (8 * j)) & 15u)));
+                    w[rr][2 * j] = __fmul_rn(s, bits_f(qt_level_bits(q.qt, (cd >> (8 * j + 4)) & 15u)));
+                    w[rr][2 * j + 1] = __fmul_rn(s, bits_f(qt_level_bits(q.qt, (cd >> (8 * j)) & 15u)));
                 }
             }
             const int n0 = (dc + 16 * i) * 8;

@@ -83,6 +83,7 @@ struct FwdArgs {
     // each) into tile-local fp32 partials [ztail][tile - tfull][RM][RN] at part
     int64_t tfull;
     int ztail, spl_tail;
+    int qt;  // quant type of the codes: 0 NF4, 1 FP4
 };
 
 // The gathered rank-r term of one output of the multi-adapter forward, fp32
@@ -150,6 +151,7 @@ struct FwdCtx {
     uint32_t coff[J];             // byte offset of this lane's code half-block, step 0
     uint32_t soff[J];             // byte offset of row j's block scale, step 0
     DecK dk;
+    Levels lv;                    // the levels of the codes' quant type
 
     // x tile of step s into LDS tile `dst`: DMA instruction i of wave w fills
     // chunk positions 64(XD w + i) .. +63 (one 16-byte chunk per lane).
@@ -280,11 +282,11 @@ __device__ __forceinline__ void nf4_step(const FwdCtx<NW>& c, int t, const uint4
     c.wread(wn, cwn, sc);
     c.wdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, wn);
     c.lookups(pl, cw, 2, ba);
-    pln[0] = make_planes(sc[0]);
+    pln[0] = make_planes(sc[0], c.lv);
     slice_mma<NW, J>(c, acc, f, bb, cur, 2);
     // slice 2: slice 3's B operand
     c.lookups(pl, cw, 3, bb);
-    if constexpr (J > 1) pln[J - 1] = make_planes(sc[J - 1]);
+    if constexpr (J > 1) pln[J - 1] = make_planes(sc[J - 1], c.lv);
     slice_mma<NW, J>(c, acc, f, ba, cur, 3);
     // slice 3: every wave's share of x tile t+1 is in (its fragments are read
     // during this slice); step t+1's first B operand
@@ -355,6 +357,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_rd(FwdArgs a) {
     c.w = w;
     c.lane = lane;
     c.dk.init();
+    c.lv.init(a.qt);
     int64_t wrow[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_rd(FwdArgs a) {
         c.wread(wb0, cw, sc);
         c.wdma(sb + 2 < S1 ? sb + 2 : S1 - 1, wb0);
 #pragma unroll
-        for (int j = 0; j < J; ++j) pl[j] = make_planes(sc[j]);
+        for (int j = 0; j < J; ++j) pl[j] = make_planes(sc[j], c.lv);
     }
     Frag fa;
     u32x4_t ba[J];
@@ -544,6 +547,7 @@ struct DxArgs {
     int KL, r;
     int spl;               // weight-row steps per split (a multiple of four)
     int f32;               // nonzero: fp32 partials even for one split
+    int qt;                // quant type of the codes: 0 NF4, 1 FP4
 };
 
 // W tile layout: row-major with a 576-byte row stride, and the 16-byte chunk
@@ -569,6 +573,7 @@ struct DxCtx {
     uint32_t soff;              // byte offset of its block scale, step 0
     uint32_t tro;               // byte offset of this lane's first transposed read in a W tile
     DecK dk;
+    Levels lv;                  // the levels of the codes' quant type
 
     __device__ __forceinline__ void hdma(int s, uint4* dst) const {
         const bool main = s < S1;
@@ -593,7 +598,7 @@ struct DxCtx {
         const char* mine = reinterpret_cast<const char*>(buf + DHBUF) + w * DSLOT;
         const uint4 cw = *reinterpret_cast<const uint4*>(mine + lane * 16);
         const float sc = *reinterpret_cast<const float*>(mine + 1024 + lane * 4);
-        const Planes p = make_planes(sc);
+        const Planes p = make_planes(sc, lv);
         u32x4_t o[4];
         lookup8(dk, p, cw.x, o[0]);
         lookup8(dk, p, cw.y, o[1]);
@@ -724,6 +729,7 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     c.lane = lane;
     c.tid = tid;
     c.dk.init();
+    c.lv.init(a.qt);
     {
         const int unit = tid >> 1, half = tid & 1;
         const int64_t row = unit >> 2, q = unit & 3;
@@ -940,7 +946,7 @@ int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, 
     const int S1 = int(q.rows / DK);
     const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);
     DxArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, dH, r > 0 ? duext : nullptr, A, dX, part_ws,
-             M, q.rows, q.cols, KL, r, spl, f32 ? 1 : 0};
+             M, q.rows, q.cols, KL, r, spl, f32 ? 1 : 0, q.qt};
     const int64_t T = cdiv(M, RM) * cdiv(q.cols, RN);
     launch_dominant(k_dx_rd, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
@@ -1005,7 +1011,7 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
     const TailPlan tp = tail_plan(M, q.rows, q.cols);
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, r > 0 ? ext : nullptr, B, h,
               M, q.rows, q.cols, KL, r, nullptr, nullptr, nullptr, 0, 0, tail_ws, int(q.cols / RKS),
-              tp.tfull, tp.z, tp.spl};
+              tp.tfull, tp.z, tp.spl, q.qt};
     launch_dominant(k_fwd_rd<false, kFwdWaves>, dim3(unsigned(tp.grid)), dim3(64 * kFwdWaves), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (tp.z > 1) {
@@ -1047,7 +1053,7 @@ int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* 
     const int S1 = int(q.cols / RKS);
     const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, nullptr, nullptr, h,
-              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl, 0, 1, spl};
+              M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl, 0, 1, spl, q.qt};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
     launch_dominant(k_fwd_rd<true, 4>, dim3(unsigned(T), unsigned(Z)), dim3(256), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t N = q.rows, K = q.cols;
     const int64_t nct = (K + MG_COLS - 1) / MG_COLS;
     const int64_t r0 = int64_t(blockIdx.x / nct) * (MG_ROWS * MG_SLABS), i0 = int64_t(blockIdx.x % nct) * MG_COLS;
-    if (tid < 16) lv[tid] = bits_f(level_bits(tid));
+    if (tid < 16) lv[tid] = bits_f(qt_level_bits(q.qt, tid));
 
     // this lane's transposed-read position: in each 16-lane group lane 4e + g
     // addresses k row 8(qq/2) + e, column 16(qq%2) + 4g of the wave's slab

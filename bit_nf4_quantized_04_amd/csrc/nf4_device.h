@@ -40,6 +40,37 @@ __host__ __device__ constexpr uint32_t cut_bits(int k) {
          : k == 12 ? 0x3f006d04u : k == 13 ? 0x3f248db0u : 0x3f5c89dau;
 }
 
+// FP4, the other quant type, read as the 4-bit float E2M1 (sign bit 3,
+// exponent bits 2..1 with bias 1, mantissa bit 0; exponent 0 subnormal; no
+// Inf/NaN -- the OCP Microscaling element type): level = fl32(value / 6), so
+// the block's absmax maps to 1.  Index = the E2M1 bit pattern: magnitudes 0,
+// 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1 and their negatives (code 8 is -0).
+__host__ __device__ inline uint32_t fp4_level_bits(int i) {
+    constexpr uint32_t t[8] = {0x00000000u, 0x3daaaaabu, 0x3e2aaaabu, 0x3e800000u,
+                               0x3eaaaaabu, 0x3f000000u, 0x3f2aaaabu, 0x3f800000u};
+    return t[i & 7] | ((i & 8) ? 0x80000000u : 0u);
+}
+
+// Decision thresholds of the FP4 magnitude search, as cut_bits does for NF4:
+// the smallest binary32 above the exact midpoint of magnitudes k and k+1, so
+// mag = #{k : |w'| >= cut_k}.  Only the midpoint of 0 and fl32(1/12) is a
+// binary32 value; a tie there goes to code 0, the even (and lower) code.
+__host__ __device__ constexpr uint32_t fp4_cut_bits(int k) {
+    return k == 0 ? 0x3d2aaaacu : k == 1 ? 0x3e000001u : k == 2 ? 0x3e555556u : k == 3 ? 0x3e955556u
+         : k == 4 ? 0x3ed55556u : k == 5 ? 0x3f155556u : 0x3f555556u;
+}
+
+// Level bits of quant type qt (0 = NF4, 1 = FP4) for code i.
+__host__ __device__ inline uint32_t qt_level_bits(int qt, int i) {
+    return qt ? fp4_level_bits(i) : level_bits(i);
+}
+
+// The same for a wave-uniform qt and constant i, as a scalar register (the
+// select would otherwise be made per lane and hold a vector register).
+__device__ __forceinline__ float uniform_level(int qt, int i) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(qt_level_bits(qt, i)));
+}
+
 __device__ __forceinline__ float bits_f(uint32_t b) { return __builtin_bit_cast(float, b); }
 __device__ __forceinline__ uint32_t f_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
@@ -133,13 +164,20 @@ __device__ __forceinline__ Planes planes_of_pairs(const uint32_t (&w)[8]) {
     return t;
 }
 
-__device__ __forceinline__ Planes make_planes(float s) {
+// Levels of a quant type as floats, held in (wave-uniform) registers.
+struct Levels {
+    float v[16];
+    __device__ __forceinline__ void init(int qt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = uniform_level(qt, e);
+    }
+};
+
+__device__ __forceinline__ Planes make_planes(float s, const Levels& lv) {
     float p[16];
-    p[0] = -s;
-    p[15] = s;
     // (level 0 too: s * 0 is -0 for a negative scale and NaN for a NaN one)
 #pragma unroll
-    for (int e = 1; e < 15; ++e) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+    for (int e = 0; e < 16; ++e) p[e] = __fmul_rn(s, lv.v[e]);
     uint32_t w[8];  // w[i] = bf16 pair (entry 2i, entry 2i+1)
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);

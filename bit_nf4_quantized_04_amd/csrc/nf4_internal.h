@@ -23,10 +23,11 @@ struct QView {  // a validated nf4_tensor
     int group;     // dq_group
     int gshift;    // log2(group) when group is a power of two, else -1
     int bshift;    // log2(block size): 6 (64 elements) or 7 (128)
+    int qt;        // quant type: 0 NF4, 1 FP4 (the level table of the codes)
 };
 
 // W: fp32, or bf16 bit patterns when `bf16`
-int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int group, uint8_t* codes,
+int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int group, int qt, uint8_t* codes,
                     float* absmax, int8_t* qcodes, float* gabs, hipStream_t s);
 // Every 64-element half of a 128-element block takes its block's fp32 scale,
 // or with double quant its int8 scale code (the group of dq_group blocks is

@@ -1,5 +1,5 @@
-// quant.hip -- NF4 blockwise quantizer, double quantization of the block
-// scales, and dequantization to fp32 / bf16.
+// quant.hip -- NF4 (or FP4) blockwise quantizer, double quantization of the
+// block scales, and dequantization to fp32 / bf16.
 //
 // Quantizer: "QLoRA Finetuner", section "2. Block-by-Block NormalFloat4 (NF4)
 // Quantization" (absmax per 64-element block, division by it, nearest of the
@@ -31,6 +31,25 @@ __device__ __forceinline__ uint32_t nearest_code(float w) {
     return c;
 }
 
+// FP4 code of a normalized value: the sign bit of w and the nearest of the
+// eight magnitudes, mag = #{k : |w| >= fp4_cut_k} by a three-step binary search.
+__device__ __forceinline__ uint32_t nearest_code_fp4(float w) {
+#define CUT(k) bits_f(fp4_cut_bits(k))
+    const float a = fabsf(w);
+    uint32_t c = (a >= CUT(3)) ? 4u : 0u;
+    c |= (a >= ((c & 4u) ? CUT(5) : CUT(1))) ? 2u : 0u;
+    const float lo = (c & 4u) ? ((c & 2u) ? CUT(6) : CUT(4)) : ((c & 2u) ? CUT(2) : CUT(0));
+    c |= (a >= lo) ? 1u : 0u;
+#undef CUT
+    return c | ((f_bits(w) >> 28) & 8u);
+}
+
+template <bool FP4>
+__device__ __forceinline__ uint32_t code_of(float w) {
+    if constexpr (FP4) return nearest_code_fp4(w);
+    else return nearest_code(w);
+}
+
 // Four consecutive input elements as fp32: an fp32 input, or bf16 bit
 // patterns widened exactly.
 __device__ __forceinline__ float4 load4(const float4* W, int64_t i) { return W[i]; }
@@ -43,7 +62,7 @@ __device__ __forceinline__ float4 load4(const uint2* W, int64_t i) {
 // (16 lanes for 64, 32 for 128).  The absmax is an L-lane butterfly max of
 // the magnitude bits (the integer order of |w| for finite w; Inf and NaN
 // sort above every finite value); codes of 4 elements pack into 2 bytes.
-template <int L, typename In>
+template <int L, typename In, bool FP4>
 __global__ __launch_bounds__(256) void k_quant_blocks(const In* __restrict__ W, int64_t n4,
                                                       uint16_t* __restrict__ codes,
                                                       float* __restrict__ absmax) {
@@ -59,18 +78,20 @@ __global__ __launch_bounds__(256) void k_quant_blocks(const In* __restrict__ W, 
         for (int off = L / 2; off >= 1; off >>= 1) mb = max(mb, uint32_t(__shfl_xor(int(mb), off, L)));
         float m = bits_f(mb);
         uint32_t packed;
+        // the code of level 0: 7 for NF4, 0 (+0) for FP4
+        constexpr uint32_t ZERO4 = FP4 ? 0x0000u : 0x7777u;
         if (mb >= 0x7f800000u) {
-            // a block holding Inf or NaN: scale NaN, every code level 7, so
-            // the whole block dequantizes to NaN
-            packed = 0x7777u;
+            // a block holding Inf or NaN: scale NaN, every code the level-0
+            // code, so the whole block dequantizes to NaN
+            packed = ZERO4;
             m = bits_f(0x7fc00000u);
         } else if (mb == 0u) {
-            packed = 0x7777u;  // an all-zero block: every element is level 7 (0.0)
+            packed = ZERO4;  // an all-zero block: every element is level 0.0
         } else {
-            const uint32_t c0 = nearest_code(__fdiv_rn(v.x, m));
-            const uint32_t c1 = nearest_code(__fdiv_rn(v.y, m));
-            const uint32_t c2 = nearest_code(__fdiv_rn(v.z, m));
-            const uint32_t c3 = nearest_code(__fdiv_rn(v.w, m));
+            const uint32_t c0 = code_of<FP4>(__fdiv_rn(v.x, m));
+            const uint32_t c1 = code_of<FP4>(__fdiv_rn(v.y, m));
+            const uint32_t c2 = code_of<FP4>(__fdiv_rn(v.z, m));
+            const uint32_t c3 = code_of<FP4>(__fdiv_rn(v.w, m));
             packed = ((c0 << 4) | c1) | (((c2 << 4) | c3) << 8);
         }
         codes[i] = uint16_t(packed);
@@ -114,9 +135,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ co
                                                  const float* __restrict__ absmax,
                                                  const int8_t* __restrict__ qcodes,
                                                  const float* __restrict__ gabs, int G, int dsh, int64_t n8,
-                                                 void* __restrict__ out) {
+                                                 int qt, void* __restrict__ out) {
     __shared__ float lv[16];
-    if (threadIdx.x < 16) lv[threadIdx.x] = bits_f(level_bits(threadIdx.x));
+    if (threadIdx.x < 16) lv[threadIdx.x] = bits_f(qt_level_bits(qt, threadIdx.x));
     __syncthreads();
     const int64_t stride = int64_t(gridDim.x) * 256;
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride) {
@@ -182,16 +203,19 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
 
 namespace nf4 {
 
-int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int group, uint8_t* codes,
+int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int group, int qt, uint8_t* codes,
                     float* absmax, int8_t* qcodes, float* gabs, hipStream_t s) {
     const int64_t n4 = n / 4;
     uint16_t* c16 = reinterpret_cast<uint16_t*>(codes);
+    const bool b128 = block == 128, fp4 = qt == 1;
     if (bf16) {
-        auto kern = block == 128 ? k_quant_blocks<32, uint2> : k_quant_blocks<16, uint2>;
+        auto kern = fp4 ? (b128 ? k_quant_blocks<32, uint2, true> : k_quant_blocks<16, uint2, true>)
+                        : (b128 ? k_quant_blocks<32, uint2, false> : k_quant_blocks<16, uint2, false>);
         hipLaunchKernelGGL(kern, dim3(grid_for(n4, 256)), dim3(256), 0, s, static_cast<const uint2*>(W), n4, c16,
                            absmax);
     } else {
-        auto kern = block == 128 ? k_quant_blocks<32, float4> : k_quant_blocks<16, float4>;
+        auto kern = fp4 ? (b128 ? k_quant_blocks<32, float4, true> : k_quant_blocks<16, float4, true>)
+                        : (b128 ? k_quant_blocks<32, float4, false> : k_quant_blocks<16, float4, false>);
         hipLaunchKernelGGL(kern, dim3(grid_for(n4, 256)), dim3(256), 0, s, static_cast<const float4*>(W), n4, c16,
                            absmax);
     }
@@ -209,14 +233,14 @@ int launch_quantize(const void* W, bool bf16, int64_t n, int block, int dq, int 
 int launch_dequant_f32(const QView& q, float* out, hipStream_t s) {
     const int64_t n8 = q.rows * q.cols / 8;
     hipLaunchKernelGGL(k_dequant<false>, dim3(grid_for(n8, 256)), dim3(256), 0, s, q.codes,
-                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, q.bshift - 3, n8, (void*)out);
+                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, q.bshift - 3, n8, q.qt, (void*)out);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 
 int launch_dequant_bf16(const QView& q, uint16_t* out, hipStream_t s) {
     const int64_t n8 = q.rows * q.cols / 8;
     hipLaunchKernelGGL(k_dequant<true>, dim3(grid_for(n8, 256)), dim3(256), 0, s, q.codes,
-                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, q.bshift - 3, n8, (void*)out);
+                       q.absmax, q.dq ? q.qcodes : nullptr, q.gabs, q.group, q.bshift - 3, n8, q.qt, (void*)out);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
         // the block's 16 products, bf16, into this lane's table column
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-            const uint32_t pk = pack_bf16x2(__fmul_rn(sblk, bits_f(level_bits(e))),
-                                            __fmul_rn(sblk, bits_f(level_bits(e + 1))));
+            const uint32_t pk = pack_bf16x2(__fmul_rn(sblk, bits_f(qt_level_bits(q.qt, e))),
+                                            __fmul_rn(sblk, bits_f(qt_level_bits(q.qt, e + 1))));
             sm.tbl[w][e][2 * l] = uint16_t(pk);
             sm.tbl[w][e + 1][2 * l] = uint16_t(pk >> 16);
         }
@@ -389,6 +389,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         ua[0] = uint32_t(hi) | (uint32_t(lo) << 16);
     }
 
+    // the levels of the weight's quant type (wave-uniform)
+    float lvf[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lvf[e] = uniform_level(q.qt, e);
     auto process = [&](const Fetch& f, bool ok, int par, int i) {
         const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
         const float s = (ok && blk_ok) ? sc : 0.0f;
@@ -396,10 +400,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         // written two per instruction (entries e and e+1 are 256 B apart)
         // (level 0 included: s * 0 is NaN for the NaN scale of a non-finite block)
         float p[16];
-        p[0] = -s;
-        p[15] = s;
 #pragma unroll
-        for (int e = 1; e < 15; ++e) p[e] = __fmul_rn(s, bits_f(level_bits(e)));
+        for (int e = 0; e < 16; ++e) p[e] = __fmul_rn(s, lvf[e]);
         if constexpr (NV < 8) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(p[e]);

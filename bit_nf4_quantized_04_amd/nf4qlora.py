@@ -26,13 +26,16 @@ _lib = C.CDLL(LIB_PATH)
 
 NF4_OK, NF4_EINVAL, NF4_ESHAPE, NF4_EUNSUPPORTED, NF4_EWORKSPACE, NF4_ELAUNCH, NF4_ETOOLARGE = range(7)
 QLORA_NOALLOC_SCRATCH_BYTES = 64 << 20
+NF4_QUANT_NF4, NF4_QUANT_FP4 = 0, 1
+QUANT_TYPES = {"nf4": NF4_QUANT_NF4, "fp4": NF4_QUANT_FP4}
 QLORA_OP_FORWARD, QLORA_OP_BACKWARD, QLORA_OP_FORWARD_MULTI = 1, 2, 3
 QLORA_OP_BLOCK128 = 0x100  # OR'ed into a workspace query for a weight with 128-element blocks
 QLORA_OP_DROPOUT = 0x200   # OR'ed into a workspace query for the *_dropout calls
 
 
 class nf4_config(C.Structure):
-    _fields_ = [("block_size", C.c_int32), ("double_quant", C.c_int32), ("dq_group", C.c_int32)]
+    _fields_ = [("block_size", C.c_int32), ("double_quant", C.c_int32), ("dq_group", C.c_int32),
+                ("quant_type", C.c_int32)]
 
 
 class nf4_tensor(C.Structure):
@@ -55,6 +58,7 @@ _P = C.c_void_p
 _I64 = C.c_int64
 _SIGS = {
     "nf4_table": (C.POINTER(C.c_float), []),
+    "nf4_levels": (C.POINTER(C.c_float), [C.c_int32]),
     "nf4_strerror": (C.c_char_p, [C.c_int]),
     "nf4_version": (C.c_int, []),
     "nf4_last_hip_error": (C.c_int, []),
@@ -120,6 +124,12 @@ def _ptr(t):
 # ------------------------------------------------------------------ host-only
 def nf4_table() -> np.ndarray:
     p = _lib.nf4_table()
+    return np.ctypeslib.as_array(p, shape=(16,)).copy()
+
+
+def nf4_levels(quant_type: str = "nf4") -> np.ndarray:
+    """The 16 levels of a quant type, index = 4-bit code."""
+    p = _lib.nf4_levels(QUANT_TYPES[quant_type])
     return np.ctypeslib.as_array(p, shape=(16,)).copy()
 
 
@@ -203,6 +213,7 @@ class NF4Weight:
     double_quant: bool
     dq_group: int = 256
     block_size: int = 64
+    quant_type: str = "nf4"  # or "fp4"
 
     @property
     def op_flags(self) -> int:
@@ -214,13 +225,15 @@ class NF4Weight:
             _ptr(self.codes) or None, _ptr(self.absmax) or None,
             _ptr(self.scale_codes) if self.double_quant else None,
             _ptr(self.group_absmax) if self.double_quant else None,
-            self.rows, self.cols, nf4_config(self.block_size, int(self.double_quant), self.dq_group))
+            self.rows, self.cols,
+            nf4_config(self.block_size, int(self.double_quant), self.dq_group, QUANT_TYPES[self.quant_type]))
 
 
-def nf4_quantize(W, double_quant: bool, dq_group: int = 256, block_size: int = 64, stream=None) -> NF4Weight:
+def nf4_quantize(W, double_quant: bool, dq_group: int = 256, block_size: int = 64, stream=None,
+                 quant_type: str = "nf4") -> NF4Weight:
     """Quantize a contiguous fp32 or bf16 CUDA tensor [rows, cols] in blocks of
     64 or 128 (bf16 through nf4_quantize_bf16: the same codes as its exact fp32
-    values)."""
+    values); quant_type "nf4" or "fp4"."""
     import torch
 
     rows, cols = W.shape
@@ -233,14 +246,14 @@ def nf4_quantize(W, double_quant: bool, dq_group: int = 256, block_size: int = 6
     if double_quant:
         sc = torch.empty(max(nb, 16), dtype=torch.int8, device=dev)
         gab = torch.empty(max((nb + dq_group - 1) // dq_group, 4), dtype=torch.float32, device=dev)
-    cfg = nf4_config(block_size, int(double_quant), dq_group)
+    cfg = nf4_config(block_size, int(double_quant), dq_group, QUANT_TYPES[quant_type])
     fn, name = ((_lib.nf4_quantize_bf16, "nf4_quantize_bf16") if W.dtype == torch.bfloat16
                 else (_lib.nf4_quantize, "nf4_quantize"))
     _check(fn(_ptr(W), rows, cols, C.byref(cfg), _ptr(codes), _ptr(absmax), _ptr(sc), _ptr(gab),
               _stream(stream)), name)
     return NF4Weight(codes[: n // 2], absmax[:nb], None if sc is None else sc[:nb],
                      None if gab is None else gab[: (nb + dq_group - 1) // dq_group],
-                     rows, cols, double_quant, dq_group, block_size)
+                     rows, cols, double_quant, dq_group, block_size, quant_type)
 
 
 def nf4_dequantize(w: NF4Weight, stream=None):

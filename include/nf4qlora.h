@@ -5,9 +5,10 @@
  *
  *     h = Wb x + (alpha/r) B (A x),        Wb = bf16( s~_b * NF4[code] )
  *
- * whose frozen base weight is stored as 4-bit NormalFloat codes in blocks of
- * 64 (or 128) elements, each block with an absmax scale that may itself be
- * quantized to int8 ("double quantization").  Sources, by page title and
+ * whose frozen base weight is stored as 4-bit NormalFloat codes (or FP4
+ * codes, the other quant type) in blocks of 64 (or 128) elements, each block
+ * with an absmax scale that may itself be quantized to int8 ("double
+ * quantization").  Sources, by page title and
  * section:
  *
  *  [P1] "QLoRA Finetuner", sections "1. Low-Rank Adaptation (LoRA)" (forward
@@ -47,7 +48,8 @@
  *    nf4_last_hip_error(), per thread).  No exception crosses the ABI.
  *  - Weights should be finite.  The calls are asynchronous and never
  *    synchronize, so a status cannot depend on device data: instead a block
- *    that holds Inf or NaN is quantized to scale NaN with code 7 everywhere
+ *    that holds Inf or NaN is quantized to scale NaN with the level-0 code
+ *    everywhere (7 for NF4, 0 for FP4)
  *    (with double quant its group gets constant NaN and scale codes 0), so
  *    every weight of that block (group) dequantizes to NaN and every output
  *    that reads it is NaN.  Activations and adapters are used as given.
@@ -62,26 +64,41 @@
 extern "C" {
 #endif
 
-#define NF4QLORA_VERSION 1
+#define NF4QLORA_VERSION 2
 
 enum {
     NF4_OK = 0,
     NF4_EINVAL = 1,        /* null pointer, negative size, r outside [0, 256], bad scale */
     NF4_ESHAPE = 2,        /* rows*cols not a multiple of the block; linear calls: cols % 64 != 0 */
-    NF4_EUNSUPPORTED = 3,  /* block_size not 64 or 128, dq_group < 1 */
+    NF4_EUNSUPPORTED = 3,  /* block_size not 64 or 128, dq_group < 1, unknown quant_type */
     NF4_EWORKSPACE = 4,    /* workspace pointer NULL or smaller than qlora_workspace_bytes() */
     NF4_ELAUNCH = 5,       /* a HIP launch failed; see nf4_last_hip_error() */
     NF4_ETOOLARGE = 6      /* qlora_linear_forward_noalloc: more scratch needed than it holds */
 };
 
-/* Quantization settings [P2 "Hyperparameters"].  The quant type is NF4 and
- * the compute dtype bf16; both are fixed. */
+/* Quant types [P2 "Hyperparameters": nf4 or fp4].  NF4: the 16 levels of
+ * [P3 "Common misconceptions"], code = level index.  FP4: the pages call it
+ * an IEEE-style exponent/mantissa format [P3 "Common misconceptions"]; this
+ * library reads it as the 4-bit float E2M1 (1 sign, 2 exponent bits with
+ * bias 1, 1 mantissa bit, subnormals, no Inf/NaN: the element type of the
+ * OCP Microscaling Formats specification v1.0), the code being its bit
+ * pattern and the level fl32(value / 6), so that +-absmax maps to +-1 as
+ * with NF4.  FP4 quantization keeps the sign of w' and takes the nearest of
+ * the eight magnitudes (an exact tie to the even code: on float32 inputs it
+ * can only occur between 0 and 1/12, where that is code 0); the level-0 code
+ * (all-zero and non-finite blocks) is 0 (+0). */
+enum { NF4_QUANT_NF4 = 0, NF4_QUANT_FP4 = 1 };
+
+/* Quantization settings [P2 "Hyperparameters"].  The compute dtype is bf16,
+ * fixed. */
 typedef struct nf4_config {
     int32_t block_size;    /* elements per block: 64 [P1 section 2] or 128 [P3 "The quantization
                               backbone"; P5 "Block-Wise (Chunking) Quantization"] */
     int32_t double_quant;  /* 0: fp32 block scales; 1: int8 scale codes + fp32 group constants */
     int32_t dq_group;      /* blocks per second-level group, >= 1 (256 [P5 Pillar 2]);
                               dq_group >= number of blocks gives one global constant [P3] */
+    int32_t quant_type;    /* NF4_QUANT_NF4 (default) or NF4_QUANT_FP4; other values give
+                              NF4_EUNSUPPORTED */
 } nf4_config;
 
 /* A quantized weight [rows, cols] in caller-owned device buffers.
@@ -109,6 +126,10 @@ typedef struct nf4_tensor {
 /* Host copy of the 16 NF4 levels (index = 4-bit code) [P3 "Common
  * misconceptions"; P5 "Pillar 1" table].  Never NULL. */
 const float* nf4_table(void);
+/* Host copy of the 16 levels of a quant type (index = 4-bit code): the NF4
+ * table, or for NF4_QUANT_FP4 fl32(E2M1 value / 6).  NULL for an unknown
+ * type. */
+const float* nf4_levels(int32_t quant_type);
 const char* nf4_strerror(int code);
 int nf4_version(void);
 /* The last hipError_t recorded by a failed launch on the calling thread. */
@@ -127,7 +148,9 @@ int nf4_storage_sizes(int64_t rows, int64_t cols, const nf4_config* cfg,
  * per contiguous block of block_size (64 or 128) elements of the row-major
  * flattening,
  *   s_b = max |w|, w' = fl32(w / s_b), code = nearest NF4 level to w'
- *   (an exact tie goes to the lower level; an all-zero block gets code 7).
+ *   (an exact tie goes to the lower level; an all-zero block gets code 7),
+ *   or with cfg->quant_type == NF4_QUANT_FP4 the FP4 code of w' (see the
+ *   quant types above; an all-zero block gets code 0).
  * Writes `codes` and `absmax` (always).  With double quant [P3 "Double
  * quantization"; P5 "Pillar 2"] also writes, per group of dq_group blocks,
  *   c_g = max s_b,  q_b = round_half_even(fl32(fl32(s_b / c_g) * 127))
@@ -150,7 +173,8 @@ int nf4_quantize_bf16(const uint16_t* W, int64_t rows, int64_t cols, const nf4_c
                       uint8_t* codes, float* absmax, int8_t* scale_codes, float* group_absmax,
                       void* stream);
 
-/* Dequantize to fp32 [rows, cols]: w~ = fl32(scale_b * NF4[code]) [P1
+/* Dequantize to fp32 [rows, cols]: w~ = fl32(scale_b * T[code]) with T the
+ * levels of W->cfg.quant_type (NF4 or FP4) [P1
  * section 2, last item].  Bit-exact contract. */
 int nf4_dequantize(const nf4_tensor* W, float* W_out, void* stream);
 /* Dequantize to bf16 bits [rows, cols]: round-to-nearest-even of w~ [P3 "The

@@ -131,4 +131,4 @@ def weight_from_oracle(F, qref, rows: int, cols: int, dq: bool, group: int = 256
     if dq:
         sc = torch.from_numpy(np.ascontiguousarray(qref["scale_codes"])).to(d)
         ga = torch.from_numpy(np.ascontiguousarray(qref["group_absmax"])).to(d)
-    return F.NF4Weight(codes, absmax, sc, ga, rows, cols, dq, group)
+    return F.NF4Weight(codes, absmax, sc, ga, rows, cols, dq, group, 64, qref.get("quant_type", "nf4"))

@@ -40,7 +40,7 @@ def test_headers_are_the_two_libraries():
 
 def test_every_declared_function_is_exported(F):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = C.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -76,7 +76,7 @@ def test_profile_hook_arguments(F):
 def test_version_table_and_strings(F):
     from oracle import nf4_oracle as O
 
-    assert F.nf4_version() == 1
+    assert F.nf4_version() == 2
     np.testing.assert_array_equal(F.nf4_table(), O.NF4_LEVELS)
     for code in range(7):
         assert F.nf4_strerror(code) and "unknown" not in F.nf4_strerror(code)
@@ -120,6 +120,9 @@ def test_quantize_argument_errors(F, entry):
     assert q(FAKE, 3, 64, C.byref(b128), FAKE, FAKE, FAKE, FAKE) == F.NF4_ESHAPE  # 192 elements: a partial block
     bad = _cfg(F, g=0)
     assert q(FAKE, 64, 64, C.byref(bad), FAKE, FAKE, FAKE, FAKE) == F.NF4_EUNSUPPORTED
+    for qt in (2, -1):
+        bad = F.nf4_config(64, 1, 256, qt)
+        assert q(FAKE, 64, 64, C.byref(bad), FAKE, FAKE, FAKE, FAKE) == F.NF4_EUNSUPPORTED
     assert q(FAKE, 64, 64, C.byref(cfg), FAKE, FAKE, None, FAKE) == F.NF4_EINVAL  # DQ needs its outputs
     assert q(C.c_void_p(0x100004), 64, 64, C.byref(cfg), FAKE, FAKE, FAKE, FAKE) == F.NF4_EINVAL
     assert q(None, 0, 64, C.byref(cfg), None, None, None, None) == F.NF4_OK  # empty: no-op
@@ -127,6 +130,27 @@ def test_quantize_argument_errors(F, entry):
 
 def _tensor(F, rows=128, cols=256, dq=1, bs=64, g=256, codes=FAKE):
     return F.nf4_tensor(codes, FAKE, FAKE, FAKE, rows, cols, F.nf4_config(bs, dq, g))
+
+
+def test_quant_type_of_a_tensor_is_validated(F):
+    lib = F._lib
+    for qt in (2, 7, -1):
+        t = F.nf4_tensor(FAKE, FAKE, FAKE, FAKE, 128, 256, F.nf4_config(64, 1, 256, qt))
+        assert lib.nf4_dequantize(C.byref(t), FAKE, None) == F.NF4_EUNSUPPORTED
+        assert lib.qlora_linear_forward(C.byref(t), FAKE, 1, FAKE, FAKE, 16, 1.0, FAKE, None, FAKE, 1 << 30,
+                                        None) == F.NF4_EUNSUPPORTED
+
+
+def test_level_tables(F):
+    """nf4_levels: the NF4 table (as nf4_table) and the FP4 levels, the
+    published E2M1 values (OCP Microscaling v1.0: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    and their negatives, code bit 3 the sign) divided by 6 in float32."""
+    np.testing.assert_array_equal(F.nf4_levels("nf4"), F.nf4_table())
+    fp4 = F.nf4_levels("fp4")
+    mags = np.float32([0, 0.5, 1, 1.5, 2, 3, 4, 6]) / np.float32(6)
+    want = np.concatenate([mags, -mags]).astype(np.float32)
+    np.testing.assert_array_equal(fp4.view(np.uint32), want.view(np.uint32))
+    assert F._lib.nf4_levels(2) is None or not bool(F._lib.nf4_levels(2))
 
 
 def test_layer_argument_errors(F):

@@ -120,8 +120,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (DQ) q127[tid] = q_over_127(int8_t(tid));
     char* tb = reinterpret_cast<char*>(&tbl[0][0][0]);
     char* mine = tb + (w * 16 * 64 + l) * 4;  // slot (w, 0, l); entry stride 256 B
-#pragma unroll
-    for (int e = 0; e < 16; ++e) *reinterpret_cast<uint32_t*>(mine + e * 256) = 0u;
     const uint32_t laneb = uint32_t(l) * 4u;
     const uint32_t P = uint32_t(w) * 0x10101010u;
     uint32_t nmask = 0x0F0F0F0Fu;  // in a VGPR: (c & mask) | P is one v_and_or_b32
@@ -168,19 +166,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     float lvf[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) lvf[e] = uniform_level(q.qt, e);
-    auto put = [&](int e, uint16_t v) { *reinterpret_cast<uint16_t*>(mine + e * 256 + 2) = v; };
     auto process = [&](const Fetch& f) {
         const float sc = DQ ? __fmul_rn(q127[f.qb], f.cg) : bits_f(f.qb);
         const float s = f.ok ? sc : 0.0f;
-        // every entry is s * T[e], level 0 included (NaN for the NaN scale of
-        // a non-finite block)
-        auto pair = [&](int e0, int e1) {
-            const uint32_t pk = pack_bf16x2(__fmul_rn(s, lvf[e0]), __fmul_rn(s, lvf[e1]));
-            put(e0, uint16_t(pk));
-            put(e1, uint16_t(pk >> 16));
-        };
+        // every entry is the slot {0, bf16(s * T[e])}, level 0 included (NaN
+        // for the NaN scale of a non-finite block); entries e and e+1 are
+        // 256 B apart, so the compiler pairs the stores into ds_write2st64
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) pair(e, e + 1);
+        for (int e = 0; e < 16; ++e) *reinterpret_cast<uint32_t*>(mine + e * 256) = slot_bf16(__fmul_rn(s, lvf[e]));
         const float d = f.ok ? bf16_f(uint16_t(f.dv)) : 0.0f;
         const uint32_t cw[8] = {f.c0.x, f.c0.y, f.c0.z, f.c0.w, f.c1.x, f.c1.y, f.c1.z, f.c1.w};
         // the lookups of code dword st+1 are issued before the FMAs of dword

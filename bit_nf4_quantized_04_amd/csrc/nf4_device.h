@@ -83,6 +83,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// The table slot {0, bf16(v)} (low half zero, the product in the high half,
+// so the dword read back is the fp32 value of the bf16) in one conversion:
+// v_cvt_pk_bf16_f32 with a constant 0 for the low half.
+__device__ __forceinline__ uint32_t slot_bf16(float v) {
+    uint32_t d;
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(d) : "v"(v));
+    return d;
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float a) {
     return __builtin_bit_cast(uint16_t, (__bf16)a);
 }

@@ -25,7 +25,10 @@ using namespace nf4dev;
 
 namespace {
 
-constexpr int SKW = 4;  // waves per workgroup; they split the K range of 16 rows
+// k_skinny: waves per workgroup (they split the K range of 16 rows): 4, or 8
+// when the weight has too few row tiles for two workgroups per CU
+constexpr int SKW = 4;
+constexpr int SKW_WIDE = 8;
 
 // Partial down-projections for M <= 16 tokens: part[z][i][c] = sum over the
 // z-th K chunk of x[i][k] A[c][k] (bf16 products, fp32 accumulation).  Grid:
@@ -75,35 +78,36 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
 }
 
 // Shared memory of the decode kernel.
-template <int MT>
+template <int MT, int NWV>
 struct SkinnySmem {
     // [wave][entry][lane] dword slots; the bf16 entry sits in the low half.
     // Every C++ access is 16-bit typed.  After the main loop the storage
     // holds the cross-wave reduction.
-    uint16_t tbl[SKW][16][128];
-    uint16_t xs[SKW][MT][256];  // x slice of the current block-step, per wave
+    uint16_t tbl[NWV][16][128];
+    uint16_t xs[NWV][MT][256];  // x slice of the current block-step, per wave
     float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
     float us[16 * 64];  // u for the epilogue (r <= 64 here)
 };
 
-// MT = token capacity (1, 4 or 16); the kernel handles any M <= MT.
-template <bool DQ, int MT>
-__global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __restrict__ x, int M,
+// MT = token capacity (1, 4 or 16); the kernel handles any M <= MT.  NWV:
+// waves per workgroup.
+template <bool DQ, int MT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_t* __restrict__ x, int M,
                                                 const float* __restrict__ upart, int r,
                                                 const uint16_t* __restrict__ B, float scale,
                                                 uint16_t* __restrict__ h, float* __restrict__ u_out) {
-    __shared__ __attribute__((aligned(16))) SkinnySmem<MT> sm;
+    __shared__ __attribute__((aligned(16))) SkinnySmem<MT, NWV> sm;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int j = l & 15, g = l >> 4;
     const int64_t N = q.rows, K = q.cols;
     const int nkb = int(K / 64);  // block indices fit in 32 bits (checked by the API)
     const int64_t o0 = int64_t(blockIdx.x) * 16;
-    if (DQ) sm.q127[tid] = q_over_127(int8_t(tid));
+    if (DQ && tid < 256) sm.q127[tid] = q_over_127(int8_t(tid));
     // The lookup addresses assume the table starts at LDS offset 0.
     __syncthreads();
 
     const int S = (nkb + 3) / 4;
-    const int sb = S * w / SKW, se = S * (w + 1) / SKW;
+    const int sb = S * w / NWV, se = S * (w + 1) / NWV;
     // Branch-free streaming: a lane whose row or block lies outside W reads a
     // clamped, valid block and uses scale 0 (its products vanish).
     const int64_t row = o0 + j;
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
     for (int e = 0; e < 4; ++e) red[w][4 * g + e][j] = acc[e];
     __syncthreads();
     // u = sum of the down-projection partials, in a fixed order
-    for (int idx = tid; idx < M * r; idx += 256) {
+    for (int idx = tid; idx < M * r; idx += 64 * NWV) {
         float a = 0.0f;
 #pragma unroll 4
         for (int zz = 0; zz < DOWN_SPLIT; ++zz) a += upart[int64_t(zz) * M * r + idx];
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
     __syncthreads();
     // epilogue: output (i, jj) of the tile is finished by 16 lanes that split
     // the rank-r dot product s * u[i] . B[o]
-    for (int oi = tid >> 4; oi < M * 16; oi += 16) {
+    for (int oi = tid >> 4; oi < M * 16; oi += 4 * NWV) {
         const int i = oi >> 4, jj = oi & 15, sub = tid & 15;
         const int64_t o = o0 + jj;
         float ls = 0.0f;
@@ -233,18 +237,12 @@ __global__ __launch_bounds__(256) void k_skinny(nf4::QView q, const uint16_t* __
         for (int off = 8; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 16);
         if (sub == 0 && o < N) {
             float v = (red[0][i][jj] + red[1][i][jj]) + (red[2][i][jj] + red[3][i][jj]);
+            if constexpr (NWV == 8)
+                v += (red[4][i][jj] + red[5][i][jj]) + (red[6][i][jj] + red[7][i][jj]);
             if (r > 0) v += scale * ls;
             h[int64_t(i) * N + o] = to_bf16(v);
         }
     }
-}
-
-// The table slot {0, bf16(v)} (low half zero, the product in the high half)
-// in one conversion: v_cvt_pk_bf16_f32 with a constant 0 for the low half.
-__device__ __forceinline__ uint32_t slot_bf16(float v) {
-    uint32_t d;
-    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(d) : "v"(v));
-    return d;
 }
 
 // v as held by another lane of the same quad (DPP quad_perm: 0x55 reads quad
@@ -548,9 +546,13 @@ int forward_skinny(const QView& q, const uint16_t* x, int64_t M, const uint16_t*
         return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
     }
     const dim3 grid(unsigned(cdiv(q.rows, 16)));
-#define NF4_SKINNY(DQV, MTV)                                                                       \
-    launch_dominant(k_skinny<DQV, MTV>, grid, dim3(256), 0, st, q, x, int(M), part, r, B, scale, h, \
-                    u_out)
+    // fewer row tiles than two per CU: eight waves split each tile's K range
+    const bool wide = cdiv(q.rows, 16) < 512;
+#define NF4_SKINNY(DQV, MTV)                                                                              \
+    (wide ? launch_dominant(k_skinny<DQV, MTV, SKW_WIDE>, grid, dim3(64 * SKW_WIDE), 0, st, q, x, int(M), \
+                            part, r, B, scale, h, u_out)                                                  \
+          : launch_dominant(k_skinny<DQV, MTV, SKW>, grid, dim3(64 * SKW), 0, st, q, x, int(M), part, r, B,  \
+                            scale, h, u_out))
     if (q.dq) {
         if (M <= 1) NF4_SKINNY(true, 1);
         else if (M <= 4) NF4_SKINNY(true, 4);

@@ -68,6 +68,25 @@ def test_forward_small(F, M, out, inp, r, dq):
     U.assert_close("u", u.cpu().numpy(), uref)
 
 
+@pytest.mark.parametrize("M", [2, 4, 16])
+@pytest.mark.parametrize("out", [4096, 8200])
+def test_few_token_forward_both_workgroup_shapes(F, M, out):
+    """The few-token forward kernel takes eight waves per workgroup below 512
+    row tiles (4096 rows) and four at or above (8200 rows: 513 tiles, the last
+    one ragged); both against the oracle."""
+    import torch
+
+    inp, r, s = 512, 16, 2.0
+    w, x, a, b, _ = _case(M * 13 + out, M, out, inp, r)
+    q = F.nf4_quantize(U.f32(w), double_quant=True)
+    h, u = F.qlora_linear_forward(q, U.bf(x), U.bf(a), U.bf(b), s, want_u=True)
+    torch.cuda.synchronize()
+    wb = O.compute_weight(O.quantize(w, double_quant=True), w.shape)
+    href, uref = O.forward(wb, x, a, b, s)
+    U.assert_close("h", U.bf16_to_f64(h), href)
+    U.assert_close("u", u.cpu().numpy(), uref)
+
+
 @pytest.mark.parametrize("M,out,inp,r", SMALL)
 def test_backward_small(F, M, out, inp, r):
     import torch

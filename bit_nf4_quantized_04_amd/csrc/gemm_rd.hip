@@ -1055,7 +1055,12 @@ int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* 
     FwdArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, x, nullptr, nullptr, h,
               M, q.rows, q.cols, 0, 0, su, ids, Bb, n_ad, r, part_ws, spl, 0, 1, spl, q.qt};
     const int64_t T = cdiv(M, RM) * cdiv(q.rows, RN);
-    launch_dominant(k_fwd_rd<true, 4>, dim3(unsigned(T), unsigned(Z)), dim3(256), 0, st, a);
+    // split: the plain forward kernel (eight waves) writes the fp32 partials
+    // and the gather follows; one split: the gathered epilogue in the kernel
+    if (Z > 1)
+        launch_dominant(k_fwd_rd<false, kFwdWaves>, dim3(unsigned(T), unsigned(Z)), dim3(64 * kFwdWaves), 0, st, a);
+    else
+        launch_dominant(k_fwd_rd<true, 4>, dim3(unsigned(T), 1u), dim3(256), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (Z > 1) {
         if (ms) return multi_fin_seg(*ms, part_ws, Z, M, q.rows, su, r, Bb, h, st);

@@ -794,18 +794,22 @@ int forward_multi_impl(const QView& q, const uint16_t* x, int64_t M, const uint1
     float* su = reinterpret_cast<float*>(w);
     MultiSort ms{};
     const bool sorted = use_multi_sort(M, n, r) && al16(ws);
+    const bool rd = use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0) && al16(Bb) && al16(ws);
+    float* sc_ws = reinterpret_cast<float*>(w + lay.sc);
     int rc;
     if (sorted) {  // tokens bucketed by adapter: each adapter's A read once per 16 tokens
-        if ((rc = multi_sort(ids, M, n, w + lay.sort, &ms, st))) return rc;
+        // (the sort's launch also decodes the base product's block scales)
+        if ((rc = multi_sort(ids, M, n, w + lay.sort, &ms, st, rd ? &q : nullptr, rd ? sc_ws : nullptr)))
+            return rc;
         if ((rc = multi_down_seg(ms, x, q.cols, Ab, r, scales, su, st))) return rc;
     } else {
         hipLaunchKernelGGL(k_multi_down, dim3(unsigned(M)), dim3(256), 0, st, x, q.cols, Ab, n, r,
                            scales, ids, su);
         if (hipPeekAtLastError() != hipSuccess) return launch_status();
     }
-    if (use_rd_grid(M, q.rows) && use_rd(q, M, 0, 0) && al16(Bb) && al16(ws))
-        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h, reinterpret_cast<float*>(w + lay.sc),
-                                reinterpret_cast<float*>(w + lay.part), sorted ? &ms : nullptr, st);
+    if (rd)
+        return forward_rd_multi(q, x, M, su, ids, Bb, n, r, h, sc_ws, reinterpret_cast<float*>(w + lay.part),
+                                sorted ? &ms : nullptr, st, sorted);
     LdRowMajor lx{x, M, q.cols, q.cols, al16(x)};
     return gemm(st, M, q.rows, lx, LdNF4Rows{q}, q.cols, LdNone{}, LdNone{}, 0,
                 OutMulti{h, q.rows, su, ids, Bb, n, r, q.rows}, 1, true);

@@ -1045,10 +1045,12 @@ size_t fwd_multi_part_bytes(int64_t M, int64_t rows, int64_t cols) {
 
 int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
                      const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, float* part_ws,
-                     const MultiSort* ms, hipStream_t st) {
-    const float* scales;
-    int rc = block_scales(q, scale_ws, &scales, st);
-    if (rc) return rc;
+                     const MultiSort* ms, hipStream_t st, bool scales_ready) {
+    const float* scales = scale_ws;
+    if (!(scales_ready && q.dq)) {
+        const int rc = block_scales(q, scale_ws, &scales, st);
+        if (rc) return rc;
+    }
     const int Z = fwd_multi_splits(M, q.rows, q.cols);
     const int S1 = int(q.cols / RKS);
     const int spl = int(cdiv(cdiv(S1, Z), 4) * 4);

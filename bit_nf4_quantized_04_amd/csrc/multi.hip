@@ -35,11 +35,24 @@ constexpr int SEG = 16;  // tokens per segment: one MFMA row block
 // Buckets b = id (valid) or n_ad.  off[b]: first bucket-ordered position of
 // bucket b, off[n_ad + 1] = M; seg[b]: first segment of bucket b,
 // seg[n_ad + 1] = number of segments.
+// Workgroups after the first, when the launch has them, decode the fp32
+// block scales of a double-quantized weight for the base product
+// (fl32(fl32(q_b/127) * c_g) into sc_out), which then needs no launch of
+// its own.
 __global__ __launch_bounds__(1024) void k_multi_sort(const int32_t* __restrict__ ids, int M, int n_ad,
                                                      int32_t* __restrict__ perm, int32_t* __restrict__ off,
-                                                     int32_t* __restrict__ seg) {
+                                                     int32_t* __restrict__ seg, nf4::QView q, int64_t nblk,
+                                                     float* __restrict__ sc_out) {
     __shared__ int cnt[nf4::kMultiSortMaxAdapters + 1];
     __shared__ int cur[nf4::kMultiSortMaxAdapters + 1];
+    if (blockIdx.x > 0) {  // workgroup-uniform
+        const int64_t stride = int64_t(gridDim.x - 1) * 1024;
+        for (int64_t b = int64_t(blockIdx.x - 1) * 1024 + threadIdx.x; b < nblk; b += stride) {
+            const int64_t g = q.gshift >= 0 ? (b >> q.gshift) : (b / q.group);
+            sc_out[b] = __fmul_rn(q_over_127(q.qcodes[b]), q.gabs[g]);
+        }
+        return;
+    }
     const int tid = threadIdx.x, nb = n_ad + 1;
     for (int b = tid; b < nb; b += 1024) cnt[b] = 0;
     __syncthreads();
@@ -244,13 +257,18 @@ bool use_multi_sort(int64_t M, int n_ad, int r) {
     return n_ad <= kMultiSortMaxAdapters && r <= 64 && M < (int64_t(1) << 30);
 }
 
-int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms, hipStream_t st) {
+int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms, hipStream_t st, const QView* q,
+               float* sc_out) {
     ms->perm = reinterpret_cast<int32_t*>(ws);
     ms->off = reinterpret_cast<int32_t*>(ws + align256(size_t(M) * 4));
     ms->seg = reinterpret_cast<int32_t*>(ws + align256(size_t(M) * 4) + align256(size_t(n_ad + 2) * 4));
     ms->n_ad = n_ad;
     ms->bound = int(cdiv(M, SEG)) + n_ad + 1;  // segments: at most one partial per bucket
-    hipLaunchKernelGGL(k_multi_sort, dim3(1), dim3(1024), 0, st, ids, int(M), n_ad, ms->perm, ms->off, ms->seg);
+    const bool scales = q && q->dq && sc_out;
+    const int64_t nblk = scales ? q->rows * q->cols / 64 : 0;
+    const unsigned extra = scales ? unsigned(std::min<int64_t>(cdiv(nblk, 1024), 1024)) : 0u;
+    hipLaunchKernelGGL(k_multi_sort, dim3(1 + extra), dim3(1024), 0, st, ids, int(M), n_ad, ms->perm, ms->off,
+                       ms->seg, scales ? *q : QView{}, nblk, sc_out);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

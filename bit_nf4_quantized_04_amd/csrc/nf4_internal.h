@@ -153,9 +153,10 @@ bool use_rd_grid(int64_t M, int64_t N);
 // On a small grid its reduction is split (fwd_multi_part_bytes() of
 // workspace for the fp32 partials) and the gather moves to the partial sum.
 size_t fwd_multi_part_bytes(int64_t M, int64_t rows, int64_t cols);
+// scales_ready: scale_ws already holds the decoded block scales.
 int forward_rd_multi(const QView& q, const uint16_t* x, int64_t M, const float* su, const int32_t* ids,
                      const uint16_t* Bb, int n_ad, int r, uint16_t* h, float* scale_ws, float* part_ws,
-                     const struct MultiSort* ms, hipStream_t st);
+                     const struct MultiSort* ms, hipStream_t st, bool scales_ready = false);
 // Multi-adapter tokens bucketed by adapter id (multi.hip): bucket order,
 // bucket and segment offsets (segments of up to 16 tokens of one bucket).
 constexpr int kMultiSortMaxAdapters = 4096;
@@ -168,7 +169,10 @@ struct MultiSort {
 };
 bool use_multi_sort(int64_t M, int n_ad, int r);
 size_t multi_sort_bytes(int64_t M, int n_ad);
-int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms, hipStream_t st);
+// With q (double-quantized) and sc_out, the same launch also decodes the
+// weight's fp32 block scales into sc_out.
+int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms, hipStream_t st,
+               const QView* q = nullptr, float* sc_out = nullptr);
 // su[t] = s_id x_t A_id^T for every token of a valid id (r <= 64, K % 32 == 0)
 int multi_down_seg(const MultiSort& ms, const uint16_t* x, int64_t K, const uint16_t* Ab, int r,
                    const float* scales, float* su, hipStream_t st);

@@ -624,58 +624,66 @@ struct DxCtx {
             *reinterpret_cast<uint4*>(wt + row * WTS + 8 * (ch ^ wt_swizzle(row, ch))) = v;
         }
     }
-    __device__ __forceinline__ void aread(const uint4* ht, int sl, Frag& f) const {
-        const int nl = lane & 31, hh = lane >> 5;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f.v[i] = __builtin_bit_cast(u32x4_t, ht[dpos(32 * i + nl, 2 * sl + hh)]);
+    // A fragment i of slice sl of dH tile `ht`
+    __device__ __forceinline__ u32x4_t afrag(const uint4* ht, int i, int sl) const {
+        return __builtin_bit_cast(u32x4_t, ht[dpos(32 * i + (lane & 31), 2 * sl + (lane >> 5))]);
     }
     // the step's B operand (2 slices x 2 column frags) from W tile `wt`: eight
-    // transposed 8-byte reads off one address, and a wait for all of them
+    // transposed 8-byte reads off one address (the compiler places the waits)
     __device__ __forceinline__ void bread(const uint16_t* wt, u32x4_t (&b0)[2], u32x4_t (&b1)[2]) const {
-        const uint32_t ad = uint32_t(reinterpret_cast<uintptr_t>(wt)) + tro;
-        uint2 v[8];
+        typedef short s16x4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+        char* base = const_cast<char*>(reinterpret_cast<const char*>(wt)) + tro;
+        auto rd = [&](int off) {
+            return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + off)));
+        };
         // offsets: +4 rows = 2304 B, +32 columns = 64 B, +16 rows (slice 1) = 9216 B
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\t"
-            "ds_read_b64_tr_b16 %1, %8 offset:2304\n\t"
-            "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
-            "ds_read_b64_tr_b16 %3, %8 offset:2368\n\t"
-            "ds_read_b64_tr_b16 %4, %8 offset:9216\n\t"
-            "ds_read_b64_tr_b16 %5, %8 offset:11520\n\t"
-            "ds_read_b64_tr_b16 %6, %8 offset:9280\n\t"
-            "ds_read_b64_tr_b16 %7, %8 offset:11584\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-              "=&v"(v[7])
-            : "v"(ad)
-            : "memory");
-        b0[0] = u32x4_t{v[0].x, v[0].y, v[1].x, v[1].y};
-        b0[1] = u32x4_t{v[2].x, v[2].y, v[3].x, v[3].y};
-        b1[0] = u32x4_t{v[4].x, v[4].y, v[5].x, v[5].y};
-        b1[1] = u32x4_t{v[6].x, v[6].y, v[7].x, v[7].y};
+        const uint2 v0 = rd(0), v1 = rd(2304), v2 = rd(64), v3 = rd(2368);
+        const uint2 v4 = rd(9216), v5 = rd(11520), v6 = rd(9280), v7 = rd(11584);
+        b0[0] = u32x4_t{v0.x, v0.y, v1.x, v1.y};
+        b0[1] = u32x4_t{v2.x, v2.y, v3.x, v3.y};
+        b1[0] = u32x4_t{v4.x, v4.y, v5.x, v5.y};
+        b1[1] = u32x4_t{v6.x, v6.y, v7.x, v7.y};
     }
 };
 
 // One K step t: MFMAs on ring buffer `bc` (dH tile of step t) and W tile
 // `wc`; meanwhile DMAs of step t+3 into buffer `bd`, and the dequantization
-// of step t+1 (staged in buffer `bn`) into W tile `wn`.
+// of step t+1 (staged in buffer `bn`) into W tile `wn`.  One set of A
+// fragments is live: during slice 0 each fragment, once its two MFMAs are
+// issued, is reloaded with slice 1's, so only the step's first reads wait.
 __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, const uint4* bn, uint4* bd,
-                                        const uint16_t* wc, uint16_t* wn, f32x16_t (&acc)[8][2]) {
-    Frag fa, fb;
+                                        const uint16_t* wc, uint16_t* wn, f32x16_t (&acc)[8][2], Frag& f) {
     u32x4_t ba[2], bb[2];
     c.bread(wc, ba, bb);
-    c.aread(bc, 0, fa);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = c.afrag(bc, i, 0);
     c.hdma(t + 3 < c.S ? t + 3 : c.S - 1, bd);
     c.sdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, bd);
-    c.aread(bc, 1, fb);
-    mma<2>(acc, fa, ba);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 0: each fragment's two MFMAs, then its reload with slice 1's
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.v[i], ba[j], acc[i][j]);
+        f.v[i] = c.afrag(bc, i, 1);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
     // (the scheduling barrier keeps the staging reads below the wait)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
     __builtin_amdgcn_sched_barrier(0);
+    // slice 1, with the dequantization of step t+1 between its MFMAs
     c.dequant(bn, wn);
-    interleave<16>();
-    mma<2>(acc, fb, bb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.v[i], bb[j], acc[i][j]);
     interleave<16>();
     // W tile t+1 (LDS writes) complete before the barrier; no fence: nothing
     // else must be waited for
@@ -691,11 +699,12 @@ __device__ __forceinline__ void dx_loop(const DxCtx& c, int sb, int se, uint4* _
                                         uint4* __restrict__ B1, uint4* __restrict__ B2, uint4* __restrict__ B3,
                                         uint16_t* __restrict__ W0, uint16_t* __restrict__ W1,
                                         f32x16_t (&acc)[8][2]) {
+    Frag f;
     for (int t = sb; t < se; t += 4) {
-        dx_step(c, t, B0, B1, B3, W0, W1, acc);
-        dx_step(c, t + 1, B1, B2, B0, W1, W0, acc);
-        dx_step(c, t + 2, B2, B3, B1, W0, W1, acc);
-        dx_step(c, t + 3, B3, B0, B2, W1, W0, acc);
+        dx_step(c, t, B0, B1, B3, W0, W1, acc, f);
+        dx_step(c, t + 1, B1, B2, B0, W1, W0, acc, f);
+        dx_step(c, t + 2, B2, B3, B1, W0, W1, acc, f);
+        dx_step(c, t + 3, B3, B0, B2, W1, W0, acc, f);
     }
 }
 
@@ -789,8 +798,11 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
         Frag f0, f1;
         u32x4_t b0[2], b1[2];
         c.bread(wt0, b0, b1);
-        c.aread(ht, 0, f0);
-        c.aread(ht, 1, f1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f0.v[i] = c.afrag(ht, i, 0);
+            f1.v[i] = c.afrag(ht, i, 1);
+        }
         mma<2>(acc, f0, b0);
         mma<2>(acc, f1, b1);
         __syncthreads();

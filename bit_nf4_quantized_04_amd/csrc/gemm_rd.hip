@@ -28,9 +28,13 @@
 // s*u (2r columns, zero padded to a multiple of 64) against [B | B], so h is
 // written once and u keeps fp32 precision.
 //
-// Every global read of the K loop is an LDS DMA (global_load_lds), so that
-// all outstanding loads are of one kind and a wait count can name exactly the
-// ones a step needs: the x tile of step t+3 goes into a ring of four shared
+// Every global read of the K loop is an LDS DMA (a buffer load with the LDS
+// bit, on a raw buffer resource per operand), so that all outstanding loads
+// are of one kind and a wait count can name exactly the ones a step needs
+// (the MUBUF form, not the global one: while a global-segment LDS DMA is in
+// flight the compiler treats the LDS wait counter as unordered and waits for
+// every outstanding LDS read at each use, so a fragment read issued long
+// before its MFMA would still wait for the reads issued after it): the x tile of step t+3 goes into a ring of four shared
 // tiles, and each lane's own code half-blocks and fp32 block scales of step
 // t+2 into a ring of two per-wave slots.  The block scales are made by a
 // small pass before the GEMM (fl32(fl32(q/127) * c_g) per block, the same
@@ -115,7 +119,23 @@ __device__ __forceinline__ float multi_term(const FwdArgs& a, int id, int64_t m,
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (the launchers keep every
+// operand of these kernels under 4 GiB; word 3 selects 32-bit data).
+__device__ __forceinline__ rsrc_t rsrc_of(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(uint32_t(bytes)), 0x00020000);
+}
+// LDS DMA of SZ bytes per lane from byte voff + soff of buffer r; lane l's
+// bytes land at dst + SZ l
+template <int SZ>
+__device__ __forceinline__ void dma(rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
+    static_assert(SZ == 16 || SZ == 4, "16- or 4-byte lanes");
+    if constexpr (SZ == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 4, voff, soff, 0, 0);
+}
 
 constexpr int XBUF = RM * 8;  // one x tile: 256 rows x 8 chunks of 16 bytes
 
@@ -152,30 +172,24 @@ struct FwdCtx {
     uint32_t soff[J];             // byte offset of row j's block scale, step 0
     DecK dk;
     Levels lv;                    // the levels of the codes' quant type
+    rsrc_t rx, re, rc, rs;        // buffers: x, the extension, codes, block scales
 
     // x tile of step s into LDS tile `dst`: DMA instruction i of wave w fills
     // chunk positions 64(XD w + i) .. +63 (one 16-byte chunk per lane).
     __device__ __forceinline__ void xdma(int s, uint4* dst) const {
         const bool main = s < S1;
-        const char* base = main ? reinterpret_cast<const char*>(a.x) + int64_t(s) * (RKS * 2)
-                                : reinterpret_cast<const char*>(a.ext) + int64_t(s - S1) * (RKS * 2);
+        const rsrc_t r = main ? rx : re;
+        const uint32_t so = uint32_t(main ? s : s - S1) * (RKS * 2);
 #pragma unroll
-        for (int i = 0; i < XD; ++i)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + (main ? xoff[i] : eoff[i])),
-                                             (lds_void_t*)(dst + 64 * (XD * w + i)), 16, 0, 0);
+        for (int i = 0; i < XD; ++i) dma<16>(r, main ? xoff[i] : eoff[i], so, dst + 64 * (XD * w + i));
     }
     // this lane's codes and block scales of step s into its wave's slot
     __device__ __forceinline__ void wdma(int s, char* slot) const {
         char* mine = slot + w * WSLOT;
-        const char* cb = reinterpret_cast<const char*>(a.codes) + int64_t(s) * 32;
-        const char* sb = reinterpret_cast<const char*>(a.scales) + int64_t(s) * 4;
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(cb + coff[j]), (lds_void_t*)(mine + j * 1024), 16, 0, 0);
+        for (int j = 0; j < J; ++j) dma<16>(rc, coff[j], uint32_t(s) * 32, mine + j * 1024);
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(sb + soff[j]), (lds_void_t*)(mine + J * 1024 + j * 256), 4,
-                                             0, 0);
+        for (int j = 0; j < J; ++j) dma<4>(rs, soff[j], uint32_t(s) * 4, mine + J * 1024 + j * 256);
     }
     __device__ __forceinline__ void wread(const char* slot, uint4 (&cw)[J], float (&sc)[J]) const {
         const char* mine = slot + w * WSLOT;
@@ -358,6 +372,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_rd(FwdArgs a) {
     c.lane = lane;
     c.dk.init();
     c.lv.init(a.qt);
+    c.rx = rsrc_of(a.x, M * K * 2);
+    c.re = rsrc_of(a.ext, M * a.KL * 2);
+    c.rc = rsrc_of(a.codes, N * K / 2);
+    c.rs = rsrc_of(a.scales, N * (K / 64) * 4);
     int64_t wrow[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -574,24 +592,19 @@ struct DxCtx {
     uint32_t tro;               // byte offset of this lane's first transposed read in a W tile
     DecK dk;
     Levels lv;                  // the levels of the codes' quant type
+    rsrc_t rh, re, rc, rs;      // buffers: dH, the extension, codes, block scales
 
     __device__ __forceinline__ void hdma(int s, uint4* dst) const {
         const bool main = s < S1;
-        const char* base = main ? reinterpret_cast<const char*>(a.dh) + int64_t(s) * (DK * 2)
-                                : reinterpret_cast<const char*>(a.ext) + int64_t(s - S1) * (DK * 2);
+        const rsrc_t r = main ? rh : re;
+        const uint32_t so = uint32_t(main ? s : s - S1) * (DK * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + (main ? hoff[i] : eoff[i])),
-                                             (lds_void_t*)(dst + 64 * (4 * w + i)), 16, 0, 0);
+        for (int i = 0; i < 4; ++i) dma<16>(r, main ? hoff[i] : eoff[i], so, dst + 64 * (4 * w + i));
     }
     __device__ __forceinline__ void sdma(int s, uint4* buf) const {
         char* mine = reinterpret_cast<char*>(buf + DHBUF) + w * DSLOT;
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const char*>(a.codes) + coff +
-                                                       int64_t(s) * DK * (a.in / 2)),
-                                         (lds_void_t*)(mine), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const char*>(a.scales) + soff +
-                                                       int64_t(s) * DK * (a.in / 64) * 4),
-                                         (lds_void_t*)(mine + 1024), 4, 0, 0);
+        dma<16>(rc, coff, uint32_t(s) * uint32_t(DK * (a.in / 2)), mine);
+        dma<4>(rs, soff, uint32_t(s) * uint32_t(DK * (a.in / 64) * 4), mine + 1024);
     }
     // this thread's 32 weights (staged in `slot`) into W tile `wt`
     __device__ __forceinline__ void dequant(const uint4* buf, uint16_t* wt) const {
@@ -739,6 +752,10 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     c.tid = tid;
     c.dk.init();
     c.lv.init(a.qt);
+    c.rh = rsrc_of(a.dh, M * a.out * 2);
+    c.re = rsrc_of(a.ext, M * a.KL * 2);
+    c.rc = rsrc_of(a.codes, a.out * N / 2);
+    c.rs = rsrc_of(a.scales, a.out * (N / 64) * 4);
     {
         const int unit = tid >> 1, half = tid & 1;
         const int64_t row = unit >> 2, q = unit & 3;

@@ -662,9 +662,12 @@ struct DxCtx {
 
 // One K step t: MFMAs on ring buffer `bc` (dH tile of step t) and W tile
 // `wc`; meanwhile DMAs of step t+3 into buffer `bd`, and the dequantization
-// of step t+1 (staged in buffer `bn`) into W tile `wn`.  One set of A
-// fragments is live: during slice 0 each fragment, once its two MFMAs are
-// issued, is reloaded with slice 1's, so only the step's first reads wait.
+// of step t+1 (staged in buffer `bn`) into W tile `wn`.  The
+// step first waits for its own DMAs of step t+1 (issued two steps earlier),
+// so the dequantization can run between all 32 MFMAs: eight VALU operations
+// after each MFMA pair, the staged codes read first and the four W-tile
+// stores in the second half.  One set of A fragments is live: during slice 0
+// each fragment, once its two MFMAs are issued, is reloaded with slice 1's.
 __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, const uint4* bn, uint4* bd,
                                         const uint16_t* wc, uint16_t* wn, f32x16_t (&acc)[8][2], Frag& f) {
     u32x4_t ba[2], bb[2];
@@ -673,8 +676,10 @@ __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, 
     for (int i = 0; i < 8; ++i) f.v[i] = c.afrag(bc, i, 0);
     c.hdma(t + 3 < c.S ? t + 3 : c.S - 1, bd);
     c.sdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, bd);
+    // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
     __builtin_amdgcn_sched_barrier(0);
-    // slice 0: each fragment's two MFMAs, then its reload with slice 1's
+    c.dequant(bn, wn);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -682,22 +687,22 @@ __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, 
         f.v[i] = c.afrag(bc, i, 1);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
-    // (the scheduling barrier keeps the staging reads below the wait)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
-    __builtin_amdgcn_sched_barrier(0);
-    // slice 1, with the dequantization of step t+1 between its MFMAs
-    c.dequant(bn, wn);
-#pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.v[i], bb[j], acc[i][j]);
-    interleave<16>();
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read: the staged codes and scale
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    }
     // W tile t+1 (LDS writes) complete before the barrier; no fence: nothing
     // else must be waited for
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP) & ~0xf00u);

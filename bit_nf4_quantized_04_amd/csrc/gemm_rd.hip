@@ -191,13 +191,15 @@ struct FwdCtx {
 #pragma unroll
         for (int j = 0; j < J; ++j) dma<4>(rs, soff[j], uint32_t(s) * 4, mine + J * 1024 + j * 256);
     }
+    // (a lane whose weight row is past N holds row N-1's codes and scale: its
+    // accumulator column is never stored)
     __device__ __forceinline__ void wread(const char* slot, uint4 (&cw)[J], float (&sc)[J]) const {
         const char* mine = slot + w * WSLOT;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             cw[j] = *reinterpret_cast<const uint4*>(mine + j * 1024 + lane * 16);
             const float v = *reinterpret_cast<const float*>(mine + J * 1024 + j * 256 + lane * 4);
-            sc[j] = wok[j] ? v : 0.0f;
+            sc[j] = v;
         }
     }
     // A fragments of slice sl: rows 32i + nl, logical chunk 4hh + sl
@@ -296,11 +298,12 @@ __device__ __forceinline__ void nf4_step(const FwdCtx<NW>& c, int t, const uint4
     c.wread(wn, cwn, sc);
     c.wdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, wn);
     c.lookups(pl, cw, 2, ba);
-    pln[0] = make_planes(sc[0], c.lv);
     slice_mma<NW, J>(c, acc, f, bb, cur, 2);
-    // slice 2: slice 3's B operand
+    // slice 2: slice 3's B operand, the planes of step t+1 (their scales read
+    // a slice earlier)
     c.lookups(pl, cw, 3, bb);
-    if constexpr (J > 1) pln[J - 1] = make_planes(sc[J - 1], c.lv);
+#pragma unroll
+    for (int j = 0; j < J; ++j) pln[j] = make_planes(sc[j], c.lv);
     slice_mma<NW, J>(c, acc, f, ba, cur, 3);
     // slice 3: every wave's share of x tile t+1 is in (its fragments are read
     // during this slice); step t+1's first B operand

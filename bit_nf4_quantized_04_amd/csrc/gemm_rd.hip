@@ -7,10 +7,11 @@
 // bf16 cast of "The LoRA adapter path").
 //
 // Tiles of 256 tokens x 256 weight rows, K in steps of 64 (one NF4 block per
-// weight row).  Four waves, one per SIMD; wave w owns the 256 x 64 slab of
-// weight rows [64w, 64w + 64) and keeps its 256 x 64 fp32 accumulator in
-// AGPRs.  v_mfma_f32_32x32x16_bf16: the tokens are the A rows (x tile staged
-// in LDS, shared by the four waves) and the weight rows the B columns.
+// weight row).  NW waves (eight, two per SIMD, for the single-adapter
+// product; four for the gathered multi-adapter epilogue); wave w owns the
+// 256 x (256/NW) slab of weight rows [w 256/NW, (w+1) 256/NW) and its fp32
+// accumulator.  v_mfma_f32_32x32x16_bf16: the tokens are the A rows (x tile
+// staged in LDS, shared by the waves) and the weight rows the B columns.
 //
 // The B operand never touches LDS.  In the 32x32x16 layout lane (n, hh)
 // (n = lane % 32, hh = lane / 32) supplies 8 k values of column n; here the
@@ -533,8 +534,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_rd(FwdArgs a) {
 // dX = dH Wb + [dU_hi | dU_lo] [A; A]  (the backward of the same layer; the
 // dequantized weight is a constant there, "QLoRA explained", "The LoRA
 // adapter path").  Tiles of 256 tokens x 256 input features, K = out in
-// steps of 32 weight rows.  Four waves, wave w owns the 256 x 64 slab of
-// columns [64w, 64w + 64) with its accumulator in AGPRs.
+// steps of 32 weight rows.  Eight waves, two per SIMD: waves w and w + 4 own
+// the 128 x 64 slabs of columns [64w, 64w + 64), rows [0, 128) and
+// [128, 256); waves 0-3 also issue the DMAs and dequantize (the same work
+// per thread as with four waves), waves 4-7 only multiply, so that one
+// wave's dequantization overlaps the other's MFMAs on the same SIMD.  (The
+// four-wave form, one 256 x 64 slab per wave with its accumulator in AGPRs,
+// remains as a build option.)
 //
 // Here the reduction runs across weight rows, so the weight is dequantized
 // in its natural layout: thread t makes 32 consecutive columns (half an NF4
@@ -546,8 +552,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd_rd(FwdArgs a) {
 // operand) and each thread's own codes and block scale come by DMA into a
 // ring of four LDS buffers (one per step: the dH tile, then the staging), so
 // the K loop issues no other global load and its wait counts name exactly
-// the DMAs a step needs.  The transposed reads of a step are one asm block
-// that waits for its own results.
+// the DMAs a step needs.
 constexpr int DK = 32;                   // weight rows per K step
 constexpr int DHBUF = RM * 4;            // dH tile: 256 rows x 4 chunks of 16 bytes
 constexpr int WTS = 256 + 32;            // W tile row stride (elements), 576 bytes
@@ -593,6 +598,7 @@ struct DxCtx {
     uint32_t coff;              // byte offset of this thread's code half-block, step 0
     uint32_t soff;              // byte offset of its block scale, step 0
     uint32_t tro;               // byte offset of this lane's first transposed read in a W tile
+    int arow0;                  // first dH-tile row of this wave's accumulator slab
     DecK dk;
     Levels lv;                  // the levels of the codes' quant type
     rsrc_t rh, re, rc, rs;      // buffers: dH, the extension, codes, block scales
@@ -642,7 +648,7 @@ struct DxCtx {
     }
     // A fragment i of slice sl of dH tile `ht`
     __device__ __forceinline__ u32x4_t afrag(const uint4* ht, int i, int sl) const {
-        return __builtin_bit_cast(u32x4_t, ht[dpos(32 * i + (lane & 31), 2 * sl + (lane >> 5))]);
+        return __builtin_bit_cast(u32x4_t, ht[dpos(arow0 + 32 * i + (lane & 31), 2 * sl + (lane >> 5))]);
     }
     // the step's B operand (2 slices x 2 column frags) from W tile `wt`: eight
     // transposed 8-byte reads off one address (the compiler places the waits)
@@ -663,52 +669,66 @@ struct DxCtx {
     }
 };
 
-// One K step t: MFMAs on ring buffer `bc` (dH tile of step t) and W tile
-// `wc`; meanwhile DMAs of step t+3 into buffer `bd`, and the dequantization
-// of step t+1 (staged in buffer `bn`) into W tile `wn`.  The
-// step first waits for its own DMAs of step t+1 (issued two steps earlier),
-// so the dequantization can run between all 32 MFMAs: eight VALU operations
-// after each MFMA pair, the staged codes read first and the four W-tile
-// stores in the second half.  One set of A fragments is live: during slice 0
-// each fragment, once its two MFMAs are issued, is reloaded with slice 1's.
+// One K step t of a wave with FI 32-row blocks: MFMAs on ring buffer `bc`
+// (dH tile of step t) and W tile `wc`.  A producing wave (PROD) also issues
+// the DMAs of step t+3 into buffer `bd` and dequantizes step t+1 (staged in
+// buffer `bn`) into W tile `wn`: it first waits for its own DMAs of step t+1
+// (issued two steps earlier), so the dequantization can run between all of
+// the step's MFMAs (64/FI VALU operations after each MFMA pair, the staged
+// codes read first and the four W-tile stores in the second half).  One set
+// of A fragments is live: during slice 0 each fragment, once its two MFMAs
+// are issued, is reloaded with slice 1's.
+template <int FI, bool PROD>
 __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, const uint4* bn, uint4* bd,
-                                        const uint16_t* wc, uint16_t* wn, f32x16_t (&acc)[8][2], Frag& f) {
+                                        const uint16_t* wc, uint16_t* wn, f32x16_t (&acc)[FI][2], Frag& f) {
     u32x4_t ba[2], bb[2];
     c.bread(wc, ba, bb);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.v[i] = c.afrag(bc, i, 0);
-    c.hdma(t + 3 < c.S ? t + 3 : c.S - 1, bd);
-    c.sdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, bd);
-    // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
+    for (int i = 0; i < FI; ++i) f.v[i] = c.afrag(bc, i, 0);
+    if constexpr (PROD) {
+        c.hdma(t + 3 < c.S ? t + 3 : c.S - 1, bd);
+        c.sdma(t + 3 < c.S1 ? t + 3 : c.S1 - 1, bd);
+        // step t+1's DMAs (dH tile and staging) are complete: issued two steps ago
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));
+    }
     __builtin_amdgcn_sched_barrier(0);
-    c.dequant(bn, wn);
+    if constexpr (PROD) c.dequant(bn, wn);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FI; ++i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.v[i], ba[j], acc[i][j]);
         f.v[i] = c.afrag(bc, i, 1);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.v[i], bb[j], acc[i][j]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read: the staged codes and scale
+    if constexpr (PROD) {
+        constexpr int NV = 64 / FI;  // VALU operations after each MFMA pair
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read: the staged codes and scale
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-    }
+        for (int k = 0; k < FI; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+        }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        for (int k = 0; k < FI; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+        }
+        // W tile t+1 (LDS writes) complete before the barrier; no fence:
+        // nothing else must be waited for
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP) & ~0xf00u);
+    } else {
+#pragma unroll
+        for (int k = 0; k < FI; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     }
-    // W tile t+1 (LDS writes) complete before the barrier; no fence: nothing
-    // else must be waited for
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP) & ~0xf00u);
     __builtin_amdgcn_s_barrier();
 }
 
@@ -716,20 +736,24 @@ __device__ __forceinline__ void dx_step(const DxCtx& c, int t, const uint4* bc, 
 // ring indices are static (the launcher guarantees a multiple of four
 // steps).  The buffers are separate arrays so that the compiler can see that
 // a DMA into one never overlaps reads of another.
+template <int FI, bool PROD>
 __device__ __forceinline__ void dx_loop(const DxCtx& c, int sb, int se, uint4* __restrict__ B0,
                                         uint4* __restrict__ B1, uint4* __restrict__ B2, uint4* __restrict__ B3,
                                         uint16_t* __restrict__ W0, uint16_t* __restrict__ W1,
-                                        f32x16_t (&acc)[8][2]) {
+                                        f32x16_t (&acc)[FI][2]) {
     Frag f;
     for (int t = sb; t < se; t += 4) {
-        dx_step(c, t, B0, B1, B3, W0, W1, acc, f);
-        dx_step(c, t + 1, B1, B2, B0, W1, W0, acc, f);
-        dx_step(c, t + 2, B2, B3, B1, W0, W1, acc, f);
-        dx_step(c, t + 3, B3, B0, B2, W1, W0, acc, f);
+        dx_step<FI, PROD>(c, t, B0, B1, B3, W0, W1, acc, f);
+        dx_step<FI, PROD>(c, t + 1, B1, B2, B0, W1, W0, acc, f);
+        dx_step<FI, PROD>(c, t + 2, B2, B3, B1, W0, W1, acc, f);
+        dx_step<FI, PROD>(c, t + 3, B3, B0, B2, W1, W0, acc, f);
     }
 }
 
-__global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
+template <int DW>
+__global__ __launch_bounds__(64 * DW, 1) void k_dx_rd(DxArgs a) {
+    static_assert(DW == 4 || DW == 8, "four or eight waves");
+    constexpr int FI = DW == 8 ? 4 : 8;  // 32-row blocks of the wave's accumulator slab
     __shared__ __attribute__((aligned(16))) uint4 h0[DXBUF], h1[DXBUF], h2[DXBUF], h3[DXBUF];
     __shared__ __attribute__((aligned(16))) uint16_t wt0[WTBUF], wt1[WTBUF];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -758,6 +782,11 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     c.w = w;
     c.lane = lane;
     c.tid = tid;
+    // slab of wave w: all 256 rows x 64 columns (four waves), or 128 rows x 64
+    // columns (eight waves: waves w and w + 4 share the columns)
+    const int cg = DW == 8 ? (w & 3) : w;
+    c.arow0 = DW == 8 ? 128 * (w >> 2) : 0;
+    const bool prod = w < 4;  // the waves that issue the DMAs and dequantize
     c.dk.init();
     c.lv.init(a.qt);
     c.rh = rsrc_of(a.dh, M * a.out * 2);
@@ -770,7 +799,7 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
         c.coff = uint32_t(row * (N / 2) + (i0 + 64 * q) / 2 + 16 * half);
         c.soff = uint32_t((row * (N / 64) + i0 / 64 + q) * 4);
         const int qq = lane >> 4, i = lane & 15;
-        const int col = 64 * w + 16 * (qq & 1) + 4 * (i & 3);
+        const int col = 64 * cg + 16 * (qq & 1) + 4 * (i & 3);
         const int rw = 8 * (qq >> 1) + (i >> 2);
         const int cc = col >> 3;
         c.tro = uint32_t((rw * WTS + 8 * (cc ^ wt_swizzle(rw, cc)) + (col & 7)) * 2);
@@ -786,9 +815,9 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
         c.eoff[i] = uint32_t((row * a.KL + 8 * ch) * 2);
     }
 
-    f32x16_t acc[8][2];
+    f32x16_t acc[FI][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -796,17 +825,22 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
 
     const int S1 = c.S1, S = c.S;
     // ---- prologue: steps sb, sb+1, sb+2 (dH tile, then staging) in flight
-    c.hdma(sb, h0);
-    c.sdma(sb, h0);
-    c.hdma(sb + 1 < S ? sb + 1 : S - 1, h1);
-    c.sdma(sb + 1 < S1 ? sb + 1 : S1 - 1, h1);
-    c.hdma(sb + 2 < S ? sb + 2 : S - 1, h2);
-    c.sdma(sb + 2 < S1 ? sb + 2 : S1 - 1, h2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));  // step sb
-    c.dequant(h0, wt0);
+    if (prod) {
+        c.hdma(sb, h0);
+        c.sdma(sb, h0);
+        c.hdma(sb + 1 < S ? sb + 1 : S - 1, h1);
+        c.sdma(sb + 1 < S1 ? sb + 1 : S1 - 1, h1);
+        c.hdma(sb + 2 < S ? sb + 2 : S - 1, h2);
+        c.sdma(sb + 2 < S1 ? sb + 2 : S1 - 1, h2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DX_VM_STEP));  // step sb
+        c.dequant(h0, wt0);
+    }
     __syncthreads();
 
-    dx_loop(c, sb, se, h0, h1, h2, h3, wt0, wt1, acc);
+    if (prod)
+        dx_loop<FI, true>(c, sb, se, h0, h1, h2, h3, wt0, wt1, acc);
+    else
+        dx_loop<FI, false>(c, sb, se, h0, h1, h2, h3, wt0, wt1, acc);
     // the loop's last steps prefetched past the split: let those DMAs land
     // before the workgroup can end
     __builtin_amdgcn_s_waitcnt(0);
@@ -816,20 +850,25 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     for (int s = S1; s < (last ? S : S1); ++s) {
         const int k = s & 3;
         uint4* ht = k == 0 ? h0 : k == 1 ? h1 : k == 2 ? h2 : h3;
-        if (s + 3 < S) c.hdma(s + 3, k == 0 ? h3 : k == 1 ? h0 : k == 2 ? h1 : h2);
-        c.afill(s, i0, wt0);
+        if (s + 3 < S && prod) c.hdma(s + 3, k == 0 ? h3 : k == 1 ? h0 : k == 2 ? h1 : h2);
+        if (prod) c.afill(s, i0, wt0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         Frag f0, f1;
         u32x4_t b0[2], b1[2];
         c.bread(wt0, b0, b1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < FI; ++i) {
             f0.v[i] = c.afrag(ht, i, 0);
             f1.v[i] = c.afrag(ht, i, 1);
         }
-        mma<2>(acc, f0, b0);
-        mma<2>(acc, f1, b1);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                acc[i][j] = mfma32(f0.v[i], b0[j], acc[i][j]);
+                acc[i][j] = mfma32(f1.v[i], b1[j], acc[i][j]);
+            }
         __syncthreads();
     }
 
@@ -838,13 +877,13 @@ __global__ __launch_bounds__(RT, 1) void k_dx_rd(DxArgs a) {
     const bool split = gridDim.y > 1 || a.f32;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int64_t n = i0 + 64 * w + 32 * j + (lane & 31);
+        const int64_t n = i0 + 64 * cg + 32 * j + (lane & 31);
         if (n >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t m = m0 + c.arow0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (m < M) {
                     if (split)
                         pz[m * N + n] = acc[i][j][v];
@@ -974,6 +1013,15 @@ size_t dx_rd_part_bytes(int64_t M, int64_t rows, int64_t cols) {
     return Z > 1 ? align256(size_t(Z) * size_t(M) * size_t(cols) * 4) : 0;
 }
 
+// Waves of the dX kernel: four (one per SIMD, each with a 256 x 64 slab,
+// every wave dequantizing), or eight (two per SIMD: waves 0-3 issue the DMAs
+// and dequantize, waves 4-7 only multiply; 128 x 64 slabs), so that one
+// wave's dequantization overlaps the other's MFMAs.
+#ifndef NF4_DX_WAVES
+#define NF4_DX_WAVES 8
+#endif
+constexpr int kDxWaves = NF4_DX_WAVES;
+
 int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, int KL, const uint16_t* A,
           int r, uint16_t* dX, float* scale_ws, float* part_ws, hipStream_t st, bool f32) {
     const float* scales;
@@ -985,7 +1033,7 @@ int dx_rd(const QView& q, const uint16_t* dH, int64_t M, const uint16_t* duext, 
     DxArgs a{reinterpret_cast<const uint8_t*>(q.codes), scales, dH, r > 0 ? duext : nullptr, A, dX, part_ws,
              M, q.rows, q.cols, KL, r, spl, f32 ? 1 : 0, q.qt};
     const int64_t T = cdiv(M, RM) * cdiv(q.cols, RN);
-    launch_dominant(k_dx_rd, dim3(unsigned(T), unsigned(Z)), dim3(RT), 0, st, a);
+    launch_dominant(k_dx_rd<kDxWaves>, dim3(unsigned(T), unsigned(Z)), dim3(64 * kDxWaves), 0, st, a);
     if (hipPeekAtLastError() != hipSuccess) return launch_status();
     if (Z > 1 && !f32) {
         const int64_t n = M * q.cols;  // a multiple of 256

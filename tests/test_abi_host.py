@@ -328,3 +328,26 @@ def test_level_table_from_many_threads(F):
     assert not errs and len(seen) == 1600
     for v in seen:
         np.testing.assert_array_equal(v, O.NF4_LEVELS)
+
+
+@pytest.mark.parametrize("src,defines", [
+    ("gemm_rd.hip", ["-DNF4_FWD_WAVES=4", "-DNF4_DX_WAVES=4"]),  # the four-wave GEMM forms
+    ("skinny.hip", ["-DNF4_GEMV_NV=2"]),  # decode lookups partly from register byte planes
+])
+def test_build_options_compile(tmp_path, src, defines):
+    """The kernels' build options other than the defaults still compile for
+    gfx950 (device code only, at -O1 to keep this check short: the templates
+    are instantiated and their static checks run; the default forms are what
+    build() links)."""
+    from bit_nf4_quantized_04_amd import build as B
+
+    if not os.path.exists(B.HIPCC):
+        pytest.skip("no hipcc")
+    import subprocess
+
+    flags = ["-O1" if f == "-O3" else f for f in B.FLAGS]
+    cmd = [B.HIPCC, *flags, "--cuda-device-only", *defines, "-c", os.path.join(B.CSRC, src),
+           "-o", str(tmp_path / "k.o")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    assert not [l for l in res.stderr.splitlines() if "error" in l]

@@ -42,35 +42,29 @@ __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, f
 
 // ------------------------------------------------------------------ k_nt
 // part[z][m][j] = sum over k in chunk z of P[m][k] * Q[j][k]; P [M][K],
-// Q [J][K] bf16, J <= 16 * NJ, K % 16 == 0, chunks of NT_SLAB multiples.
-// A workgroup owns 32 rows and one chunk, walked in slabs of 512 k; wave w
-// takes the 128 k at 128 w of each slab, so a workgroup streams 1 KB of
-// every row per slab.  Each wave stages its 32 x 128 piece of P in its own
-// LDS tile, loading four rows of 256 contiguous bytes per instruction
-// (16-byte chunk c of row i stored at chunk c ^ (i % 16), so that both the
-// stores and the fragment reads are free of bank conflicts).
+// Q [J][K] bf16, J <= 16 * NJ, K % 16 == 0, chunks of whole 128-k pieces.
+// A workgroup owns 128 rows (wave w: rows 32 w .. 32 w + 31) and one chunk,
+// walked in pieces of 128 k that all four waves take together: each wave
+// stages its 32 x 128 piece of P in its own LDS tile (four rows of 256
+// contiguous bytes per load instruction), and the workgroup stages the
+// J x 128 piece of Q once, in a tile all four waves read their MFMA B
+// fragments from, so Q crosses the L2 once per 128 rows of P.  16-byte chunk
+// c of tile row i is stored at chunk c ^ (i % 16): the stores and the
+// fragment reads are free of bank conflicts.  The next piece's loads are
+// issued before the current piece's MFMAs (two pieces in flight per lane).
 // v_mfma_f32_16x16x32_bf16: lane (i, g) = (lane % 16, lane / 16) holds k
-// 8g .. 8g + 7 of a 32-k slice of row (or Q row) i; the Q fragments, which
-// every workgroup rereads from L2, load straight from global memory.  The
-// four waves' sums meet in LDS at the end, and only one fp32 partial per
-// workgroup goes to memory: short rows of tokens with long chunks keep the
-// partials small next to the streamed operand.  Every workgroup reads its chunk of Q; when the splits are a
-// multiple of 8 the workgroups that share an XCD (consecutive ids go round
-// the eight XCDs) share chunks, so each XCD's L2 holds an eighth of Q while
-// P streams past.
-constexpr int NT_ROWS = 32, NT_SLAB = 512;
+// 8g .. 8g + 7 of a 32-k slice of row (or Q row) i.  Each wave writes the
+// fp32 partial of its own rows.  When the splits are a multiple of 8 the
+// workgroups that share an XCD (consecutive ids go round the eight XCDs)
+// share chunks, so each XCD's L2 holds an eighth of Q while P streams past.
+constexpr int NT_ROWS = 128, NT_PIECE = 128;
 
 template <int NJ>
 __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int64_t M, int64_t K,
                                             const uint16_t* __restrict__ Q, int J, int64_t kchunk, int Z,
                                             float* __restrict__ part) {
-    constexpr int RS = 16 * NJ + 4;  // LDS row stride (floats): the four row groups of a fragment 16 banks apart
-    // the per-wave P tiles (32 rows x 128 k each) and, after the K loop, the
-    // four waves' sums share one buffer
-    constexpr int RED_F = 4 * NT_ROWS * RS, PT_F = 4 * NT_ROWS * 16 * 4;
-    __shared__ __attribute__((aligned(16))) float lbuf[RED_F > PT_F ? RED_F : PT_F];
-    uint4(*pt)[NT_ROWS][16] = reinterpret_cast<uint4(*)[NT_ROWS][16]>(lbuf);
-    float(*red)[NT_ROWS][RS] = reinterpret_cast<float(*)[NT_ROWS][RS]>(lbuf);
+    __shared__ __attribute__((aligned(16))) uint4 pt[4][32][16];   // per-wave P tiles
+    __shared__ __attribute__((aligned(16))) uint4 qt[16 * NJ][16];  // the shared Q tile
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const int64_t lin = blockIdx.x;
@@ -84,10 +78,10 @@ __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int6
         z = int(lin % Z);
         tile = lin / Z;
     }
-    const int64_t m0 = tile * NT_ROWS;
+    const int64_t m0 = tile * NT_ROWS + 32 * w;  // the wave's first row
     const int64_t k0 = int64_t(z) * kchunk, k1 = std::min<int64_t>(K, k0 + kchunk);
-    // staging loads: instruction t, lane l -> row 4t + l/16, 16-byte chunk l
-    // % 16 (rows past M read row M - 1; their sums are dropped)
+    // P loads: instruction t, lane l -> row 4t + l/16 of the wave's 32,
+    // 16-byte chunk l % 16 (rows past M read row M - 1; they are not stored)
     const uint16_t* pr = P + 8 * li;
     int64_t roff[8];
 #pragma unroll
@@ -95,67 +89,78 @@ __global__ __launch_bounds__(256) void k_nt(const uint16_t* __restrict__ P, int6
         const int64_t m = m0 + 4 * t + (lane >> 4);
         roff[t] = (m < M ? m : M - 1) * K;
     }
-    const uint16_t* qr[NJ];
+    // Q loads: instruction u, thread t -> Q row (t + 256 u) / 16, chunk t % 16
+    // (rows past J repeat row J - 1; their columns are not stored)
+    constexpr int QU = NJ;  // 16 NJ rows x 16 chunks / 256 threads
+    const uint16_t* qsrc[QU];
 #pragma unroll
-    for (int jb = 0; jb < NJ; ++jb) {
-        const int j = 16 * jb + li;
-        qr[jb] = Q + int64_t(j < J ? j : J - 1) * K + 8 * g;
+    for (int u = 0; u < QU; ++u) {
+        const int row = (tid + 256 * u) >> 4;
+        qsrc[u] = Q + int64_t(row < J ? row : J - 1) * K + 8 * (tid & 15);
     }
+    auto load = [&](int64_t kb, uint4 (&v)[8], uint4 (&qv)[QU]) {
+        // zero past K: K % 16 == 0 keeps every 16-byte chunk either whole or
+        // wholly past the end
+        const bool full = kb + NT_PIECE <= k1;
+        const bool pok = full || kb + 8 * li < k1;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            v[t] = pok ? *reinterpret_cast<const uint4*>(pr + roff[t] + kb) : make_uint4(0u, 0u, 0u, 0u);
+        const bool qok = full || kb + 8 * (tid & 15) < k1;
+#pragma unroll
+        for (int u = 0; u < QU; ++u)
+            qv[u] = qok ? *reinterpret_cast<const uint4*>(qsrc[u] + kb) : make_uint4(0u, 0u, 0u, 0u);
+    };
     f32x4_t acc[2][NJ];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int64_t kb = k0 + 128 * w; kb < k1; kb += NT_SLAB) {
-        // the wave's 32 x 128 piece of P into LDS (zero past K: K % 16 == 0
-        // keeps every 16-byte chunk either whole or wholly past the end)
-        const bool full = kb + 128 <= k1;
-        uint4 v[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            v[t] = (full || kb + 8 * li < k1) ? *reinterpret_cast<const uint4*>(pr + roff[t] + kb) : make_uint4(0u, 0u, 0u, 0u);
-        u32x4_t b[4][NJ];
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            const bool ok = full || kb + 32 * sl + 8 * g < k1;
-#pragma unroll
-            for (int jb = 0; jb < NJ; ++jb)
-                b[sl][jb] = ok ? *reinterpret_cast<const u32x4_t*>(qr[jb] + kb + 32 * sl) : u32x4_t{0u, 0u, 0u, 0u};
-        }
+    uint4 v[8], qv[QU];
+    if (k0 < k1) load(k0, v, qv);
+    for (int64_t kb = k0; kb < k1; kb += NT_PIECE) {
+        __syncthreads();  // every wave is done reading the previous piece's tiles
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int row = 4 * t + (lane >> 4);
             pt[w][row][li ^ (row & 15)] = v[t];
         }
-        // one wave writes and reads its own tile, and LDS keeps a wave's
-        // accesses in order; the barrier keeps the compiler from moving them
-        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
+        for (int u = 0; u < QU; ++u) {
+            const int row = (tid + 256 * u) >> 4, ch = tid & 15;
+            qt[row][ch ^ (row & 15)] = qv[u];
+        }
+        __syncthreads();  // the piece's tiles are in
+        if (kb + NT_PIECE < k1) load(kb + NT_PIECE, v, qv);  // the next piece in flight
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            u32x4_t b[NJ];
+#pragma unroll
+            for (int jb = 0; jb < NJ; ++jb) {
+                const int row = 16 * jb + li;
+                b[jb] = __builtin_bit_cast(u32x4_t, qt[row][(4 * sl + g) ^ (row & 15)]);
+            }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 const int row = 16 * rb + li;
                 const u32x4_t a = __builtin_bit_cast(u32x4_t, pt[w][row][(4 * sl + g) ^ (row & 15)]);
 #pragma unroll
-                for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a, b[sl][jb], acc[rb][jb]);
+                for (int jb = 0; jb < NJ; ++jb) acc[rb][jb] = mfma16(a, b[jb], acc[rb][jb]);
             }
-        __builtin_amdgcn_wave_barrier();
+        }
     }
-    __syncthreads();  // every wave is done with its tile
     // D layout of the 16x16 MFMA: lane holds column li and rows 4g + e
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int jb = 0; jb < NJ; ++jb)
+        for (int jb = 0; jb < NJ; ++jb) {
+            const int j = 16 * jb + li;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[w][16 * rb + 4 * g + e][16 * jb + li] = acc[rb][jb][e];
-    __syncthreads();
-    const int rows = int(std::min<int64_t>(NT_ROWS, M - m0));
-    for (int idx = tid; idx < rows * J; idx += 256) {
-        const int row = idx / J, j = idx - row * J;
-        const float a = (red[0][row][j] + red[1][row][j]) + (red[2][row][j] + red[3][row][j]);
-        part[(int64_t(z) * M + m0 + row) * J + j] = a;
-    }
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + 16 * rb + 4 * g + e;
+                if (m < M && j < J) part[(int64_t(z) * M + m) * J + j] = acc[rb][jb][e];
+            }
+        }
 }
 
 // ------------------------------------------------------------------ k_tn
@@ -415,13 +420,15 @@ namespace nf4 {
 // Splits of the reduction: one per slab when there are fewer than eight
 // slabs, else a multiple of 8 (at least 512 workgroups when the rows allow);
 // chunks are whole slabs, and a trailing chunk past K adds zero.
+int64_t nt_chunk(int64_t K, int Z) { return cdiv(cdiv(K, Z), NT_PIECE) * NT_PIECE; }
 int nt_splits(int64_t M, int64_t K) {
-    const int64_t slabs = cdiv(K, NT_SLAB);
-    if (slabs < 8) return int(slabs);
+    const int64_t pieces = cdiv(K, NT_PIECE);
+    if (pieces < 8) return int(std::max<int64_t>(1, pieces));
+    // about one workgroup per CU: a workgroup keeps two pieces of 128 rows in flight
     const int64_t tiles = std::max<int64_t>(1, cdiv(M, NT_ROWS));  // (M = 0: a workspace query)
-    return int(8 * std::max<int64_t>(1, std::min<int64_t>(cdiv(512, 8 * tiles), slabs / 8)));
+    const int64_t z = 8 * std::max<int64_t>(1, std::min<int64_t>(cdiv(256, 8 * tiles), pieces / 8));
+    return int(cdiv(K, nt_chunk(K, int(z))));  // no empty chunk
 }
-int64_t nt_chunk(int64_t K, int Z) { return cdiv(cdiv(K, Z), NT_SLAB) * NT_SLAB; }
 // Token chunks of the column-stripe products: about 512 workgroups, chunks
 // of whole 64-token steps, and no empty chunk.
 int64_t tn_chunk(int64_t RR, int64_t M) {

@@ -375,11 +375,9 @@ __global__ __launch_bounds__(256) void k_fin_u_bs(const float* __restrict__ part
         }
         return;
     }
-    const int64_t stride = int64_t(gridDim.x - gu) * 256;
-    for (int64_t k = int64_t(blockIdx.x - gu) * 256 + threadIdx.x; k < nbk; k += stride) {
-        const int64_t g = GSH ? (k >> q.gshift) : (k / q.group);
-        sc[k] = __fmul_rn(q_over_127(q.qcodes[k]), q.gabs[g]);
-    }
+    __shared__ float tab[256];
+    block_scales_wg<GSH>(q.qcodes, q.gabs, q.group, q.gshift, nbk, sc, int64_t(blockIdx.x) - gu,
+                         int64_t(gridDim.x) - gu, tab);
 }
 
 // From v [M][r] fp32: ext [M][KL] = (bf16 hi of scale*v | bf16 lo | 0 pad),
@@ -578,7 +576,7 @@ int down_projection(hipStream_t st, const nf4::QView& q, const uint16_t* x, int6
     if (bs && q.dq) {
         const int gu = int(ew_grid(M * ext_cols(r)));
         const int64_t nbk = q.rows * q.cols / 64;
-        const dim3 grid = dim3(unsigned(gu + std::min<int64_t>(nf4::cdiv(nbk, 256), 4096)));
+        const dim3 grid = dim3(unsigned(gu + std::min<int64_t>(nf4::cdiv(nbk, 1024), 4096)));
         if (q.gshift >= 0)
             hipLaunchKernelGGL(k_fin_u_bs<true>, grid, dim3(256), 0, st, part, fp.Zu, M, r, ext_cols(r), scale, u,
                                ext, gu, q, nbk, bs);

@@ -954,11 +954,8 @@ __global__ __launch_bounds__(256) void k_multi_fin(FwdArgs a, int Z) {
 // fp32 block scales of a double-quantized weight: fl32(fl32(q_b/127) * c_g).
 template <bool GSH>
 __global__ __launch_bounds__(256) void k_block_scales(nf4::QView q, int64_t nb, float* __restrict__ out) {
-    const int64_t stride = int64_t(gridDim.x) * 256;
-    for (int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x; b < nb; b += stride) {
-        const int64_t g = GSH ? (b >> q.gshift) : (b / q.group);
-        out[b] = __fmul_rn(q_over_127(q.qcodes[b]), q.gabs[g]);
-    }
+    __shared__ float tab[256];
+    block_scales_wg<GSH>(q.qcodes, q.gabs, q.group, q.gshift, nb, out, blockIdx.x, gridDim.x, tab);
 }
 
 }  // namespace
@@ -979,7 +976,7 @@ int block_scales(const QView& q, float* scale_ws, const float** scales, hipStrea
     *scales = q.absmax;
     if (!q.dq) return NF4_OK;
     const int64_t nb = q.rows * q.cols / 64;
-    const unsigned g = unsigned(std::min<int64_t>(cdiv(nb, 256), 4096));
+    const unsigned g = unsigned(std::min<int64_t>(cdiv(nb, 1024), 4096));
     if (q.gshift >= 0)
         hipLaunchKernelGGL(k_block_scales<true>, dim3(g), dim3(256), 0, st, q, nb, scale_ws);
     else
@@ -1085,7 +1082,7 @@ int forward_rd(const QView& q, const uint16_t* x, int64_t M, const uint16_t* ext
     const float* scales = q.absmax;
     const int64_t nb = q.rows * q.cols / 64;
     if (q.dq) {
-        const unsigned g = unsigned(std::min<int64_t>(cdiv(nb, 256), 4096));
+        const unsigned g = unsigned(std::min<int64_t>(cdiv(nb, 1024), 4096));
         if (q.gshift >= 0)
             hipLaunchKernelGGL(k_block_scales<true>, dim3(g), dim3(256), 0, st, q, nb, scale_ws);
         else

@@ -345,11 +345,9 @@ __global__ __launch_bounds__(256) void k_tr_bs(const uint16_t* __restrict__ b, i
         transpose_tile(b, n, r, bt, blockIdx.x);
         return;
     }
-    const int64_t stride = int64_t(gridDim.x - gt) * 256;
-    for (int64_t k = int64_t(blockIdx.x - gt) * 256 + threadIdx.x; k < nbk; k += stride) {
-        const int64_t g = GSH ? (k >> q.gshift) : (k / q.group);
-        sc[k] = __fmul_rn(q_over_127(q.qcodes[k]), q.gabs[g]);
-    }
+    __shared__ float tab[256];
+    block_scales_wg<GSH>(q.qcodes, q.gabs, q.group, q.gshift, nbk, sc, int64_t(blockIdx.x) - gt,
+                         int64_t(gridDim.x) - gt, tab);
 }
 
 // out[j][i] = scale * sum_z part[z][i][j]  (i < n, j < r): the transposed reduce of dA
@@ -479,7 +477,7 @@ int transpose_bs(hipStream_t st, const uint16_t* b, int64_t n, int r, uint16_t* 
     if (r > 64 || !q.dq) return NF4_EINVAL;
     const int gt = int(cdiv(n, 64));
     const int64_t nbk = q.rows * q.cols / 64;
-    const int64_t gs = std::min<int64_t>(cdiv(nbk, 256), 4096);
+    const int64_t gs = std::min<int64_t>(cdiv(nbk, 1024), 4096);
     const dim3 grid = dim3(unsigned(gt + gs));
     if (q.gshift >= 0)
         hipLaunchKernelGGL(k_tr_bs<true>, grid, dim3(256), 0, st, b, n, r, bt, gt, q, nbk, sc);

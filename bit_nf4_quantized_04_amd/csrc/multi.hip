@@ -46,11 +46,13 @@ __global__ __launch_bounds__(1024) void k_multi_sort(const int32_t* __restrict__
     __shared__ int cnt[nf4::kMultiSortMaxAdapters + 1];
     __shared__ int cur[nf4::kMultiSortMaxAdapters + 1];
     if (blockIdx.x > 0) {  // workgroup-uniform
-        const int64_t stride = int64_t(gridDim.x - 1) * 1024;
-        for (int64_t b = int64_t(blockIdx.x - 1) * 1024 + threadIdx.x; b < nblk; b += stride) {
-            const int64_t g = q.gshift >= 0 ? (b >> q.gshift) : (b / q.group);
-            sc_out[b] = __fmul_rn(q_over_127(q.qcodes[b]), q.gabs[g]);
-        }
+        __shared__ float tab[256];
+        if (q.gshift >= 0)
+            block_scales_wg<true>(q.qcodes, q.gabs, q.group, q.gshift, nblk, sc_out, blockIdx.x - 1,
+                                  gridDim.x - 1, tab);
+        else
+            block_scales_wg<false>(q.qcodes, q.gabs, q.group, q.gshift, nblk, sc_out, blockIdx.x - 1,
+                                   gridDim.x - 1, tab);
         return;
     }
     const int tid = threadIdx.x, nb = n_ad + 1;
@@ -266,7 +268,7 @@ int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms,
     ms->bound = int(cdiv(M, SEG)) + n_ad + 1;  // segments: at most one partial per bucket
     const bool scales = q && q->dq && sc_out;
     const int64_t nblk = scales ? q->rows * q->cols / 64 : 0;
-    const unsigned extra = scales ? unsigned(std::min<int64_t>(cdiv(nblk, 1024), 1024)) : 0u;
+    const unsigned extra = scales ? unsigned(std::min<int64_t>(cdiv(nblk, 4096), 1024)) : 0u;
     hipLaunchKernelGGL(k_multi_sort, dim3(1 + extra), dim3(1024), 0, st, ids, int(M), n_ad, ms->perm, ms->off,
                        ms->seg, scales ? *q : QView{}, nblk, sc_out);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();

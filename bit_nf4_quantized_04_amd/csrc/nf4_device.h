@@ -117,6 +117,38 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, f3
 // fl32(q / 127) for an int8 scale code, as one correctly rounded division.
 __device__ __forceinline__ float q_over_127(int q) { return __fdiv_rn((float)q, 127.0f); }
 
+// fp32 block scales of a double-quantized weight, fl32(fl32(q_b/127) * c_g)
+// with g = b >> gshift (GSH) or b / group, for blocks [0, nbk), spread over
+// the threads of `nwg` workgroups of which this one is number `wg`.  The
+// workgroup first tabulates fl32(q/127) for the 256 int8 codes in `tab`
+// (LDS, the same division), then a thread takes four consecutive blocks at
+// a time (one 4-byte code load, one 16-byte store) when the arrays are
+// aligned for it, and single blocks for the rest.  Every thread of the
+// workgroup must call it (it synchronizes the workgroup once).
+template <bool GSH>
+__device__ __forceinline__ void block_scales_wg(const int8_t* __restrict__ qcodes, const float* __restrict__ gabs,
+                                                int group, int gshift, int64_t nbk, float* __restrict__ sc,
+                                                int64_t wg, int64_t nwg, float* tab) {
+    const int nt = int(blockDim.x);
+    for (int i = int(threadIdx.x); i < 256; i += nt) tab[i] = q_over_127(int8_t(i));
+    __syncthreads();
+    auto grp = [&](int64_t k) { return GSH ? (k >> gshift) : (k / group); };
+    const int64_t t0 = wg * nt + threadIdx.x, stride = nwg * nt;
+    const bool vec = (reinterpret_cast<uintptr_t>(qcodes) & 3) == 0 && (reinterpret_cast<uintptr_t>(sc) & 15) == 0;
+    const int64_t nu = vec ? nbk / 4 : 0;
+    for (int64_t u = t0; u < nu; u += stride) {
+        const uint32_t c = reinterpret_cast<const uint32_t*>(qcodes)[u];
+        const int64_t k = 4 * u;
+        float4 o;
+        o.x = __fmul_rn(tab[c & 255u], gabs[grp(k)]);
+        o.y = __fmul_rn(tab[(c >> 8) & 255u], gabs[grp(k + 1)]);
+        o.z = __fmul_rn(tab[(c >> 16) & 255u], gabs[grp(k + 2)]);
+        o.w = __fmul_rn(tab[c >> 24], gabs[grp(k + 3)]);
+        reinterpret_cast<float4*>(sc)[u] = o;
+    }
+    for (int64_t k = 4 * nu + t0; k < nbk; k += stride) sc[k] = __fmul_rn(tab[uint8_t(qcodes[k])], gabs[grp(k)]);
+}
+
 // Split an fp32 value into bf16 hi + bf16 lo with hi + lo == v to within
 // 2^-16 |v| (hi = RNE(v), lo = RNE(v - hi); v - hi is exact).
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {

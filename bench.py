@@ -42,7 +42,7 @@ KERNEL_MS_WHAT = ("mean over the timed steps of HIP events on the library's stre
                   "launched just before it in the same call to its own end (so it includes the dispatch gap "
                   "before it and cannot exceed the step)")
 ONLY = ("decode", "decode_bwd", "train", "train_fwd", "train_bwd", "train7", "train7_fwd", "train7_bwd",
-        "multi", "decode_c2", "read", "mfma", "copy")
+        "multi", "decode_c2", "read", "mfma", "structure", "vendor", "copy")
 
 
 def decode_bytes(out, inp, M, r, ngroups, with_A=True, block=64):
@@ -341,6 +341,39 @@ def main():
                 best = (rate, wgs, waves, t)
         return best
 
+    def tile_rate(dequant):
+        # the fused GEMM's inner loop without memory traffic (one workgroup of
+        # eight waves per CU, one LDS fragment per MFMA, with or without the
+        # dequantizing lookups): the ceiling of that structure on this GPU
+        wgs = CAL.default_workgroups(1) // 4
+        sink_t = torch.zeros(wgs * 8, dtype=torch.float32, device=dev)
+        iters = 4000
+        fl = CAL.mfma_tile(iters, sink_t, wgs, dequant)
+        t, _ = timed(lambda i: CAL.mfma_tile(iters, sink_t, wgs, dequant), 5, 2)
+        return fl / (t * 1e-3) / 1e12
+
+    def vendor_gemm(M, n_out, n_in):
+        # context only: the vendor library's plain bf16 product (torch.mm on
+        # hipBLASLt) at the same shapes, on a bf16 weight that needs no
+        # dequantization, forward (x W^T) and dX (dH W)
+        g = torch.Generator(device=dev).manual_seed(7)
+        xv = torch.randn(M, n_in, device=dev, dtype=torch.bfloat16, generator=g)
+        wv = (torch.randn(n_out, n_in, device=dev, dtype=torch.bfloat16, generator=g) * 0.02)
+        dv = torch.randn(M, n_out, device=dev, dtype=torch.bfloat16, generator=g)
+        fl = 2.0 * M * n_out * n_in
+        tf_, _ = timed(lambda i: torch.nn.functional.linear(xv, wv), 10, 3)
+        td_, _ = timed(lambda i: torch.mm(dv, wv), 10, 3)
+        del xv, wv, dv
+        return {"forward_ms": round(tf_, 4), "forward_TFLOPs": round(fl / (tf_ * 1e-3) / 1e12, 1),
+                "dx_ms": round(td_, 4), "dx_TFLOPs": round(fl / (td_ * 1e-3) / 1e12, 1)}
+
+    if args.only == "structure":
+        print("gemm structure: %.1f TFLOP/s bare, %.1f TFLOP/s with the dequantizing lookups"
+              % (tile_rate(False), tile_rate(True)), flush=True)
+        return
+    if args.only == "vendor":
+        print("vendor bf16 GEMM, M=4096 28672x8192: %s" % json.dumps(vendor_gemm(4096, 28672, 8192)), flush=True)
+        return
     if args.only == "copy":
         src = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev).uniform_()
         dst = torch.empty_like(src)
@@ -525,6 +558,9 @@ def main():
     read_kb, _ = read_rate(kb // 16 * 16, 5, K)
     read_1g, _ = read_rate(1 << 30, 2, max(K // 2, 3))
     mfma_meas, mfma_wgs, mfma_waves, _ = mfma_rate()
+    tile_bare, tile_deq = tile_rate(False), tile_rate(True)
+    vendor_70b = vendor_gemm(Mtrain, out, inp)
+    vendor_7b = vendor_gemm(M7, sh7["out"], sh7["inp"])
 
     # ------------------------------------------------ the line
     dec_bytes = decode_bytes(out, inp, 1, r, ngroups)
@@ -592,6 +628,15 @@ def main():
             "mfma_bf16_TFLOPs": round(mfma_meas, 1),
             "mfma_loop": "%d workgroups x %d waves, 8 independent v_mfma_f32_32x32x16_bf16 per wave"
                          % (mfma_wgs, mfma_waves),
+            "gemm_structure_TFLOPs": round(tile_bare, 1),
+            "gemm_structure_dequant_TFLOPs": round(tile_deq, 1),
+            "gemm_structure": "the fused GEMM's inner loop without memory traffic: 8 waves per CU, each a 256x32 "
+                              "slab, one 16-byte LDS A-fragment read per MFMA; _dequant adds the byte-plane lookup "
+                              "of one B operand per 8 MFMAs",
+            "vendor_bf16_gemm_70b_M4096": vendor_70b,
+            "vendor_bf16_gemm_7b_M2048": vendor_7b,
+            "vendor_bf16_gemm": "context only: torch.mm / linear (hipBLASLt) on plain bf16 operands of the same "
+                                "shapes, no dequantization",
         },
         "roofline_train": {
             "bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -600,6 +645,7 @@ def main():
             "forward_achieved": round(tf(gemm_flops, kf_ms), 2),
             "forward_frac": round(tf(gemm_flops, kf_ms) / MFMA_BF16_PEAK_TFLOPS, 4),
             "forward_frac_measured": round(tf(gemm_flops, kf_ms) / mfma_meas, 4),
+            "forward_frac_structure": round(tf(gemm_flops, kf_ms) / tile_deq, 4),
             "dx_kernel_ms": round(kd_ms, 4),
             "dx_achieved": round(tf(dx_flops, kd_ms), 2),
             "dx_frac": round(tf(dx_flops, kd_ms) / MFMA_BF16_PEAK_TFLOPS, 4),

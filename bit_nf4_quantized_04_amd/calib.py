@@ -1,6 +1,7 @@
 """ctypes binding of libnf4calib.so (include/nf4calib.h): the measurement
 kernels behind the achievable ceilings the benchmark quotes -- a plain
-streaming read of device memory and a loop of bf16 MFMA instructions.
+streaming read of device memory, a loop of bf16 MFMA instructions, and that
+loop fed like the fused GEMM's inner loop.
 Argument marshalling only."""
 
 from __future__ import annotations
@@ -20,10 +21,12 @@ _lib.nf4calib_read.restype = C.c_int
 _lib.nf4calib_read.argtypes = [_P, C.c_size_t, _P, C.c_int, _P]
 _lib.nf4calib_mfma.restype = C.c_int
 _lib.nf4calib_mfma.argtypes = [C.c_int, C.c_int, C.c_int, _P, _P]
+_lib.nf4calib_mfma_tile.restype = C.c_int
+_lib.nf4calib_mfma_tile.argtypes = [C.c_int, C.c_int, C.c_int, _P, _P]
 _lib.nf4calib_default_workgroups.restype = C.c_int
 _lib.nf4calib_default_workgroups.argtypes = [C.c_int]
 
-EXPORTS = ("nf4calib_read", "nf4calib_mfma", "nf4calib_default_workgroups")
+EXPORTS = ("nf4calib_read", "nf4calib_mfma", "nf4calib_mfma_tile", "nf4calib_default_workgroups")
 MFMA_FLOPS_PER_INSTR = 32 * 32 * 16 * 2
 MFMA_INSTR_PER_ITER = 8
 
@@ -51,3 +54,13 @@ def mfma(iters: int, sink: torch.Tensor, workgroups: int, waves: int) -> int:
     if rc:
         raise RuntimeError("nf4calib_mfma failed (%d)" % rc)
     return workgroups * waves * iters * MFMA_INSTR_PER_ITER * MFMA_FLOPS_PER_INSTR
+
+
+def mfma_tile(iters: int, sink: torch.Tensor, workgroups: int, dequant: bool) -> int:
+    """Run the GEMM-structure loop (8 waves per workgroup, one LDS fragment
+    per MFMA, with or without the dequantizing lookups); `sink` holds 8
+    floats per workgroup.  Returns the flops it performs."""
+    rc = _lib.nf4calib_mfma_tile(iters, workgroups, int(bool(dequant)), C.c_void_p(sink.data_ptr()), _stream())
+    if rc:
+        raise RuntimeError("nf4calib_mfma_tile failed (%d)" % rc)
+    return workgroups * 8 * iters * MFMA_INSTR_PER_ITER * MFMA_FLOPS_PER_INSTR

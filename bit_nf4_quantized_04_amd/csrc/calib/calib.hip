@@ -1,10 +1,13 @@
 // calib.hip -- the measurement kernels declared in include/nf4calib.h: a
-// plain streaming read (the achievable HBM read rate for a given size) and a
+// plain streaming read (the achievable HBM read rate for a given size), a
 // loop of bf16 matrix-core instructions (the achievable MFMA rate under a
-// sustained load).  Nothing here is used by the layer's kernels.
+// sustained load), and the same loop fed the way the fused GEMM's inner
+// loop feeds it (the ceiling of that structure).  Nothing here is used by
+// the layer's kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../nf4_device.h"
 #include "nf4calib.h"
 
 namespace {
@@ -90,6 +93,80 @@ __global__ __launch_bounds__(512) void k_mfma(int iters, float* __restrict__ sin
     if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 
+// The inner loop of the fused forward GEMM without its memory traffic: one
+// workgroup of eight waves per CU (the 96 KB of LDS keep a second one off),
+// each wave a 256 x 32 slab of eight 32x32 accumulators.  Per iteration
+// (one 16-k slice) the wave issues eight v_mfma_f32_32x32x16_bf16, each
+// followed by the 16-byte LDS read of its A fragment for the next slice
+// (eight waves read the same 8 KB, as they share the token tile); with
+// `DEQ` it also turns one code dword into the next slice's B operand with
+// the byte-plane lookup the layer's kernels use (four bf16 pairs from eight
+// 4-bit codes).  The LDS holds bf16 values with random mantissas.
+constexpr int TILE_LDS = 6144;  // uint4 entries: 96 KB
+
+template <bool DEQ>
+__global__ __launch_bounds__(512, 1) void k_mfma_tile(int iters, float* __restrict__ sink) {
+    __shared__ uint4 buf[TILE_LDS];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < TILE_LDS; i += 512) {
+        const uint32_t s = uint32_t(blockIdx.x) * TILE_LDS + uint32_t(i);
+        buf[i] = make_uint4((mix32(4 * s) & 0x807F807Fu) | 0x3F003F00u, (mix32(4 * s + 1) & 0x807F807Fu) | 0x3F003F00u,
+                            (mix32(4 * s + 2) & 0x807F807Fu) | 0x3F003F00u,
+                            (mix32(4 * s + 3) & 0x807F807Fu) | 0x3F003F00u);
+    }
+    __syncthreads();
+    const uint32_t seed = blockIdx.x * 512u + uint32_t(tid);
+    nf4dev::DecK dk;
+    dk.init();
+    nf4dev::Levels lv;
+    lv.init(0);
+    const nf4dev::Planes pl = nf4dev::make_planes(0.01f + float(seed & 255u) * 1e-4f, lv);
+    u32x4_t fr[8], b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fr[i] = __builtin_bit_cast(u32x4_t, buf[(i * 64 + lane + w * 512) % TILE_LDS]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = (mix32(seed * 8u + 4u + e) & 0x807F807Fu) | 0x3F003F00u;
+    f32x16_t acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    uint32_t cd = mix32(seed);
+    const uint32_t base = uint32_t(w * 512 + lane) % 4096u;
+    for (int it = 0; it < iters; ++it) {
+        const uint32_t ib = (base + uint32_t(it & 7) * 512u) % 4096u;  // < 4096 + 7 * 64 < TILE_LDS
+        u32x4_t bn;
+        if constexpr (DEQ)
+            nf4dev::lookup8(dk, pl, cd, bn);
+        else
+            bn = b ^ uint32_t(it & 0x007F007F);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[i]),
+                                                             __builtin_bit_cast(bf16x8_t, b), acc[i], 0, 0, 0);
+            fr[i] = __builtin_bit_cast(u32x4_t, buf[ib + uint32_t(i) * 64u]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {  // the forward kernel's schedule: MFMA, LDS read, up to four VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        b = bn;
+        cd = cd * 1664525u + 1013904223u;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[i][e];
+        s += float(fr[i][0] & 255u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) sink[blockIdx.x * 8 + w] = s;
+}
+
 int resident(const void* kern, int threads) {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -136,6 +213,19 @@ int nf4calib_mfma(int iters, int workgroups, int waves, float* sink, void* strea
     if (workgroups <= 0) return 5;
     hipLaunchKernelGGL(k_mfma, dim3(unsigned(workgroups)), dim3(unsigned(64 * waves)), 0,
                        static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int nf4calib_mfma_tile(int iters, int workgroups, int dequant, float* sink, void* stream) {
+    if (!sink || iters < 1 || workgroups < 0 || (dequant != 0 && dequant != 1)) return 1;
+    if (workgroups == 0) workgroups = cus_of_device();
+    if (workgroups <= 0) return 5;
+    if (dequant)
+        hipLaunchKernelGGL(k_mfma_tile<true>, dim3(unsigned(workgroups)), dim3(512), 0,
+                           static_cast<hipStream_t>(stream), iters, sink);
+    else
+        hipLaunchKernelGGL(k_mfma_tile<false>, dim3(unsigned(workgroups)), dim3(512), 0,
+                           static_cast<hipStream_t>(stream), iters, sink);
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

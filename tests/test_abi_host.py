@@ -64,6 +64,9 @@ def test_calibration_library_exports_and_argument_errors():
     assert L.nf4calib_mfma(0, 4, 4, FAKE, None) == 1
     assert L.nf4calib_mfma(10, 4, 9, FAKE, None) == 1
     assert L.nf4calib_mfma(10, 4, 4, None, None) == 1
+    assert L.nf4calib_mfma_tile(0, 4, 0, FAKE, None) == 1
+    assert L.nf4calib_mfma_tile(10, 4, 2, FAKE, None) == 1
+    assert L.nf4calib_mfma_tile(10, 4, 1, None, None) == 1
 
 
 def test_profile_hook_arguments(F):

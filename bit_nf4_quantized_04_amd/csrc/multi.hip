@@ -112,16 +112,17 @@ __device__ __forceinline__ int bucket_of(const int32_t* seg, int nb, int w) {
 }
 
 // su[t][j] for the tokens of one segment of a valid bucket.  NJ blocks of 16
-// adapter rows (r <= 16 NJ).  K % 32 == 0.
-template <int NJ>
-__global__ __launch_bounds__(256) void k_multi_down_seg(const uint16_t* __restrict__ x, int64_t K,
+// adapter rows (r <= 16 NJ); NWD waves split the K range (32-k slices w,
+// w + NWD, ...) and their sums are added in LDS in wave order.  K % 32 == 0.
+template <int NJ, int NWD>
+__global__ __launch_bounds__(64 * NWD) void k_multi_down_seg(const uint16_t* __restrict__ x, int64_t K,
                                                         const uint16_t* __restrict__ Ab, int n_ad, int r,
                                                         const float* __restrict__ scales,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ off,
                                                         const int32_t* __restrict__ seg, float* __restrict__ su) {
     constexpr int RS = 16 * NJ + 4;  // the four row groups of a fragment 16 banks apart
-    __shared__ float red[4][SEG][RS];
+    __shared__ float red[NWD][SEG][RS];
     const int w_idx = blockIdx.x;
     if (w_idx >= seg[n_ad]) return;  // past the segments of the valid buckets (workgroup-uniform)
     const int a = bucket_of(seg, n_ad, w_idx);
@@ -139,22 +140,23 @@ __global__ __launch_bounds__(256) void k_multi_down_seg(const uint16_t* __restri
     f32x4_t acc[NJ];
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // 32-k slices s = w, w + 4, ...; four in flight
+    // 32-k slices s = w, w + NWD, ...; four in flight
+    constexpr int KS = 32 * NWD;
     int64_t k = 32 * w;
-    for (; k + 3 * 128 < K; k += 4 * 128) {
+    for (; k + 3 * KS < K; k += 4 * KS) {
         u32x4_t xa[4], ab[4][NJ];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            xa[u] = *reinterpret_cast<const u32x4_t*>(xr + k + 128 * u);
+            xa[u] = *reinterpret_cast<const u32x4_t*>(xr + k + KS * u);
 #pragma unroll
-            for (int jb = 0; jb < NJ; ++jb) ab[u][jb] = *reinterpret_cast<const u32x4_t*>(ar[jb] + k + 128 * u);
+            for (int jb = 0; jb < NJ; ++jb) ab[u][jb] = *reinterpret_cast<const u32x4_t*>(ar[jb] + k + KS * u);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int jb = 0; jb < NJ; ++jb) acc[jb] = mfma16(xa[u], ab[u][jb], acc[jb]);
     }
-    for (; k < K; k += 128) {
+    for (; k < K; k += KS) {
         const u32x4_t xa = *reinterpret_cast<const u32x4_t*>(xr + k);
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb)
@@ -168,9 +170,11 @@ __global__ __launch_bounds__(256) void k_multi_down_seg(const uint16_t* __restri
     __syncthreads();
     const float s = scales[a];
     const int n = p1 - p0;
-    for (int idx = tid; idx < n * r; idx += 256) {
+    for (int idx = tid; idx < n * r; idx += 64 * NWD) {
         const int i = idx / r, j = idx - i * r;
-        const float v = (red[0][i][j] + red[1][i][j]) + (red[2][i][j] + red[3][i][j]);
+        float v = red[0][i][j];
+#pragma unroll
+        for (int ww = 1; ww < NWD; ++ww) v += red[ww][i][j];
         su[int64_t(perm[p0 + i]) * r + j] = v * s;
     }
 }
@@ -276,16 +280,17 @@ int multi_sort(const int32_t* ids, int64_t M, int n_ad, char* ws, MultiSort* ms,
 
 int multi_down_seg(const MultiSort& ms, const uint16_t* x, int64_t K, const uint16_t* Ab, int r,
                    const float* scales, float* su, hipStream_t st) {
+    // sixteen waves per segment: the segments alone are fewer than the CUs
     const dim3 grid(unsigned(ms.bound));
     if (r <= 16)
-        hipLaunchKernelGGL(k_multi_down_seg<1>, grid, dim3(256), 0, st, x, K, Ab, ms.n_ad, r, scales, ms.perm, ms.off,
-                           ms.seg, su);
+        hipLaunchKernelGGL((k_multi_down_seg<1, 16>), grid, dim3(1024), 0, st, x, K, Ab, ms.n_ad, r, scales, ms.perm,
+                           ms.off, ms.seg, su);
     else if (r <= 32)
-        hipLaunchKernelGGL(k_multi_down_seg<2>, grid, dim3(256), 0, st, x, K, Ab, ms.n_ad, r, scales, ms.perm, ms.off,
-                           ms.seg, su);
+        hipLaunchKernelGGL((k_multi_down_seg<2, 16>), grid, dim3(1024), 0, st, x, K, Ab, ms.n_ad, r, scales, ms.perm,
+                           ms.off, ms.seg, su);
     else
-        hipLaunchKernelGGL(k_multi_down_seg<4>, grid, dim3(256), 0, st, x, K, Ab, ms.n_ad, r, scales, ms.perm, ms.off,
-                           ms.seg, su);
+        hipLaunchKernelGGL((k_multi_down_seg<4, 16>), grid, dim3(1024), 0, st, x, K, Ab, ms.n_ad, r, scales, ms.perm,
+                           ms.off, ms.seg, su);
     return hipPeekAtLastError() == hipSuccess ? NF4_OK : launch_status();
 }
 

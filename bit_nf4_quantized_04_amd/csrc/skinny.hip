@@ -77,14 +77,25 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
     }
 }
 
+// Whether the decode kernel for MT tokens loads its MFMA A fragments (x)
+// straight from memory (16 tokens: each lane's eight fragments of a
+// block-step are eight 16-byte loads) rather than staging the step's x slice
+// through LDS (fewer tokens: one 8-byte load per token per lane).
+#ifndef NF4_SKINNY_XDIRECT
+#define NF4_SKINNY_XDIRECT 16
+#endif
+template <int MT>
+constexpr bool skinny_xdirect() { return MT >= NF4_SKINNY_XDIRECT; }
+
 // Shared memory of the decode kernel.
 template <int MT, int NWV>
 struct SkinnySmem {
+    static constexpr bool XS = !skinny_xdirect<MT>();
     // [wave][entry][lane] dword slots; the bf16 entry sits in the low half.
     // Every C++ access is 16-bit typed.  After the main loop the storage
     // holds the cross-wave reduction.
     uint16_t tbl[NWV][16][128];
-    uint16_t xs[NWV][MT][256];  // x slice of the current block-step, per wave
+    uint16_t xs[XS ? NWV : 1][XS ? MT : 1][256];  // x slice of the current block-step, per wave
     float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
     float us[16 * 64];  // u for the epilogue (r <= 64 here)
 };
@@ -124,14 +135,18 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
     const char* tb = reinterpret_cast<const char*>(&sm.tbl[0][0][0]);
 
     // One block-step = 4 blocks of 16 rows (256 k).  Everything it needs from
-    // memory -- codes, the block scale, the x slice (lane l holds k 4l..4l+3
-    // of every token) -- is fetched one step ahead into a ping-pong buffer.
+    // memory -- codes, the block scale, and x: either the step's slice (lane
+    // l holds k 4l..4l+3 of every token, staged through LDS) or, direct, the
+    // lane's own A fragments (token j, k 64g + 8st .. +7 of the step) -- is
+    // fetched one step ahead into a ping-pong buffer.
+    constexpr bool XD = skinny_xdirect<MT>();
     struct Fetch {  // raw loads only: nothing here waits for memory
         uint4 c0, c1;
         uint32_t qb;  // int8 scale code (DQ) or the fp32 absmax bits
         float cg;     // group constant (DQ)
         bool ok;
-        uint2 xv[MT];
+        uint2 xv[XD ? 1 : MT];
+        u32x4_t xa[XD ? 8 : 1];
     };
     auto fetch = [&](int kb, Fetch& f) {
         const int blk = kb * 4 + g;
@@ -148,21 +163,35 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
             f.qb = __builtin_bit_cast(uint32_t, arow[cb]);
             f.cg = 0.0f;
         }
-        int64_t kx = int64_t(kb) * 256 + 4 * l;
-        if (kx + 4 > K) kx = K - 4;  // past the end only for zero-scale blocks
+        if constexpr (XD) {
+            // token j's k chunk g of the step (a block past the end of the row
+            // has zero scales for every row: any finite x will do there)
+            const int64_t kx = int64_t(blk < nkb ? blk : nkb - 1) * 64;
+            const uint16_t* xp = x + int64_t(j < M ? j : 0) * K + kx;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            f.xv[m] = make_uint2(0, 0);
-            if (m < M) f.xv[m] = *reinterpret_cast<const uint2*>(x + int64_t(m) * K + kx);
+            for (int st = 0; st < 8; ++st) {
+                f.xa[st] = u32x4_t{0u, 0u, 0u, 0u};
+                if (j < M) f.xa[st] = *reinterpret_cast<const u32x4_t*>(xp + st * 8);
+            }
+        } else {
+            int64_t kx = int64_t(kb) * 256 + 4 * l;
+            if (kx + 4 > K) kx = K - 4;  // past the end only for zero-scale blocks
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                f.xv[m] = make_uint2(0, 0);
+                if (m < M) f.xv[m] = *reinterpret_cast<const uint2*>(x + int64_t(m) * K + kx);
+            }
         }
     };
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     auto process = [&](const Fetch& f) {
         // stage the x slice (this wave only: LDS operations of a wave are in order)
+        if constexpr (!XD) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < M) *reinterpret_cast<uint2*>(&sm.xs[w][m][4 * l]) = f.xv[m];
+            for (int m = 0; m < MT; ++m)
+                if (m < M) *reinterpret_cast<uint2*>(&sm.xs[w][m][4 * l]) = f.xv[m];
+        }
         const float sc = DQ ? __fmul_rn(sm.q127[f.qb], f.cg) : bits_f(f.qb);
         const float sblk = f.ok ? sc : 0.0f;
         // the block's 16 products, bf16, into this lane's table column
@@ -177,7 +206,9 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             u32x4_t xa = {0u, 0u, 0u, 0u};  // MFMA rows >= M are never stored
-            if (j < M)
+            if constexpr (XD)
+                xa = f.xa[st];
+            else if (j < M)
                 xa = *reinterpret_cast<const u32x4_t*>(&sm.xs[w][j < MT ? j : 0][g * 64 + st * 8]);
             const uint32_t cd = cw[st];
             const uint32_t clo = (cd & 0x0F0F0F0Fu) | P;         // low nibbles: odd elements
@@ -198,6 +229,16 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
 
     Fetch fa, fb;
     if (sb < se) fetch(sb, fa);
+    // u = sum of the down-projection partials, in a fixed order, into LDS
+    // while the first block-step's loads are in flight (the epilogue reads
+    // it after the barriers that follow the main loop)
+    for (int idx = tid; idx < M * r; idx += 64 * NWV) {
+        float a = 0.0f;
+#pragma unroll 4
+        for (int zz = 0; zz < DOWN_SPLIT; ++zz) a += upart[int64_t(zz) * M * r + idx];
+        sm.us[idx] = a;
+        if (blockIdx.x == 0 && u_out) u_out[idx] = a;
+    }
     for (int kb = sb; kb < se; kb += 2) {
         if (kb + 1 < se) fetch(kb + 1, fb);
         process(fa);
@@ -212,15 +253,6 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
     float (*red)[16][17] = reinterpret_cast<float (*)[16][17]>(&sm.tbl[0][0][0]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[w][4 * g + e][j] = acc[e];
-    __syncthreads();
-    // u = sum of the down-projection partials, in a fixed order
-    for (int idx = tid; idx < M * r; idx += 64 * NWV) {
-        float a = 0.0f;
-#pragma unroll 4
-        for (int zz = 0; zz < DOWN_SPLIT; ++zz) a += upart[int64_t(zz) * M * r + idx];
-        sm.us[idx] = a;
-        if (blockIdx.x == 0 && u_out) u_out[idx] = a;
-    }
     __syncthreads();
     // epilogue: output (i, jj) of the tile is finished by 16 lanes that split
     // the rank-r dot product s * u[i] . B[o]
@@ -286,7 +318,7 @@ __device__ __forceinline__ float lane_val(float v, int lane) {
 // of resident workgroups (at most), and workgroup b takes chunks b, b + G,
 // b + 2G, ... of the G-strided sequence: neighbouring workgroups stream
 // neighbouring rows, and no counter or atomic is involved.
-constexpr int G1_NC = 3;  // rows per wave per chunk (and fetch ring slots)
+constexpr int G1_NC = 4;  // rows per wave per chunk (and fetch ring slots)
 #ifndef NF4_GEMV_NV
 #define NF4_GEMV_NV 0
 #endif

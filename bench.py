@@ -97,6 +97,11 @@ def measured_traffic(kernel):
 
 
 # ----------------------------------------------------------------- CPU oracle
+def progress(msg):
+    """One line on stderr when a section of the run has finished."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
 def _cores():
     try:
         aff = len(os.sched_getaffinity(0))
@@ -514,14 +519,18 @@ def main():
     settle(decode_bwd_step)
     t_dbw, _ = timed(decode_bwd_step, K, W)
     _, k_dbw = timed(decode_bwd_step, K, 1, hook=1)
+    progress("decode (70B, M=1) timed")
     t_tr, _ = timed(train_step, max(K // 2, 3), max(W // 2, 1))
     _, fwd_k = timed(train_fwd, max(K // 2, 3), 1, hook=0)
     _, bwd_k = timed(train_bwd, max(K // 2, 3), 1, hook=0)
+    progress("training pass (70B, M=4096) timed")
     t_7b, _ = timed(train7_step, K, W)
     _, fwd7_k = timed(train7_fwd, K, 1, hook=0)
     _, bwd7_k = timed(train7_bwd, K, 1, hook=0)
+    progress("training pass (7B, M=2048) timed")
     t_mu, _ = timed(multi_step, K, W)
     _, mu_k = timed(multi_step, K, 1, hook=0)
+    progress("multi-adapter forward timed")
     t_c2 = {}
     for M2, step in dec2.items():
         settle(step)
@@ -551,6 +560,7 @@ def main():
         hev.destroy(e1)
         del g
     del q2
+    progress("4096 x 4096 decode timed")
 
     # the measured ceilings: a plain read of the GEMV kernel's bytes (rotated
     # over 5 buffers like the weight copies), of 1 GiB, and the MFMA loop
@@ -561,6 +571,7 @@ def main():
     tile_bare, tile_deq = tile_rate(False), tile_rate(True)
     vendor_70b = vendor_gemm(Mtrain, out, inp)
     vendor_7b = vendor_gemm(M7, sh7["out"], sh7["inp"])
+    progress("ceilings measured")
 
     # ------------------------------------------------ the line
     dec_bytes = decode_bytes(out, inp, 1, r, ngroups)
@@ -703,8 +714,10 @@ def main():
               file=sys.stderr)
     extra_timings(line, args, timed, torch, F, wl, dev, bf, ws, copies_of, qs, A, B, x1, scale, sh, out, inp, r,
                   ngroups, Mtrain, xt, dH, ht, t_tr, ffwd, fbwd, q7, x7, dH7, A7, B7, s7, sh7, M7, r7, h7, f7, t_7b, settle)
+    progress("merge, AdamW, blocks of 128, FP4 and dropout timed")
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["cpu_baseline_other"] = cpu_baselines()
+        progress("oracle baselines timed")
     print(json.dumps(line), flush=True)
 
 

@@ -98,6 +98,7 @@ struct SkinnySmem {
     uint16_t xs[XS ? NWV : 1][XS ? MT : 1][256];  // x slice of the current block-step, per wave
     float q127[256];  // fl32(q/127) for the int8 code q, indexed by its byte
     float us[16 * 64];  // u for the epilogue (r <= 64 here)
+    uint16_t bs[16 * 64];  // the tile's 16 rows of B, for the epilogue
 };
 
 // MT = token capacity (1, 4 or 16); the kernel handles any M <= MT.  NWV:
@@ -229,9 +230,14 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
 
     Fetch fa, fb;
     if (sb < se) fetch(sb, fa);
-    // u = sum of the down-projection partials, in a fixed order, into LDS
-    // while the first block-step's loads are in flight (the epilogue reads
-    // it after the barriers that follow the main loop)
+    // u = sum of the down-projection partials, in a fixed order, and the
+    // tile's rows of B, into LDS while the first block-step's loads are in
+    // flight (the epilogue reads both after the barriers that follow the
+    // main loop)
+    for (int idx = tid; idx < 16 * r; idx += 64 * NWV) {
+        const int64_t o = o0 + idx / r;
+        sm.bs[idx] = o < N ? B[o * r + idx % r] : uint16_t(0);
+    }
     for (int idx = tid; idx < M * r; idx += 64 * NWV) {
         float a = 0.0f;
 #pragma unroll 4
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_
         float ls = 0.0f;
         if (o < N) {
             const float* ui = &sm.us[i * r];
-            const uint16_t* br = B + o * r;
+            const uint16_t* br = &sm.bs[jj * r];
             for (int c = sub; c < r; c += 16) ls = fmaf(ui[c], bf16_f(br[c]), ls);
         }
 #pragma unroll

@@ -87,6 +87,13 @@ __global__ __launch_bounds__(256) void k_down_small(const uint16_t* __restrict__
 template <int MT>
 constexpr bool skinny_xdirect() { return MT >= NF4_SKINNY_XDIRECT; }
 
+// Waves per SIMD the few-token kernel's registers must leave room for: five
+// at 2 to 4 tokens (the compiler otherwise takes 100 registers, i.e. four
+// waves: 8 % slower on the 70B weight at 4 tokens); no bound at 16 tokens,
+// whose x fragments need 144 registers (held to four waves they spill).
+template <int MT>
+constexpr int skinny_min_waves() { return MT == 4 ? 5 : 1; }
+
 // Shared memory of the decode kernel.
 template <int MT, int NWV>
 struct SkinnySmem {
@@ -104,7 +111,7 @@ struct SkinnySmem {
 // MT = token capacity (1, 4 or 16); the kernel handles any M <= MT.  NWV:
 // waves per workgroup.
 template <bool DQ, int MT, int NWV>
-__global__ __launch_bounds__(64 * NWV) void k_skinny(nf4::QView q, const uint16_t* __restrict__ x, int M,
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(skinny_min_waves<MT>()))) void k_skinny(nf4::QView q, const uint16_t* __restrict__ x, int M,
                                                 const float* __restrict__ upart, int r,
                                                 const uint16_t* __restrict__ B, float scale,
                                                 uint16_t* __restrict__ h, float* __restrict__ u_out) {
